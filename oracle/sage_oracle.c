@@ -1,0 +1,387 @@
+/*
+ * sage_oracle.c -- plain, slow, scalar CPU oracle for the SageAttention /
+ * SageAttention2 quantized attention forward pass (INT8 Q.K^T, FP8 P.V).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the independent checker of the HIP
+ * library: only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark may load it.  It shares no code, header, table or constant
+ * generator with the GPU path and never includes a HIP header.  Build:
+ *     gcc -O2 -ffp-contract=off -fPIC -shared -pthread sage_oracle.c -lm
+ * (no -ffast-math, default rounding mode, IEEE denormals).
+ *
+ * Sources (web pages; cited by title and section):
+ *  [PKG]   "sageattention" package page -- "What it is and what it does":
+ *          smoothing, per-block quantization of Q and K, head dims 64/96/128,
+ *          Nq != Nkv, GQA; "Quickstart": sageattn(q, k, v, tensor_layout,
+ *          is_causal, smooth_k).
+ *  [BLOG]  ComfyUI blog on SageAttention, list "main roles and features",
+ *          item 2 ("keeping accuracy"): smoothing lowers quantization error;
+ *          QK is computed in INT8 and PV in FP8, with different granularities.
+ *  [SA2]   "SageAttention2: technical report" summary -- "Main concepts",
+ *          item 2: Q and V are smoothed by subtracting their channel mean
+ *          before quantization; item 3: the INT8+FP8 precision branch.
+ *  [SA1]   SA1 abstract (llama.cpp discussion #9901): attention is O(N^2) and
+ *          the method quantizes attention itself.
+ *
+ * Every step below follows the plainest reading of those pages; where they
+ * are silent the reading is named in the comment (R-n numbering of the
+ * design notes).  Floating point: the recipe functions use FP32 exactly as
+ * the method's GPU arithmetic is specified (so that quantized codes are
+ * decided in the same precision on both sides); the exact reference
+ * (orc_attn_exact_rows) is FP64 throughout.
+ *
+ * Pins: codecs are checked against numpy/torch conversions and their
+ * definitions; the channel mean against closed forms; quantizers against
+ * round-trip bounds; int32 Q.K^T against brute force; the recipe against
+ * textbook special cases and FP64 attention (tests/test_oracle_*.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+
+#define ORC_EXPORT __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------ */
+/* Codecs, written from the format definitions.                              */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+ORC_EXPORT float orc_f16_decode(uint16_t h) {
+    int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0)       v = ldexp((double)m, -24);               /* subnormal  */
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else              v = ldexp((double)(1024 + m), e - 25);
+    return (float)(s ? -v : v);
+}
+
+/* Round-to-nearest-even encode of an FP32 value into binary16. */
+ORC_EXPORT uint16_t orc_f16_encode(float f) {
+    uint32_t u = f2u(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000);
+    float a = fabsf(f);
+    if (isnan(f)) return (uint16_t)(sign | 0x7e00);
+    if (a >= 65520.0f) return (uint16_t)(sign | 0x7c00);     /* rounds to inf */
+    /* Work in double: a is exact there; scale to integer units of the target
+       ulp and round half to even with nearbyint (default mode = RNE). */
+    double da = (double)a;
+    if (da < ldexp(1.0, -14)) {                                 /* subnormal  */
+        double q = nearbyint(da * ldexp(1.0, 24));
+        return (uint16_t)(sign | (uint16_t)q);                  /* q<=1024 ok */
+    }
+    int e; double fr = frexp(da, &e);                           /* da=fr*2^e  */
+    double q = nearbyint(fr * 2048.0);                          /* 1024..2048 */
+    if (q == 2048.0) { q = 1024.0; e += 1; }
+    int ef = e - 1 + 15;
+    if (ef >= 31) return (uint16_t)(sign | 0x7c00);
+    return (uint16_t)(sign | (ef << 10) | ((int)q - 1024));
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+ORC_EXPORT float orc_bf16_decode(uint16_t h) { return u2f((uint32_t)h << 16); }
+
+ORC_EXPORT uint16_t orc_bf16_encode(float f) {
+    if (isnan(f)) return (uint16_t)((f2u(f) >> 16) | 0x40);
+    double a = fabs((double)f);
+    uint16_t sign = (uint16_t)((f2u(f) >> 16) & 0x8000);
+    if (a == 0.0) return sign;
+    if (isinf(f)) return (uint16_t)(sign | 0x7f80);
+    if (a < ldexp(1.0, -126)) {                                 /* subnormal  */
+        double q = nearbyint(a * ldexp(1.0, 133));
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    int e; double fr = frexp(a, &e);
+    double q = nearbyint(fr * 256.0);                           /* 128..256   */
+    if (q == 256.0) { q = 128.0; e += 1; }
+    int ef = e - 1 + 127;
+    if (ef >= 255) return (uint16_t)(sign | 0x7f80);
+    return (uint16_t)(sign | (ef << 7) | ((int)q - 128));
+}
+
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits, no
+   infinities, S.1111.111 is NaN, largest finite 448, subnormals 2^-9..      */
+ORC_EXPORT float orc_e4m3_decode(uint8_t b) {
+    int s = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) v = NAN;
+    else if (e == 0)       v = ldexp((double)m, -9);
+    else                   v = ldexp((double)(8 + m), e - 10);
+    return (float)(s ? -v : v);
+}
+
+/* RNE encode with saturation to +-448 (R-11).  NaN maps to 0x7f. */
+ORC_EXPORT uint8_t orc_e4m3_encode_sat(float f) {
+    if (isnan(f)) return 0x7f;
+    uint8_t sign = (f2u(f) >> 31) ? 0x80 : 0x00;
+    double a = fabs((double)f);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7e);              /* saturate   */
+    if (a < ldexp(1.0, -6)) {                                   /* subnormal  */
+        double q = nearbyint(a * 512.0);                        /* 0..8       */
+        return (uint8_t)(sign | (uint8_t)q);                    /* 8 = 2^-6 ok*/
+    }
+    int e; double fr = frexp(a, &e);
+    double q = nearbyint(fr * 16.0);                            /* 8..16      */
+    if (q == 16.0) { q = 8.0; e += 1; }
+    int ef = e - 1 + 7;
+    if (ef > 15 || (ef == 15 && q - 8 >= 7)) return (uint8_t)(sign | 0x7e);
+    return (uint8_t)(sign | (ef << 3) | ((int)q - 8));
+}
+
+/* Bulk decoders: dtype 0 = fp16, 1 = bf16. */
+ORC_EXPORT void orc_decode16(const uint16_t* in, float* out, int64_t n, int dtype) {
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = dtype ? orc_bf16_decode(in[i]) : orc_f16_decode(in[i]);
+}
+ORC_EXPORT void orc_encode16(const float* in, uint16_t* out, int64_t n, int dtype) {
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = dtype ? orc_bf16_encode(in[i]) : orc_f16_encode(in[i]);
+}
+ORC_EXPORT void orc_decode_e4m3(const uint8_t* in, float* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(in[i]);
+}
+ORC_EXPORT void orc_encode_e4m3(const float* in, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode_sat(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pre-pass: smoothing and quantization ([PKG], [BLOG] item 2, [SA2] item 2) */
+/* ------------------------------------------------------------------------ */
+
+/* Per-channel mean over the n tokens of one (sequence, head) (R-6, R-7).
+   x is [n][d] row-major FP32 (exactly decoded inputs).  Order: tokens are
+   grouped in chunks of 64 aligned to the sequence start; each chunk is summed
+   token by token in FP32, the chunk sums are added in chunk order in FP32,
+   and the total is divided by n with one correctly rounded FP32 division.  */
+ORC_EXPORT void orc_channel_mean(const float* x, int64_t n, int d, float* mu) {
+    for (int c = 0; c < d; ++c) {
+        float total = 0.0f;
+        for (int64_t t0 = 0; t0 < n; t0 += 64) {
+            float part = 0.0f;
+            int64_t t1 = t0 + 64 < n ? t0 + 64 : n;
+            for (int64_t t = t0; t < t1; ++t) part = part + x[t * d + c];
+            total = total + part;
+        }
+        mu[c] = n > 0 ? total / (float)n : 0.0f;
+    }
+}
+
+/* x_s = fl32(x - mu) per element (R-8: the smoothed value stays FP32).
+   mu == NULL means no smoothing (x_s = x). */
+ORC_EXPORT void orc_smooth(const float* x, const float* mu, int64_t n, int d, float* xs) {
+    for (int64_t t = 0; t < n; ++t)
+        for (int c = 0; c < d; ++c)
+            xs[t * d + c] = mu ? x[t * d + c] - mu[c] : x[t * d + c];
+}
+
+/* Per-block symmetric INT8 quantization (R-1..R-5): blocks of `blk` tokens
+   aligned to the sequence start (the last one may be short).  a = max |x_s|
+   over the block; a == 0 gives scale 0 and zero codes; otherwise
+   inv = fl32(127/a), scale = fl32(a/127), code = clamp(rne(fl32(x_s*inv)),
+   -127, 127).  codes: [n][d]; scales: [ceil(n/blk)].                        */
+ORC_EXPORT void orc_quant_int8_blocks(const float* xs, int64_t n, int d, int blk,
+                                      int8_t* codes, float* scales) {
+    for (int64_t b0 = 0, bi = 0; b0 < n; b0 += blk, ++bi) {
+        int64_t b1 = b0 + blk < n ? b0 + blk : n;
+        float a = 0.0f;
+        for (int64_t t = b0; t < b1; ++t)
+            for (int c = 0; c < d; ++c) {
+                float v = fabsf(xs[t * d + c]);
+                if (v > a) a = v;
+            }
+        if (a == 0.0f) {
+            scales[bi] = 0.0f;
+            for (int64_t t = b0; t < b1; ++t)
+                for (int c = 0; c < d; ++c) codes[t * d + c] = 0;
+            continue;
+        }
+        float inv = 127.0f / a;
+        scales[bi] = a / 127.0f;
+        for (int64_t t = b0; t < b1; ++t)
+            for (int c = 0; c < d; ++c) {
+                float y = xs[t * d + c] * inv;
+                float r = nearbyintf(y);                      /* RNE (R-3)   */
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                codes[t * d + c] = (int8_t)r;
+            }
+    }
+}
+
+/* Per-channel FP8 E4M3 quantization of (smoothed) V (R-11, R-12): per
+   channel c, a = max over the n tokens of |v_s|; a == 0 gives scale 0 and
+   zero codes; otherwise inv = fl32(448/a), scale = fl32(a/448) and
+   code = e4m3_rne_sat(fl32(v_s*inv)).  codes: [n][d]; scales: [d].          */
+ORC_EXPORT void orc_quant_fp8_channels(const float* vs, int64_t n, int d,
+                                       uint8_t* codes, float* scales) {
+    for (int c = 0; c < d; ++c) {
+        float a = 0.0f;
+        for (int64_t t = 0; t < n; ++t) {
+            float v = fabsf(vs[t * d + c]);
+            if (v > a) a = v;
+        }
+        if (a == 0.0f) {
+            scales[c] = 0.0f;
+            for (int64_t t = 0; t < n; ++t) codes[t * d + c] = 0;
+            continue;
+        }
+        float inv = 448.0f / a;
+        scales[c] = a / 448.0f;
+        for (int64_t t = 0; t < n; ++t)
+            codes[t * d + c] = orc_e4m3_encode_sat(vs[t * d + c] * inv);
+    }
+}
+
+/* Score bias that compensates Q smoothing (R-9): subtracting mu_q from every
+   query changes each score q_i.k_j by mu_q.k_j, which depends on j, so it is
+   added back: ds_j = sum_c mu_q[c] * k_s[j][c], accumulated in FP32 in
+   ascending c.  k_s: [n_kv][d]; ds: [n_kv].                                 */
+ORC_EXPORT void orc_delta_s(const float* mu_q, const float* ks, int64_t n_kv, int d,
+                            float* ds) {
+    for (int64_t j = 0; j < n_kv; ++j) {
+        float acc = 0.0f;
+        for (int c = 0; c < d; ++c) acc = acc + mu_q[c] * ks[j * d + c];
+        ds[j] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* S = Qc . Kc^T in int32 ([BLOG] item 2: QK in INT8).  qc [nq][d],
+   kc [nkv][d], s [nq][nkv].  |S| <= d*127^2 < 2^24 for d <= 128.           */
+ORC_EXPORT void orc_qk_int32(const int8_t* qc, const int8_t* kc, int64_t nq, int64_t nkv,
+                             int d, int32_t* s) {
+    for (int64_t i = 0; i < nq; ++i)
+        for (int64_t j = 0; j < nkv; ++j) {
+            int32_t acc = 0;
+            for (int c = 0; c < d; ++c) acc += (int32_t)qc[i * d + c] * (int32_t)kc[j * d + c];
+            s[i * nkv + j] = acc;
+        }
+}
+
+/* Last key index visible to query row i (inclusive), or nkv-1 if not causal.
+   Causal masking is aligned bottom-right (R-16): row i sees j <= i + nkv - nq. */
+static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
+    if (!causal) return nkv - 1;
+    int64_t lim = i + nkv - nq;
+    return lim < nkv - 1 ? lim : nkv - 1;
+}
+
+/* Same-recipe forward for selected query rows of one (sequence, q-head).
+ *   qc, q_scale : int8 codes [nq][d], FP32 scale per 64-token block
+ *   kc, k_scale : int8 codes [nkv][d], FP32 scale per 64-token block
+ *   vc, v_scale : e4m3 codes [nkv][d] (logical row-major), FP32 scale per channel
+ *   delta_s     : FP32 [nkv] Q-smoothing compensation, or NULL
+ *   mu_v        : FP32 [d] V mean to add back at the output, or NULL (R-10)
+ *   bkv         : key-tile width of the online softmax (R-15)
+ *   rows[nrows] : query rows to compute; out [nrows][d] FP32, lse [nrows]
+ * Steps: s = fl32(S)*(sq*sk*sm_scale) (+ ds_j*sm_scale); for each key tile in
+ * order: m' = max(m, max s), alpha = e^(m-m'), p = e^(s-m') (FP32),
+ * l = alpha*l + sum p (FP32 p, R-14), p^ = e4m3(p*448) (R-13),
+ * acc = alpha*acc + sum p^ * v^; finally o = acc*(v_scale/448)/l (+ mu_v).
+ * A row that sees no key gives o = 0 and lse = -inf (R-17).  LSE is the
+ * natural log of sum_j e^(s_j) over the scores as the recipe forms them. */
+ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
+                                     const int8_t* kc, const float* k_scale,
+                                     const uint8_t* vc, const float* v_scale,
+                                     const float* delta_s, const float* mu_v,
+                                     int64_t nq, int64_t nkv, int d, float sm_scale,
+                                     int causal, int bkv, int blk,
+                                     const int64_t* rows, int64_t nrows,
+                                     float* out, float* lse) {
+    float* s = (float*)malloc(sizeof(float) * (size_t)(bkv > 0 ? bkv : 1));
+    float* acc = (float*)malloc(sizeof(float) * (size_t)d);
+    /* decode every V code once; dec(v^) is exact in FP32 */
+    float* vdec = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1) * (size_t)d);
+    for (int64_t j = 0; j < nkv * d; ++j) vdec[j] = orc_e4m3_decode(vc[j]);
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows[r];
+        int64_t jmax = last_visible(i, nq, nkv, causal);
+        float sq = q_scale[i / blk];
+        float m = -INFINITY, l = 0.0f;
+        for (int c = 0; c < d; ++c) acc[c] = 0.0f;
+        for (int64_t t0 = 0; t0 <= jmax; t0 += bkv) {
+            int64_t t1 = t0 + bkv - 1 < jmax ? t0 + bkv - 1 : jmax;
+            int64_t nt = t1 - t0 + 1;
+            float mt = -INFINITY;
+            for (int64_t j = t0; j <= t1; ++j) {
+                int32_t S = 0;
+                for (int c = 0; c < d; ++c) S += (int32_t)qc[i * d + c] * (int32_t)kc[j * d + c];
+                float comb = sq * k_scale[j / blk];
+                comb = comb * sm_scale;
+                float sv = (float)S * comb;
+                if (delta_s) sv = sv + delta_s[j] * sm_scale;
+                s[j - t0] = sv;
+                if (sv > mt) mt = sv;
+            }
+            float mn = m > mt ? m : mt;
+            float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)(m - mn));
+            float psum = 0.0f;
+            for (int c = 0; c < d; ++c) acc[c] = alpha * acc[c];
+            for (int64_t jj = 0; jj < nt; ++jj) {
+                float p = (float)exp((double)(s[jj] - mn));
+                psum = psum + p;
+                float ph = orc_e4m3_decode(orc_e4m3_encode_sat(p * 448.0f));
+                if (ph == 0.0f) continue;     /* a zero product leaves acc as is */
+                const float* vrow = vdec + (t0 + jj) * d;
+                for (int c = 0; c < d; ++c) acc[c] = acc[c] + ph * vrow[c];
+            }
+            l = alpha * l + psum;
+            m = mn;
+        }
+        float* o = out + r * d;
+        if (jmax < 0 || l == 0.0f) {
+            for (int c = 0; c < d; ++c) o[c] = 0.0f;
+            if (lse) lse[r] = -INFINITY;
+            continue;
+        }
+        for (int c = 0; c < d; ++c) {
+            float val = acc[c] * (v_scale[c] / 448.0f) / l;
+            if (mu_v) val = val + mu_v[c];
+            o[c] = val;
+        }
+        if (lse) lse[r] = m + logf(l);
+    }
+    free(s);
+    free(acc);
+    free(vdec);
+}
+
+/* Exact softmax attention in FP64 ([SA1]: the quantity the method
+ * approximates).  q [nq][d], k [nkv][d], v [nkv][d] are the exactly decoded
+ * inputs; t_ij = sm_scale * q_i.k_j over visible j; o_i = sum_j w_ij v_j with
+ * w the softmax of t over visible j.  Rows with no visible key give 0.
+ * out [nrows][d] FP64; lse [nrows] FP64 natural-log (or NULL).             */
+ORC_EXPORT void orc_attn_exact_rows(const float* q, const float* k, const float* v,
+                                    int64_t nq, int64_t nkv, int d, double sm_scale,
+                                    int causal, const int64_t* rows, int64_t nrows,
+                                    double* out, double* lse) {
+    double* t = (double*)malloc(sizeof(double) * (size_t)(nkv > 0 ? nkv : 1));
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows[r];
+        int64_t jmax = last_visible(i, nq, nkv, causal);
+        double* o = out + r * d;
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        if (jmax < 0) { if (lse) lse[r] = -INFINITY; continue; }
+        double mx = -INFINITY;
+        for (int64_t j = 0; j <= jmax; ++j) {
+            double dot = 0.0;
+            for (int c = 0; c < d; ++c) dot += (double)q[i * d + c] * (double)k[j * d + c];
+            t[j] = sm_scale * dot;
+            if (t[j] > mx) mx = t[j];
+        }
+        double den = 0.0;
+        for (int64_t j = 0; j <= jmax; ++j) { t[j] = exp(t[j] - mx); den += t[j]; }
+        for (int64_t j = 0; j <= jmax; ++j) {
+            double w = t[j] / den;
+            for (int c = 0; c < d; ++c) o[c] += w * (double)v[j * d + c];
+        }
+        if (lse) lse[r] = mx + log(den);
+    }
+    free(t);
+}

@@ -1,0 +1,226 @@
+"""Pins of the oracle's attention functions (CPU only).
+
+* exact FP64 attention == torch's scaled_dot_product_attention in FP64 with an
+  explicit bottom-right causal mask (library routine), and its invariances
+  under a per-channel shift of K and of V;
+* int32 Q.K^T == brute force;
+* the same-recipe forward on textbook special cases (one key, uniform weights,
+  a dominant key, rows with no visible key), against exact FP64 attention on
+  tiny inputs of every head dim, its LSE, and its independence of the tile
+  width up to FP8 rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+
+def _cos(a, b):
+    a, b = np.ravel(a).astype(np.float64), np.ravel(b).astype(np.float64)
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+
+
+def _sdpa64(q, k, v, scale, causal):
+    nq, nkv = q.shape[0], k.shape[0]
+    mask = None
+    if causal:
+        i = torch.arange(nq)[:, None]
+        j = torch.arange(nkv)[None, :]
+        mask = j <= i + nkv - nq
+    t = lambda a: torch.from_numpy(a.astype(np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=mask, scale=scale)[0, 0].numpy()
+
+
+@pytest.mark.parametrize("nq,nkv,d,causal", [(17, 17, 64, False), (33, 70, 96, True),
+                                             (64, 50, 128, False), (8, 40, 64, True)])
+def test_exact_matches_torch_sdpa(orc, nq, nkv, d, causal):
+    rng = np.random.default_rng(nq + nkv)
+    q = rng.normal(0, 1, (nq, d)).astype(np.float32)
+    k = rng.normal(0, 1, (nkv, d)).astype(np.float32)
+    v = rng.normal(0, 1, (nkv, d)).astype(np.float32)
+    sc = 1 / math.sqrt(d)
+    out, lse = orc.attn_exact_rows(q, k, v, sc, causal, np.arange(nq))
+    ref = _sdpa64(q, k, v, sc, causal)
+    assert np.max(np.abs(out - ref)) < 1e-12
+    # LSE: log sum_j exp(t_ij)
+    t = (q.astype(np.float64) @ k.T.astype(np.float64)) * sc
+    if causal:
+        t = np.where(np.arange(nkv)[None, :] <= np.arange(nq)[:, None] + nkv - nq, t, -np.inf)
+    ref_lse = np.log(np.exp(t - t.max(1, keepdims=True)).sum(1)) + t.max(1)
+    assert np.max(np.abs(lse - ref_lse)) < 1e-10
+
+
+def test_exact_shift_invariance(orc):
+    rng = np.random.default_rng(5)
+    nq, nkv, d = 20, 45, 64
+    # fp16-representable inputs and a dyadic shift: K - mu and V - mu are exact
+    q = rng.normal(0, 1, (nq, d)).astype(np.float16).astype(np.float32)
+    k = rng.normal(0, 1, (nkv, d)).astype(np.float16).astype(np.float32)
+    v = rng.normal(0, 1, (nkv, d)).astype(np.float16).astype(np.float32)
+    mu = (rng.integers(-16, 16, d) / 4.0).astype(np.float32)
+    rows = np.arange(nq)
+    for causal in (False, True):
+        base, _ = orc.attn_exact_rows(q, k, v, 0.125, causal, rows)
+        ks, _ = orc.attn_exact_rows(q, k - mu, v, 0.125, causal, rows)
+        vs, _ = orc.attn_exact_rows(q, k, v - mu, 0.125, causal, rows)
+        assert np.max(np.abs(ks - base)) <= 1e-12 * np.abs(base).max()
+        assert np.max(np.abs(vs + mu - base)) <= 1e-12 * np.abs(base).max() + 1e-13
+
+
+def test_qk_int32_brute_force(orc):
+    rng = np.random.default_rng(6)
+    qc = rng.integers(-127, 128, (7, 96)).astype(np.int8)
+    kc = rng.integers(-127, 128, (9, 96)).astype(np.int8)
+    s = orc.qk_int32(qc, kc)
+    for i in range(7):
+        for j in range(9):
+            assert s[i, j] == sum(int(qc[i, c]) * int(kc[j, c]) for c in range(96))
+    # extreme codes: d * 127^2 fits in int32 and in FP32 exactly
+    big = np.full((2, 128), 127, np.int8)
+    assert orc.qk_int32(big, -big)[0, 0] == -128 * 127 * 127
+
+
+def _prob(orc, nq, nkv, d, **kw):
+    return orc.Problem("f16", "HND", kw.pop("Hq", 1), kw.pop("Hkv", 1), d, [(nq, nkv)], **kw)
+
+
+def _f16(x):
+    return np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+def _run(orc, prob, q, k, v, bkv=128):
+    pre = orc.prepass(prob, q, k, v)
+    out, lse = orc.forward_rows(prob, pre, bkv=bkv)
+    return pre, out[0], lse[0]
+
+
+def test_one_key_returns_v(orc):
+    rng = np.random.default_rng(7)
+    d = 64
+    q = _f16(rng.normal(0, 1, (1, 1, 5, d)))
+    k = _f16(rng.normal(0, 1, (1, 1, 1, d)))
+    v = _f16(rng.normal(0, 1, (1, 1, 1, d)))
+    vf = orc.decode16(v, "f16")[0, 0, 0]
+    # smooth_v: V - mean = 0 exactly, so O = mu_v = v exactly
+    _, out, _ = _run(orc, _prob(orc, 5, 1, d, smooth_v=True), q, k, v)
+    assert np.array_equal(out[0], np.broadcast_to(vf, (5, d)))
+    # without smoothing O = dec(v^) * scale_v within the FP8 error of v
+    _, out, _ = _run(orc, _prob(orc, 5, 1, d), q, k, v)
+    assert np.all(np.abs(out[0] - vf) <= np.abs(vf) * 2 ** -4 + np.abs(vf).max() * 2 ** -9)
+
+
+def test_uniform_weights(orc):
+    rng = np.random.default_rng(8)
+    d, n = 96, 150
+    v = _f16(rng.normal(0, 1, (1, 1, n, d)))
+    # constant keys: all scores equal after smoothing -> every p^ is 448 and
+    # O is the plain mean of the visible (dequantized) v rows
+    krow = rng.normal(0, 1, (1, 1, 1, d))
+    k = _f16(np.broadcast_to(krow, (1, 1, n, d)))
+    q = _f16(rng.normal(0, 1, (1, 1, n, d)))
+    vf = orc.decode16(v, "f16")[0, 0].astype(np.float64)
+    for causal in (False, True):
+        pre, out, _ = _run(orc, _prob(orc, n, n, d, causal=causal), q, k, v)
+        vq = orc.e4m3_decode(pre.vc[0][0]).astype(np.float64) * pre.vs[0][0]
+        for i in (0, 1, 63, 64, 149):
+            m = (i + 1) if causal else n
+            assert np.max(np.abs(out[0][i] - vq[:m].mean(0))) < 1e-5
+            assert np.max(np.abs(out[0][i] - vf[:m].mean(0))) < 2 ** -4 * np.abs(vf).max()
+    # q = 0 -> uniform as well
+    q0 = _f16(np.zeros((1, 1, 4, d)))
+    pre, out, _ = _run(orc, _prob(orc, 4, n, d, smooth_k=False), q0, k, v)
+    vq = orc.e4m3_decode(pre.vc[0][0]).astype(np.float64) * pre.vs[0][0]
+    assert np.max(np.abs(out[0] - vq.mean(0))) < 1e-5
+
+
+def test_dominant_key(orc):
+    rng = np.random.default_rng(9)
+    d, n = 64, 100
+    q = rng.normal(0, 1, (1, 1, 3, d))
+    k = rng.normal(0, 0.1, (1, 1, n, d))
+    k[0, 0, 37] = q[0, 0, 0] * 3.0                     # row 0 attends to key 37
+    v = rng.normal(0, 1, (1, 1, n, d))
+    qh, kh, vh = _f16(q), _f16(k), _f16(v)
+    _, out, _ = _run(orc, _prob(orc, 3, n, d, sm_scale=1.0), qh, kh, vh)
+    v37 = orc.decode16(vh, "f16")[0, 0, 37]
+    assert _cos(out[0][0], v37) > 0.999
+
+
+def test_rows_without_visible_keys(orc):
+    rng = np.random.default_rng(10)
+    d, nq, nkv = 64, 50, 20                            # rows 0..29 see nothing
+    q, k, v = (_f16(rng.normal(0, 1, (1, 1, n, d))) for n in (nq, nkv, nkv))
+    _, out, lse = _run(orc, _prob(orc, nq, nkv, d, causal=True, smooth_v=True), q, k, v)
+    assert not out[0][:30].any() and np.all(np.isneginf(lse[0][:30]))
+    assert np.all(np.isfinite(lse[0][30:])) and np.abs(out[0][30:]).min(1).max() > 0
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("nq,nkv,causal", [(65, 65, False), (33, 64, True), (64, 17, False),
+                                          (40, 65, True)])
+def test_recipe_vs_exact_tiny(orc, d, nq, nkv, causal):
+    rng = np.random.default_rng(d * 1000 + nq)
+    q = rng.normal(0, 1, (1, 2, nq, d))
+    k = rng.normal(0, 1, (1, 1, nkv, d)) + rng.normal(0, 3, (1, 1, 1, d))
+    v = rng.normal(0, 1, (1, 1, nkv, d))
+    qh, kh, vh = _f16(q), _f16(k), _f16(v)
+    prob = _prob(orc, nq, nkv, d, causal=causal, Hq=2, Hkv=1)
+    pre, out, lse = _run(orc, prob, qh, kh, vh)
+    ex, ex_lse = orc.exact_rows(prob, qh, kh, vh)
+    assert _cos(out, ex[0]) >= 0.99
+    assert np.max(np.abs(out - ex[0])) < 0.1
+    # LSE of the recipe is that of the smoothed scores: exact LSE - q.mu_k*scale
+    qf = orc.decode16(qh, "f16")[0].astype(np.float64)
+    shift = (qf @ pre.mu_k[0][0].astype(np.float64)) / math.sqrt(d)
+    assert np.max(np.abs(lse - (ex_lse[0] - shift))) < 0.05
+
+
+def test_q_and_v_smoothing_recipe(orc):
+    rng = np.random.default_rng(11)
+    d, n = 64, 130
+    q = rng.normal(0, 1, (1, 1, n, d)) + rng.normal(0, 1.5, (1, 1, 1, d))
+    k = rng.normal(0, 1, (1, 1, n, d))
+    v = rng.normal(0, 1, (1, 1, n, d)) + rng.normal(0, 1.5, (1, 1, 1, d))
+    qh, kh, vh = _f16(q), _f16(k), _f16(v)
+    prob = _prob(orc, n, n, d, smooth_q=True, smooth_v=True)
+    pre, out, _ = _run(orc, prob, qh, kh, vh)
+    ex, _ = orc.exact_rows(prob, qh, kh, vh)
+    assert pre.ds[0] is not None and pre.mu_v[0] is not None
+    assert _cos(out, ex[0]) >= 0.999
+    # dropping the compensation must visibly break the result
+    pre.ds[0] = np.zeros_like(pre.ds[0])
+    bad, _ = orc.forward_rows(prob, pre)
+    assert _cos(bad[0], ex[0]) < _cos(out, ex[0]) - 1e-3
+
+
+def test_tile_width_only_moves_fp8_rounding(orc):
+    rng = np.random.default_rng(12)
+    d, n = 128, 300
+    q, k, v = (_f16(rng.normal(0, 1, (1, 1, n, d))) for _ in range(3))
+    prob = _prob(orc, n, n, d, causal=True)
+    pre = orc.prepass(prob, q, k, v)
+    a, la = orc.forward_rows(prob, pre, bkv=16)
+    b, lb = orc.forward_rows(prob, pre, bkv=n)
+    assert np.max(np.abs(a[0] - b[0])) < 0.05 and _cos(a[0], b[0]) > 0.9995
+    assert np.max(np.abs(la[0] - lb[0])) < 1e-4
+
+
+def test_dequantized_score_bound(orc):
+    rng = np.random.default_rng(13)
+    d, n = 128, 200
+    q = rng.normal(0, 1, (n, d)).astype(np.float32)
+    k = (rng.normal(0, 1, (n, d)) + 2.0).astype(np.float32)
+    mu = orc.channel_mean(k)
+    ks = orc.smooth(k, mu)
+    qc, qsc = orc.quant_int8_blocks(q)
+    kc, ksc = orc.quant_int8_blocks(ks)
+    S = orc.qk_int32(qc, kc).astype(np.float64)
+    sq = np.repeat(qsc, 64)[:n].astype(np.float64)
+    sk = np.repeat(ksc, 64)[:n].astype(np.float64)
+    s = S * sq[:, None] * sk[None, :]
+    t = q.astype(np.float64) @ ks.T.astype(np.float64)
+    bound = (np.abs(q) @ np.ones((d, n))) * sk[None, :] / 2 \
+        + (np.ones((n, d)) @ np.abs(ks).T) * sq[:, None] / 2 + d * sq[:, None] * sk[None, :] / 4
+    assert np.all(np.abs(s - t) <= bound * (1 + 1e-6))

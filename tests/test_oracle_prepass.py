@@ -1,0 +1,125 @@
+"""Pins of the oracle's pre-pass: channel means, smoothing, INT8 per-block and
+FP8 per-channel quantization, and the Q-smoothing score bias (CPU only)."""
+import numpy as np
+import pytest
+
+
+def test_mean_closed_form_dyadic(orc):
+    # x[t,c] = o_c + e_t * z with sum_t e_t = 0 and dyadic values: every partial
+    # sum is exact in FP32, so the mean is exactly o_c.
+    rng = np.random.default_rng(0)
+    for n in (1, 2, 64, 65, 200, 1000):
+        d = 32
+        o = rng.integers(-64, 64, d) / 8.0
+        e = np.where(np.arange(n) % 2 == 0, 1.0, -1.0)
+        if n % 2:
+            e[-1] = 0.0
+        x = (o[None, :] + e[:, None] * 0.25).astype(np.float32)
+        mu = orc.channel_mean(x)
+        assert np.array_equal(mu, o.astype(np.float32)), n
+
+
+def test_mean_sequential_order_within_and_across_chunks(orc):
+    # chunk 0: 2^24 then 63 ones -> each +1 rounds back to 2^24 (ties to even)
+    x = np.ones((128, 1), np.float32)
+    x[0, 0] = 2.0 ** 24
+    # chunk 1 sums to 64 exactly; 2^24 + 64 is exact, so the total is 2^24+64
+    mu = orc.channel_mean(x)
+    assert mu[0] == np.float32((2.0 ** 24 + 64) / 128)
+    # a single chunk: the sequential FP32 order loses all 63 ones
+    mu1 = orc.channel_mean(x[:64])
+    assert mu1[0] == np.float32(2.0 ** 24 / 64)
+    # chunk sums are added in chunk order: 64 ones, then 2^24 in the next chunk
+    y = np.ones((65, 1), np.float32)
+    y[64, 0] = 2.0 ** 24
+    # chunk 0 = 64, chunk 1 = 2^24 -> 64 + 2^24 exact
+    assert orc.channel_mean(y)[0] == np.float32((64 + 2.0 ** 24) / 65)
+
+
+def test_mean_close_to_fp64(orc):
+    rng = np.random.default_rng(1)
+    x = rng.normal(3.0, 2.0, (4096, 64)).astype(np.float32)
+    mu = orc.channel_mean(x)
+    ref = x.astype(np.float64).mean(0)
+    assert np.max(np.abs(mu - ref)) < 1e-4
+
+
+def test_int8_blocks_roundtrip_bound(orc):
+    rng = np.random.default_rng(2)
+    for n in (1, 63, 64, 65, 300):
+        x = (rng.normal(0, 1, (n, 96)) * rng.uniform(0.1, 10)).astype(np.float32)
+        codes, scales = orc.quant_int8_blocks(x)
+        assert codes.dtype == np.int8 and scales.shape == (-(-n // 64),)
+        assert codes.min() >= -127 and codes.max() <= 127
+        for b in range(scales.size):
+            blk = x[64 * b:64 * (b + 1)].astype(np.float64)
+            cb = codes[64 * b:64 * (b + 1)].astype(np.float64)
+            s = float(scales[b])
+            a = np.abs(blk).max()
+            assert s == np.float32(np.float32(a) / np.float32(127.0))
+            err = np.abs(blk - s * cb)
+            assert err.max() <= s * 0.5 * (1 + 1e-5)
+            # the block's absmax element maps to +-127
+            idx = np.unravel_index(np.abs(blk).argmax(), blk.shape)
+            assert abs(cb[idx]) == 127 and np.sign(cb[idx]) == np.sign(blk[idx])
+
+
+def test_int8_zero_block(orc):
+    x = np.zeros((100, 64), np.float32)
+    x[70:, :] = 1.5
+    codes, scales = orc.quant_int8_blocks(x)
+    assert scales[0] == 0.0 and not codes[:64].any()
+    assert np.all(codes[70:] == 127) and not codes[64:70].any()
+
+
+def test_int8_rne_ties(orc):
+    # block absmax 127 -> inv = 1 exactly; x = k + 0.5 rounds to even
+    x = np.array([[127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5]], np.float32)
+    codes, scales = orc.quant_int8_blocks(x)
+    assert scales[0] == 1.0
+    assert codes[0].tolist() == [127, 0, 2, 2, 0, -2, -2, 126]
+
+
+def test_fp8_channels_bounds(orc):
+    rng = np.random.default_rng(3)
+    v = rng.normal(0, 1, (500, 64)).astype(np.float32)
+    v[:, 5] *= 10.0
+    v[:, 6] = 0.0
+    codes, scales = orc.quant_fp8_channels(v)
+    assert scales[6] == 0.0 and not codes[:, 6].any()
+    dec = orc.e4m3_decode(codes).astype(np.float64)
+    for c in range(64):
+        if c == 6:
+            continue
+        s = float(scales[c])
+        a = np.abs(v[:, c]).max()
+        assert s == np.float32(np.float32(a) / np.float32(448.0))
+        recon = dec[:, c] * s
+        x = v[:, c].astype(np.float64)
+        big = np.abs(x) >= s * 2.0 ** -6          # normal range of the codes
+        assert np.all(np.abs(recon[big] - x[big]) <= np.abs(x[big]) * 2.0 ** -4 * (1 + 1e-5))
+        assert np.all(np.abs(recon[~big] - x[~big]) <= s * 2.0 ** -10 * (1 + 1e-5))
+        # the channel absmax maps to +-448 (codes 0x7e / 0xfe)
+        i = np.abs(x).argmax()
+        assert codes[i, c] in (0x7e, 0xfe)
+
+
+def test_delta_s_compensates_q_smoothing(orc):
+    # (q - mu_q).k_s + ds = q.k_s for every pair: checks the bias's sign,
+    # index and the mean it uses.
+    rng = np.random.default_rng(4)
+    q = rng.normal(0.5, 1.0, (80, 64)).astype(np.float32)
+    k = rng.normal(0, 1, (90, 64)).astype(np.float32)
+    mu = orc.channel_mean(q)
+    qs = orc.smooth(q, mu)
+    ds = orc.delta_s(mu, k)
+    lhs = qs.astype(np.float64) @ k.T.astype(np.float64) + ds[None, :].astype(np.float64)
+    rhs = q.astype(np.float64) @ k.T.astype(np.float64)
+    assert np.max(np.abs(lhs - rhs)) < 1e-4 * np.abs(rhs).max()
+
+
+def test_smooth_is_exact_subtraction(orc):
+    x = np.array([[1.0, 2.0], [3.0, 5.0]], np.float32)
+    mu = np.array([0.5, 3.0], np.float32)
+    assert np.array_equal(orc.smooth(x, mu), np.array([[0.5, -1.0], [2.5, 2.0]], np.float32))
+    assert np.array_equal(orc.smooth(x, None), x)
