@@ -1,0 +1,180 @@
+"""Benchmark of the quantized attention forward pass on one MI355X.
+
+One step = one sage_attn_fwd call (pre-pass: means, INT8/FP8 quantization;
+then the fused INT8-QK / online-softmax / FP8-PV kernel) over the causal GQA
+workload (B=1, Hq=32, Hkv=8, N=8192, d=128, fp16, seeded synthetic inputs
+already resident in HBM).  The metric is attention TOPS with the headline
+formula 4*B*Hq*Nq*Nkv*d, halved for causal.
+
+Prints ONE JSON line.  Besides the standard fields it carries
+  roofline     : the fused kernel (the dominant launch) timed alone with HIP
+                 events on its stream, algorithmic ops (4*d per visible
+                 (q, k) pair) per launch / average launch time, against the
+                 dense INT8/FP8 MFMA peak of MI355X (5.0 POPS);
+  cpu_baseline : the CPU oracle (same recipe, plain C) timed on a bounded
+                 sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TOPS = 5000.0           # MI355X dense INT8 / FP8 MFMA peak (T-ops/s)
+WORKLOAD = "causal_gqa"
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle rows per query head")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, rows_per_head: int):
+    """Time the oracle's same-recipe forward on evenly spaced query rows of
+    every head (the pre-pass is run first and not timed)."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle as orc
+
+    def u16(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    prob = orc.problem_from_workload(w)
+    pre = orc.prepass(prob, u16(q), u16(k), u16(v))
+    threads = os.cpu_count() or 1
+    rows, pairs = [], 0
+    for nq, nkv in w.seq_lens():
+        r = np.unique(np.linspace(0, nq - 1, rows_per_head).astype(np.int64))
+        rows.append(r)
+        vis = np.minimum(nkv, np.maximum(0, r + nkv - nq + 1)) if w.causal else np.full(r.size, nkv)
+        pairs += int(vis.sum()) * w.Hq
+    t0 = time.perf_counter()
+    orc.forward_rows(prob, pre, rows=rows, bkv=128, threads=threads)
+    dt = time.perf_counter() - t0
+    ops = 4.0 * w.d * pairs
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"same-recipe forward of {sum(len(r) for r in rows)} query rows per head "
+                      f"group ({rows_per_head} evenly spaced rows x {w.Hq} heads, {pairs} visible "
+                      f"pairs, {dt:.1f} s wall), pre-pass excluded"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the forward pass shards over batch/heads with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_attention_03_amd as qa
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v, meta = synth.make_inputs(w, device=dev)
+    kw = dict(tensor_layout=w.layout, is_causal=w.causal, smooth_q=w.smooth_q,
+              smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale)
+    o = torch.empty_like(q)
+    cu = {}
+    if w.varlen:
+        cu = dict(cu_seqlens_q=meta["cu_seqlens_q"], cu_seqlens_kv=meta["cu_seqlens_kv"])
+        desc = qa.make_desc(q, k, v, o, varlen=True, **kw)
+        ws = torch.empty(qa.workspace_size(desc, cu["cu_seqlens_q"], cu["cu_seqlens_kv"]),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            qa.sage_attn_fwd_varlen(q, k, v, cu["cu_seqlens_q"], cu["cu_seqlens_kv"], out=o,
+                                    workspace=ws, **kw)
+    else:
+        desc = qa.make_desc(q, k, v, o, **kw)
+        ws = torch.empty(qa.workspace_size(desc), dtype=torch.uint8, device=dev)
+
+        def step():
+            qa.sage_attn_fwd(q, k, v, out=o, workspace=ws, **kw)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # the fused kernel alone, on buffers quantized once (one launch per call)
+    bufs = qa.sage_quant_qkv(q, k, v, **kw, **cu)
+    o2 = torch.empty_like(q)
+    for _ in range(max(3, args.warmup)):
+        qa.sage_attn_fwd_quantized(bufs, o2, **cu)
+    torch.cuda.synchronize()
+    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ka.record(stream)
+    for _ in range(args.steps):
+        qa.sage_attn_fwd_quantized(bufs, o2, **cu)
+    kb.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = ka.elapsed_time(kb) / args.steps
+    pa, pb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pa.record(stream)
+    for _ in range(args.steps):
+        qa.sage_quant_qkv(q, k, v, **kw, **cu)
+    pb.record(stream)
+    torch.cuda.synchronize()
+    pre_ms = pa.elapsed_time(pb) / args.steps
+
+    formula = w.formula_ops()
+    exact = w.exact_ops()
+    value = formula / (ms * 1e-3) / 1e12
+    achieved = exact / (kern_ms * 1e-3) / 1e12
+    line = {
+        "metric": "attention TOPS at d=128, N=8K/32K; % of dense INT8/FP8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8-qk/fp8-pv (fp16 io)" if w.dtype == "f16" else "int8-qk/fp8-pv (bf16 io)",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
+                               f"Nq=Nkv={w.Nq} d={w.d} {w.dtype} {w.layout}"
+                               f"{' causal' if w.causal else ''}",
+                   "global_batch": w.B, "seq_len": w.Nq, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TOPS, 4), "traffic": None,
+                     "kernel": "k_attn (fused INT8-QK / softmax / FP8-PV)",
+                     "kernel_ms": round(kern_ms, 4), "ops_per_launch": exact},
+        "prepass_ms": round(pre_ms, 4),
+        "exact_pair_tops": round(exact / (ms * 1e-3) / 1e12, 2),
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

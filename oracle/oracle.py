@@ -273,36 +273,45 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
     """Smoothing and quantization for every (sequence, head)."""
     qh, kh, vh = (split_heads(prob, t, w) for t, w in ((q, "q"), (k, "k"), (v, "k")))
     G = prob.Hq // prob.Hkv
-    R = Prepass()
+    S = len(prob.seqs)
 
-    def one_seq(s):
-        qf = decode16(qh[s], prob.dtype)
-        kf = decode16(kh[s], prob.dtype)
-        vf = decode16(vh[s], prob.dtype)
-        mu_q = np.stack([channel_mean(x) for x in qf]) if prob.smooth_q else None
-        mu_k = np.stack([channel_mean(x) for x in kf]) if prob.smooth_k else None
-        mu_v = np.stack([channel_mean(x) for x in vf]) if prob.smooth_v else None
-        qcs, qss, kcs, kss, vcs, vss, dss = [], [], [], [], [], [], []
-        k_s = [smooth(kf[h], None if mu_k is None else mu_k[h]) for h in range(prob.Hkv)]
-        for h in range(prob.Hq):
-            c_, s_ = quant_int8_blocks(smooth(qf[h], None if mu_q is None else mu_q[h]))
-            qcs.append(c_); qss.append(s_)
-            if prob.smooth_q:
-                dss.append(delta_s(mu_q[h], k_s[h // G]))
-        for h in range(prob.Hkv):
-            c_, s_ = quant_int8_blocks(k_s[h])
-            kcs.append(c_); kss.append(s_)
-            c_, s_ = quant_fp8_channels(smooth(vf[h], None if mu_v is None else mu_v[h]))
-            vcs.append(c_); vss.append(s_)
-        return (mu_q, mu_k, mu_v, np.stack(qcs), np.stack(qss), np.stack(kcs), np.stack(kss),
-                np.stack(vcs), np.stack(vss), np.stack(dss) if dss else None)
+    def kv_unit(u):
+        s, h = u
+        kf = decode16(kh[s][h], prob.dtype)
+        vf = decode16(vh[s][h], prob.dtype)
+        mu_k = channel_mean(kf) if prob.smooth_k else None
+        mu_v = channel_mean(vf) if prob.smooth_v else None
+        k_s = smooth(kf, mu_k)
+        kc, ks = quant_int8_blocks(k_s)
+        vc, vs = quant_fp8_channels(smooth(vf, mu_v))
+        return mu_k, mu_v, k_s, kc, ks, vc, vs
 
-    nseq = len(prob.seqs)
+    def q_unit(u, k_s):
+        s, h = u
+        qf = decode16(qh[s][h], prob.dtype)
+        mu_q = channel_mean(qf) if prob.smooth_q else None
+        qc, qs = quant_int8_blocks(smooth(qf, mu_q))
+        ds = delta_s(mu_q, k_s) if prob.smooth_q else None
+        return mu_q, qc, qs, ds
+
     with ThreadPoolExecutor(max_workers=threads or os.cpu_count()) as ex:
-        res = list(ex.map(one_seq, range(nseq)))
-    for r in res:
-        for name, val in zip(("mu_q", "mu_k", "mu_v", "qc", "qs", "kc", "ks", "vc", "vs", "ds"), r):
-            getattr(R, name).append(val)
+        kv = list(ex.map(kv_unit, [(s, h) for s in range(S) for h in range(prob.Hkv)]))
+        qq = list(ex.map(lambda u: q_unit(u, kv[u[0] * prob.Hkv + u[1] // G][2]),
+                         [(s, h) for s in range(S) for h in range(prob.Hq)]))
+    R = Prepass()
+    for s in range(S):
+        ks_ = kv[s * prob.Hkv:(s + 1) * prob.Hkv]
+        qs_ = qq[s * prob.Hq:(s + 1) * prob.Hq]
+        R.mu_k.append(np.stack([x[0] for x in ks_]) if prob.smooth_k else None)
+        R.mu_v.append(np.stack([x[1] for x in ks_]) if prob.smooth_v else None)
+        R.kc.append(np.stack([x[3] for x in ks_]))
+        R.ks.append(np.stack([x[4] for x in ks_]))
+        R.vc.append(np.stack([x[5] for x in ks_]))
+        R.vs.append(np.stack([x[6] for x in ks_]))
+        R.mu_q.append(np.stack([x[0] for x in qs_]) if prob.smooth_q else None)
+        R.qc.append(np.stack([x[1] for x in qs_]))
+        R.qs.append(np.stack([x[2] for x in qs_]))
+        R.ds.append(np.stack([x[3] for x in qs_]) if prob.smooth_q else None)
     return R
 
 

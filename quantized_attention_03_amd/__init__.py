@@ -1,0 +1,236 @@
+"""Thin Python binding of libsage (include/sage.h): argument marshalling only.
+
+Every step of the forward pass runs in the HIP library; PyTorch provides the
+device memory and the stream.  If libsage.so has not been built, every call
+raises (there is no CPU or eager fallback).
+
+    from quantized_attention_03_amd import sageattn
+    o = sageattn(q, k, v, tensor_layout="HND", is_causal=False, smooth_k=True)
+
+mirrors the `sageattn` call of the "sageattention" package page (Quickstart).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _abi
+from ._abi import BF16, F16, HND, NHD, KV_TILE, QK_BLOCK, SageError, lib
+
+__all__ = ["sageattn", "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_quant_qkv",
+           "sage_attn_fwd_quantized",
+           "sage_debug_qk_int32", "workspace_size", "quant_buf_sizes", "make_desc",
+           "SageError", "lib", "abi_version"]
+
+_DT = {torch.float16: F16, torch.bfloat16: BF16}
+
+
+def abi_version() -> int:
+    return lib().sage_abi_version()
+
+
+def _strides(t: torch.Tensor, layout: str, varlen: bool):
+    if t.stride(-1) != 1:
+        raise ValueError("the head_dim dimension must have stride 1")
+    s = t.stride()
+    if varlen:
+        return (0, s[1], s[0]) if layout == "NHD" else (0, s[0], s[1])
+    return (s[0], s[2], s[1]) if layout == "NHD" else (s[0], s[1], s[2])
+
+
+def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q=False,
+              smooth_k=True, smooth_v=False, sm_scale=None, varlen=False) -> _abi.Desc:
+    """Descriptor for q/k/v torch tensors (dense [B,H,N,d] / [B,N,H,d], or packed
+    varlen [T,H,d] / [H,T,d])."""
+    if tensor_layout not in ("HND", "NHD"):
+        raise ValueError(f"tensor_layout must be 'HND' or 'NHD', got {tensor_layout!r}")
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    d = _abi.Desc()
+    lay = NHD if tensor_layout == "NHD" else HND
+    hd = q.shape[-1]
+    if varlen:
+        hq = q.shape[1] if lay == NHD else q.shape[0]
+        hkv = k.shape[1] if lay == NHD else k.shape[0]
+        lib().sage_desc_init(ctypes.byref(d), _DT[q.dtype], lay, 0, hq, hkv, 0, 0, hd)
+    else:
+        B = q.shape[0]
+        if lay == NHD:
+            nq, hq, nkv, hkv = q.shape[1], q.shape[2], k.shape[1], k.shape[2]
+        else:
+            hq, nq, hkv, nkv = q.shape[1], q.shape[2], k.shape[1], k.shape[2]
+        lib().sage_desc_init(ctypes.byref(d), _DT[q.dtype], lay, B, hq, hkv, nq, nkv, hd)
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o if o is not None else q)):
+        arr = getattr(d, name)
+        for i, x in enumerate(_strides(t, tensor_layout, varlen)):
+            arr[i] = x
+    d.is_causal = int(bool(is_causal))
+    d.smooth_q = int(bool(smooth_q))
+    d.smooth_k = int(bool(smooth_k))
+    d.smooth_v = int(bool(smooth_v))
+    d.sm_scale = float(sm_scale) if sm_scale else 0.0
+    return d
+
+
+def _cu(cu):
+    if cu is None:
+        return None, 0
+    vals = [int(x) for x in (cu.tolist() if isinstance(cu, torch.Tensor) else cu)]
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    return arr, len(vals) - 1
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def workspace_size(desc, cu_seqlens_q=None, cu_seqlens_kv=None) -> int:
+    cq, n = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_kv)
+    out = ctypes.c_size_t(0)
+    _abi.check("sage_workspace_size",
+               lib().sage_workspace_size(ctypes.byref(desc), cq, ck, n, ctypes.byref(out)))
+    return out.value
+
+
+def quant_buf_sizes(desc, cu_seqlens_q=None, cu_seqlens_kv=None) -> dict:
+    cq, n = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_kv)
+    z = _abi.QuantSizes()
+    _abi.check("sage_quant_buf_sizes",
+               lib().sage_quant_buf_sizes(ctypes.byref(desc), cq, ck, n, ctypes.byref(z)))
+    return {name: getattr(z, name) for name, _ in _abi.QuantSizes._fields_}
+
+
+_BUF_DT = {"mu_q": torch.float32, "mu_k": torch.float32, "mu_v": torch.float32,
+           "q_codes": torch.int8, "q_scale": torch.float32, "k_codes": torch.int8,
+           "k_scale": torch.float32, "v_codes": torch.uint8, "v_scale": torch.float32,
+           "delta_s": torch.float32}
+
+
+def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
+                   smooth_k=True, smooth_v=False, sm_scale=None, cu_seqlens_q=None,
+                   cu_seqlens_kv=None):
+    """Run the pre-pass alone; returns a dict of flat device tensors laid out as
+    documented for sage_quant_bufs in include/sage.h."""
+    varlen = cu_seqlens_q is not None
+    desc = make_desc(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal,
+                     smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
+                     sm_scale=sm_scale, varlen=varlen)
+    sizes = quant_buf_sizes(desc, cu_seqlens_q, cu_seqlens_kv)
+    bufs = {name: torch.zeros(max(1, nbytes // torch.empty((), dtype=_BUF_DT[name]).element_size()),
+                              dtype=_BUF_DT[name], device=q.device)
+            for name, nbytes in sizes.items()}
+    qb = _abi.QuantBufs(**{name: (t.data_ptr() if sizes[name] else None) for name, t in bufs.items()})
+    ws = torch.empty(workspace_size(desc, cu_seqlens_q, cu_seqlens_kv), dtype=torch.uint8,
+                     device=q.device)
+    cq, n = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_kv)
+    _abi.check("sage_quant_qkv",
+               lib().sage_quant_qkv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), cq, ck, n,
+                                    ctypes.byref(qb), _ptr(ws), ws.numel(), _stream(q)))
+    bufs["_desc"] = desc
+    bufs["_workspace"] = ws
+    bufs["_sizes"] = sizes
+    return bufs
+
+
+def quant_bufs_struct(bufs) -> _abi.QuantBufs:
+    """ctypes sage_quant_bufs for a dict returned by sage_quant_qkv."""
+    sizes = bufs["_sizes"]
+    return _abi.QuantBufs(**{name: (bufs[name].data_ptr() if sizes[name] else None)
+                             for name in sizes})
+
+
+def sage_attn_fwd_quantized(bufs, out, *, cu_seqlens_q=None, cu_seqlens_kv=None, lse=None):
+    """The fused kernel alone on buffers from sage_quant_qkv (same problem).
+    `out` has q's shape and dtype; lse (optional) is FP32 as in sage_attn_fwd."""
+    desc = bufs["_desc"]
+    cq, n = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_kv)
+    qb = quant_bufs_struct(bufs)
+    _abi.check("sage_attn_fwd_quantized",
+               lib().sage_attn_fwd_quantized(ctypes.byref(desc), cq, ck, n, ctypes.byref(qb),
+                                             _ptr(out), _ptr(lse), _stream(out)))
+    return out
+
+
+def sage_debug_qk_int32(bufs, *, cu_seqlens_q=None, cu_seqlens_kv=None, device=None):
+    """int32 Q.K^T of the codes produced by sage_quant_qkv (same desc)."""
+    desc = bufs["_desc"]
+    cq, n = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_kv)
+    if cq is None:
+        total = desc.batch * desc.hq * desc.nq * desc.nkv
+    else:
+        lq = [cq[i + 1] - cq[i] for i in range(n)]
+        lk = [ck[i + 1] - ck[i] for i in range(n)]
+        total = sum(desc.hq * a * b for a, b in zip(lq, lk))
+    dev = device or bufs["q_codes"].device
+    out = torch.empty(max(1, total), dtype=torch.int32, device=dev)
+    qb = _abi.QuantBufs(q_codes=bufs["q_codes"].data_ptr(), k_codes=bufs["k_codes"].data_ptr())
+    _abi.check("sage_debug_qk_int32",
+               lib().sage_debug_qk_int32(ctypes.byref(desc), cq, ck, n, ctypes.byref(qb),
+                                         _ptr(out), _stream(out)))
+    return out[:total]
+
+
+def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
+                  smooth_k=True, smooth_v=False, sm_scale=None, return_lse=False,
+                  out=None, workspace=None):
+    """Dense forward pass.  Returns o (and lse [B, hq, nq] FP32 if asked)."""
+    o = torch.empty_like(q) if out is None else out
+    desc = make_desc(q, k, v, o, tensor_layout=tensor_layout, is_causal=is_causal,
+                     smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
+                     sm_scale=sm_scale)
+    lse = None
+    if return_lse:
+        lse = torch.empty((desc.batch, desc.hq, desc.nq), dtype=torch.float32, device=q.device)
+    need = workspace_size(desc)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _abi.check("sage_attn_fwd",
+               lib().sage_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q)))
+    return (o, lse) if return_lse else o
+
+
+def sage_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, tensor_layout="NHD",
+                         is_causal=False, smooth_q=False, smooth_k=True, smooth_v=False,
+                         sm_scale=None, return_lse=False, out=None, workspace=None):
+    """Packed variable-length forward pass (q [T,H,d] for NHD or [H,T,d] for
+    HND; cu_seqlens are host int32 prefix offsets).  lse is [hq, T_q]."""
+    o = torch.empty_like(q) if out is None else out
+    desc = make_desc(q, k, v, o, tensor_layout=tensor_layout, is_causal=is_causal,
+                     smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
+                     sm_scale=sm_scale, varlen=True)
+    cq, n = _cu(cu_seqlens_q)
+    ck, nk = _cu(cu_seqlens_kv)
+    if nk != n:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must have the same length")
+    lse = None
+    if return_lse:
+        tq = cq[n] if n > 0 else 0
+        lse = torch.empty((desc.hq, tq), dtype=torch.float32, device=q.device)
+    need = workspace_size(desc, cu_seqlens_q, cu_seqlens_kv)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _abi.check("sage_attn_fwd_varlen",
+               lib().sage_attn_fwd_varlen(ctypes.byref(desc), cq, ck, n, _ptr(q), _ptr(k),
+                                          _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                                          workspace.numel(), _stream(q)))
+    return (o, lse) if return_lse else o
+
+
+def sageattn(q, k, v, tensor_layout="HND", is_causal=False, smooth_k=True, sm_scale=None,
+             smooth_q=False, smooth_v=False, return_lse=False):
+    """The package page's call: attention output of the quantized forward pass."""
+    return sage_attn_fwd(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal,
+                         smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
+                         sm_scale=sm_scale, return_lse=return_lse)

@@ -1,0 +1,520 @@
+// sage_api.cpp -- host side of libsage: argument checks, workspace plan,
+// sequence tables and the launch sequence of the pre-pass and the fused
+// kernel.  The C ABI is declared (and documented) in include/sage.h.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "sage.h"
+#include "sage_internal.h"
+
+using namespace sage;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t al(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Everything the host derives from a descriptor (and cu_seqlens).
+struct Plan {
+    int S = 0;
+    bool varlen = false;
+    int d = 0, hq = 0, hkv = 0, group = 1;
+    std::vector<int32_t> nq, nkv, tq, tk;
+    std::vector<int64_t> rq, rk;      // padded row bases per sequence
+    int64_t rows_q = 0, rows_k = 0;   // sum of padded lengths
+    int64_t total_q = 0;              // packed query tokens (varlen) for lse
+    Strides qs{}, ks{}, vs{}, os{};
+    float sm_scale = 0.0f;
+    bool causal = false, smooth_q = false, smooth_k = false, smooth_v = false;
+};
+
+// Byte offsets of everything placed in a workspace (quantized tensors first,
+// then scratch).  `quant_in_ws` = false gives the scratch-only layout used by
+// sage_quant_qkv (whose quantized tensors are caller buffers).
+struct WsLayout {
+    size_t mu_q, mu_k, mu_v, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, delta_s;
+    size_t part_q, part_k, part_v, part_vmax, v_amax;
+    size_t total;
+};
+
+sage_quant_sizes quant_sizes(const Plan& p) {
+    sage_quant_sizes z{};
+    const size_t S = p.S, d = p.d;
+    z.mu_q = p.smooth_q ? S * p.hq * d * 4 : 0;
+    z.mu_k = p.smooth_k ? S * p.hkv * d * 4 : 0;
+    z.mu_v = p.smooth_v ? S * p.hkv * d * 4 : 0;
+    z.q_codes = (size_t)p.rows_q * p.hq * d;
+    z.q_scale = (size_t)p.rows_q * p.hq / QBLK * 4;
+    z.k_codes = (size_t)p.rows_k * p.hkv * d;
+    z.k_scale = (size_t)p.rows_k * p.hkv / QBLK * 4;
+    z.v_codes = (size_t)p.rows_k * p.hkv * d;
+    z.v_scale = S * p.hkv * d * 4;
+    z.delta_s = p.smooth_q ? (size_t)p.rows_k * p.hq * 4 : 0;
+    return z;
+}
+
+WsLayout ws_layout(const Plan& p, bool quant_in_ws) {
+    WsLayout w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += al(bytes);
+        return o;
+    };
+    if (quant_in_ws) {
+        const sage_quant_sizes z = quant_sizes(p);
+        w.mu_q = take(z.mu_q);
+        w.mu_k = take(z.mu_k);
+        w.mu_v = take(z.mu_v);
+        w.q_codes = take(z.q_codes);
+        w.q_scale = take(z.q_scale);
+        w.k_codes = take(z.k_codes);
+        w.k_scale = take(z.k_scale);
+        w.v_codes = take(z.v_codes);
+        w.v_scale = take(z.v_scale);
+        w.delta_s = take(z.delta_s);
+    }
+    const size_t d = p.d;
+    w.part_q = take(p.smooth_q ? (size_t)p.rows_q / QBLK * p.hq * d * 4 : 0);
+    w.part_k = take(p.smooth_k ? (size_t)p.rows_k / QBLK * p.hkv * d * 4 : 0);
+    w.part_v = take(p.smooth_v ? (size_t)p.rows_k / QBLK * p.hkv * d * 4 : 0);
+    w.part_vmax = take((size_t)p.rows_k / QBLK * p.hkv * d * 4);
+    w.v_amax = take((size_t)p.S * p.hkv * d * 4);
+    w.total = off + ALIGN;   // slack so that an unaligned base can be rounded up
+    return w;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool flag_ok(int32_t f) { return f == 0 || f == 1; }
+
+// Checks on the descriptor and cu_seqlens (host only, no HIP call).
+sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int32_t* cuk,
+                      int32_t nseq, bool varlen, Plan* out) {
+    if (!desc) return SAGE_ERR_NULL;
+    if (varlen && (!cuq || !cuk)) return SAGE_ERR_NULL;
+    const sage_attn_desc& D = *desc;
+    if (D.dtype != SAGE_F16 && D.dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+    if (D.layout != SAGE_HND && D.layout != SAGE_NHD) return SAGE_ERR_LAYOUT;
+    if (!flag_ok(D.is_causal) || !flag_ok(D.smooth_q) || !flag_ok(D.smooth_k) ||
+        !flag_ok(D.smooth_v) || D.reserved[0] || D.reserved[1] || D.reserved[2] ||
+        !std::isfinite(D.sm_scale))
+        return SAGE_ERR_FLAGS;
+    if (D.head_dim != 64 && D.head_dim != 96 && D.head_dim != 128) return SAGE_ERR_HEAD_DIM;
+    if (D.hq < 1 || D.hkv < 1 || D.hq > 65536 || D.hkv > 65536) return SAGE_ERR_SHAPE;
+    if (!varlen && (D.batch < 0 || D.nq < 0 || D.nkv < 0 || D.nq > (1 << 24) ||
+                    D.nkv > (1 << 24) || D.batch > (1 << 20)))
+        return SAGE_ERR_SHAPE;
+    if (varlen && (nseq < 0 || nseq > (1 << 20))) return SAGE_ERR_SHAPE;
+    if (D.hq % D.hkv != 0) return SAGE_ERR_GQA;
+    const int64_t* st[4] = {D.q_stride, D.k_stride, D.v_stride, D.o_stride};
+    for (auto s : st)
+        for (int i = 0; i < 3; ++i)
+            if (s[i] < 0 || s[i] % 8 != 0) return SAGE_ERR_STRIDE;
+
+    Plan p;
+    p.varlen = varlen;
+    p.d = D.head_dim;
+    p.hq = D.hq;
+    p.hkv = D.hkv;
+    p.group = D.hq / D.hkv;
+    p.causal = D.is_causal;
+    p.smooth_q = D.smooth_q;
+    p.smooth_k = D.smooth_k;
+    p.smooth_v = D.smooth_v;
+    p.sm_scale = D.sm_scale > 0.0f ? D.sm_scale : 1.0f / std::sqrt((float)D.head_dim);
+    if (varlen) {
+        if (cuq[0] != 0 || cuk[0] != 0) return SAGE_ERR_SEQLENS;
+        p.S = nseq;
+        for (int s = 0; s < nseq; ++s) {
+            const int64_t lq = (int64_t)cuq[s + 1] - cuq[s];
+            const int64_t lk = (int64_t)cuk[s + 1] - cuk[s];
+            if (lq < 0 || lk < 0 || lq > (1 << 24) || lk > (1 << 24)) return SAGE_ERR_SEQLENS;
+            p.nq.push_back((int32_t)lq);
+            p.nkv.push_back((int32_t)lk);
+            p.tq.push_back(cuq[s]);
+            p.tk.push_back(cuk[s]);
+        }
+        p.total_q = nseq > 0 ? cuq[nseq] : 0;
+    } else {
+        p.S = D.batch;
+        p.nq.assign(p.S, D.nq);
+        p.nkv.assign(p.S, D.nkv);
+        p.tq.assign(p.S, 0);
+        p.tk.assign(p.S, 0);
+        p.total_q = (int64_t)D.batch * D.nq;
+    }
+    for (int s = 0; s < p.S; ++s) {
+        p.rq.push_back(p.rows_q);
+        p.rk.push_back(p.rows_k);
+        p.rows_q += round_up(p.nq[s], QBLK);
+        p.rows_k += round_up(p.nkv[s], KVT);
+    }
+    // strides: all-zero triple = contiguous in the layout
+    const int64_t d = D.head_dim;
+    auto fill = [&](const int64_t* in, int heads, int64_t n, Strides* o) {
+        if (in[0] || in[1] || in[2]) {
+            *o = Strides{in[0], in[1], in[2]};
+            return;
+        }
+        if (D.layout == SAGE_HND) {
+            // dense [B,H,N,d]; varlen [H,T,d]
+            *o = Strides{heads * n * d, n * d, d};
+        } else {
+            // dense [B,N,H,d]; varlen [T,H,d]
+            *o = Strides{n * heads * d, d, heads * d};
+        }
+    };
+    int64_t tot_k = 0;
+    if (varlen) tot_k = nseq > 0 ? cuk[nseq] : 0;
+    fill(D.q_stride, D.hq, varlen ? p.total_q : D.nq, &p.qs);
+    fill(D.k_stride, D.hkv, varlen ? tot_k : D.nkv, &p.ks);
+    fill(D.v_stride, D.hkv, varlen ? tot_k : D.nkv, &p.vs);
+    fill(D.o_stride, D.hq, varlen ? p.total_q : D.nq, &p.os);
+    *out = std::move(p);
+    return SAGE_OK;
+}
+
+// gfx950 check, cached per device.
+sage_status check_arch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SAGE_ERR_HIP;
+    static std::mutex mu;
+    static std::vector<int> known;   // 0 unknown, 1 ok, 2 bad
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)known.size() <= dev) known.resize(dev + 1, 0);
+    if (known[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SAGE_ERR_HIP;
+        known[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return known[dev] == 1 ? SAGE_OK : SAGE_ERR_ARCH;
+}
+
+// Kernel parameter blocks: one per group of at most MAXSEQ sequences.  Dense
+// problems need a single uniform table.  Varlen sequences are ordered by
+// descending work so that the heaviest are dispatched first.
+std::vector<KParams> make_params(const Plan& p) {
+    KParams base{};
+    base.d = p.d;
+    base.hq = p.hq;
+    base.hkv = p.hkv;
+    base.group = p.group;
+    base.causal = p.causal;
+    base.sm_scale = p.sm_scale;
+    base.sml2 = (float)((double)p.sm_scale * 1.4426950408889634);
+    base.qs = p.qs;
+    base.ks = p.ks;
+    base.vs = p.vs;
+    base.os = p.os;
+    std::vector<KParams> out;
+    if (!p.varlen) {
+        if (p.S == 0) return out;
+        KParams k = base;
+        k.lse_hstride = p.nq[0];
+        k.tab.n = p.S;
+        k.tab.uniform = 1;
+        k.tab.nq[0] = p.nq[0];
+        k.tab.nkv[0] = p.nkv[0];
+        out.push_back(k);
+        return out;
+    }
+    std::vector<int> order(p.S);
+    for (int s = 0; s < p.S; ++s) order[s] = s;
+    auto cost = [&](int s) {
+        const double nq = p.nq[s], nkv = p.nkv[s];
+        return p.causal ? nq * nkv - 0.5 * std::min(nq, nkv) * std::min(nq, nkv) : nq * nkv;
+    };
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost(a) > cost(b); });
+    for (size_t i0 = 0; i0 < order.size(); i0 += MAXSEQ) {
+        KParams k = base;
+        k.lse_hstride = p.total_q;
+        k.tab.uniform = 0;
+        k.tab.n = (int)std::min<size_t>(MAXSEQ, order.size() - i0);
+        for (int j = 0; j < k.tab.n; ++j) {
+            const int s = order[i0 + j];
+            k.tab.nq[j] = p.nq[s];
+            k.tab.nkv[j] = p.nkv[s];
+            k.tab.tq[j] = p.tq[s];
+            k.tab.tk[j] = p.tk[s];
+            k.tab.rq[j] = p.rq[s];
+            k.tab.rk[j] = p.rk[s];
+            k.tab.sid[j] = s;
+            k.tab.lse_base[j] = p.tq[s];
+        }
+        out.push_back(k);
+    }
+    return out;
+}
+
+// Blocks of a launch over (head, 64-token chunk) pairs for one table.
+int chunk_blocks(const KParams& k, bool is_q, int heads, bool padded) {
+    int tot = 0;
+    const int n = k.tab.uniform ? 1 : k.tab.n;
+    for (int s = 0; s < n; ++s) {
+        const int len = is_q ? k.tab.nq[s] : k.tab.nkv[s];
+        const int np = padded ? round_up(len, is_q ? QBLK : KVT) : round_up(len, QBLK);
+        tot += heads * (np / QBLK);
+    }
+    return k.tab.uniform ? tot * k.tab.n : tot;
+}
+
+int tab_seqs(const KParams& k) { return k.tab.n; }
+
+#define SAGE_TRY(x)                                  \
+    do {                                             \
+        if ((x) != hipSuccess) return SAGE_ERR_HIP;  \
+    } while (0)
+
+// The pre-pass.  `bufs` are the destination tensors, `sc` the scratch area.
+sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype, const void* q,
+                        const void* k, const void* v, const sage_quant_bufs& b, uint8_t* sc,
+                        const WsLayout& w, hipStream_t st) {
+    float* part_q = reinterpret_cast<float*>(sc + w.part_q);
+    float* part_k = reinterpret_cast<float*>(sc + w.part_k);
+    float* part_v = reinterpret_cast<float*>(sc + w.part_v);
+    float* part_vmax = reinterpret_cast<float*>(sc + w.part_vmax);
+    float* v_amax = reinterpret_cast<float*>(sc + w.v_amax);
+    for (const KParams& P : kp) {
+        if (p.smooth_k) {
+            SAGE_TRY(launch_stats(P, dtype, STAT_SUM, k, P.ks, 1, p.hkv, nullptr, part_k,
+                                  chunk_blocks(P, false, p.hkv, false), st));
+            SAGE_TRY(launch_finalize(P, STAT_SUM, false, p.hkv, part_k, b.mu_k, nullptr, nullptr,
+                                     tab_seqs(P), st));
+        }
+        if (p.smooth_q) {
+            SAGE_TRY(launch_stats(P, dtype, STAT_SUM, q, P.qs, 0, p.hq, nullptr, part_q,
+                                  chunk_blocks(P, true, p.hq, false), st));
+            SAGE_TRY(launch_finalize(P, STAT_SUM, true, p.hq, part_q, b.mu_q, nullptr, nullptr,
+                                     tab_seqs(P), st));
+        }
+        if (p.smooth_v) {
+            SAGE_TRY(launch_stats(P, dtype, STAT_SUM, v, P.vs, 2, p.hkv, nullptr, part_v,
+                                  chunk_blocks(P, false, p.hkv, false), st));
+            SAGE_TRY(launch_finalize(P, STAT_SUM, false, p.hkv, part_v, b.mu_v, nullptr, nullptr,
+                                     tab_seqs(P), st));
+        }
+        SAGE_TRY(launch_stats(P, dtype, STAT_ABSMAX, v, P.vs, 2, p.hkv,
+                              p.smooth_v ? b.mu_v : nullptr, part_vmax,
+                              chunk_blocks(P, false, p.hkv, false), st));
+        SAGE_TRY(launch_finalize(P, STAT_ABSMAX, false, p.hkv, part_vmax, nullptr, v_amax,
+                                 b.v_scale, tab_seqs(P), st));
+        SAGE_TRY(launch_quant_qk(P, dtype, q, P.qs, true, p.hq, p.smooth_q ? b.mu_q : nullptr,
+                                 b.q_codes, b.q_scale, nullptr, nullptr,
+                                 chunk_blocks(P, true, p.hq, true), st));
+        SAGE_TRY(launch_quant_qk(P, dtype, k, P.ks, false, p.hkv, p.smooth_k ? b.mu_k : nullptr,
+                                 b.k_codes, b.k_scale, p.smooth_q ? b.mu_q : nullptr,
+                                 p.smooth_q ? b.delta_s : nullptr,
+                                 chunk_blocks(P, false, p.hkv, true), st));
+        SAGE_TRY(launch_quant_v(P, dtype, v, p.smooth_v ? b.mu_v : nullptr, v_amax, b.v_codes,
+                                chunk_blocks(P, false, p.hkv, true), st));
+    }
+    return SAGE_OK;
+}
+
+uint8_t* align_up(void* p) {
+    uintptr_t u = reinterpret_cast<uintptr_t>(p);
+    return reinterpret_cast<uint8_t*>((u + ALIGN - 1) / ALIGN * ALIGN);
+}
+
+sage_quant_bufs bufs_in_ws(const Plan& p, uint8_t* ws, const WsLayout& w) {
+    sage_quant_bufs b{};
+    b.mu_q = p.smooth_q ? reinterpret_cast<float*>(ws + w.mu_q) : nullptr;
+    b.mu_k = p.smooth_k ? reinterpret_cast<float*>(ws + w.mu_k) : nullptr;
+    b.mu_v = p.smooth_v ? reinterpret_cast<float*>(ws + w.mu_v) : nullptr;
+    b.q_codes = reinterpret_cast<int8_t*>(ws + w.q_codes);
+    b.q_scale = reinterpret_cast<float*>(ws + w.q_scale);
+    b.k_codes = reinterpret_cast<int8_t*>(ws + w.k_codes);
+    b.k_scale = reinterpret_cast<float*>(ws + w.k_scale);
+    b.v_codes = reinterpret_cast<uint8_t*>(ws + w.v_codes);
+    b.v_scale = reinterpret_cast<float*>(ws + w.v_scale);
+    b.delta_s = p.smooth_q ? reinterpret_cast<float*>(ws + w.delta_s) : nullptr;
+    return b;
+}
+
+sage_status forward(const sage_attn_desc* desc, const int32_t* cuq, const int32_t* cuk,
+                    int32_t nseq, bool varlen, const void* q, const void* k, const void* v,
+                    void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    sage_status e = make_plan(desc, cuq, cuk, nseq, varlen, &p);
+    if (e != SAGE_OK) return e;
+    const bool empty = p.S == 0 || p.total_q == 0;
+    if (!empty && (!q || !o || (p.rows_k > 0 && (!k || !v)) || !ws)) return SAGE_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return SAGE_ERR_ALIGN;
+    const WsLayout w = ws_layout(p, true);
+    if (!empty && ws_bytes < w.total) return SAGE_ERR_WORKSPACE;
+    if ((e = check_arch()) != SAGE_OK) return e;
+    if (empty) return SAGE_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* base = align_up(ws);
+    const sage_quant_bufs b = bufs_in_ws(p, base, w);
+    const std::vector<KParams> kp = make_params(p);
+    if ((e = run_prepass(p, kp, desc->dtype, q, k, v, b, base, w, st)) != SAGE_OK) return e;
+    for (const KParams& P : kp)
+        SAGE_TRY(launch_attn(P, desc->dtype, b.q_codes, b.q_scale, b.k_codes, b.k_scale,
+                             b.v_codes, b.v_scale, b.delta_s, b.mu_v, o, lse,
+                             attn_blocks_host(P), st));
+    return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void sage_desc_init(sage_attn_desc* desc, int32_t dtype, int32_t layout, int32_t batch,
+                    int32_t hq, int32_t hkv, int32_t nq, int32_t nkv, int32_t head_dim) {
+    if (!desc) return;
+    std::memset(desc, 0, sizeof(*desc));
+    desc->dtype = dtype;
+    desc->layout = layout;
+    desc->batch = batch;
+    desc->hq = hq;
+    desc->hkv = hkv;
+    desc->nq = nq;
+    desc->nkv = nkv;
+    desc->head_dim = head_dim;
+    desc->smooth_k = 1;
+    desc->sm_scale = 0.0f;
+}
+
+sage_status sage_quant_buf_sizes(const sage_attn_desc* desc, const int32_t* cuq,
+                                 const int32_t* cuk, int32_t nseq, sage_quant_sizes* sizes) {
+    if (!sizes) return SAGE_ERR_NULL;
+    Plan p;
+    const sage_status e = make_plan(desc, cuq, cuk, nseq, cuq != nullptr, &p);
+    if (e != SAGE_OK) return e;
+    *sizes = quant_sizes(p);
+    return SAGE_OK;
+}
+
+sage_status sage_workspace_size(const sage_attn_desc* desc, const int32_t* cuq,
+                                const int32_t* cuk, int32_t nseq, size_t* bytes) {
+    if (!bytes) return SAGE_ERR_NULL;
+    Plan p;
+    const sage_status e = make_plan(desc, cuq, cuk, nseq, cuq != nullptr, &p);
+    if (e != SAGE_OK) return e;
+    *bytes = ws_layout(p, true).total;
+    return SAGE_OK;
+}
+
+sage_status sage_quant_qkv(const sage_attn_desc* desc, const void* q, const void* k,
+                           const void* v, const int32_t* cuq, const int32_t* cuk, int32_t nseq,
+                           const sage_quant_bufs* out, void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    sage_status e = make_plan(desc, cuq, cuk, nseq, cuq != nullptr, &p);
+    if (e != SAGE_OK) return e;
+    if (!out) return SAGE_ERR_NULL;
+    const bool empty = p.S == 0;
+    if (!empty) {
+        if (!q || !k || !v || !ws || !out->q_codes || !out->q_scale || !out->k_codes ||
+            !out->k_scale || !out->v_codes || !out->v_scale || (p.smooth_q && !out->mu_q) ||
+            (p.smooth_k && !out->mu_k) || (p.smooth_v && !out->mu_v) ||
+            (p.smooth_q && !out->delta_s))
+            return SAGE_ERR_NULL;
+    }
+    const void* ptrs[] = {q, k, v, out->q_codes, out->k_codes, out->v_codes, out->q_scale,
+                          out->k_scale, out->v_scale, out->mu_q, out->mu_k, out->mu_v,
+                          out->delta_s};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return SAGE_ERR_ALIGN;
+    const WsLayout w = ws_layout(p, false);
+    if (!empty && ws_bytes < w.total) return SAGE_ERR_WORKSPACE;
+    if ((e = check_arch()) != SAGE_OK) return e;
+    if (empty) return SAGE_OK;
+    const std::vector<KParams> kp = make_params(p);
+    return run_prepass(p, kp, desc->dtype, q, k, v, *out, align_up(ws), w,
+                       static_cast<hipStream_t>(stream));
+}
+
+sage_status sage_attn_fwd(const sage_attn_desc* desc, const void* q, const void* k,
+                          const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                          void* stream) {
+    return forward(desc, nullptr, nullptr, 0, false, q, k, v, o, lse, ws, ws_bytes, stream);
+}
+
+sage_status sage_attn_fwd_varlen(const sage_attn_desc* desc, const int32_t* cuq,
+                                 const int32_t* cuk, int32_t nseq, const void* q, const void* k,
+                                 const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    return forward(desc, cuq, cuk, nseq, true, q, k, v, o, lse, ws, ws_bytes, stream);
+}
+
+sage_status sage_attn_fwd_quantized(const sage_attn_desc* desc, const int32_t* cuq,
+                                    const int32_t* cuk, int32_t nseq, const sage_quant_bufs* b,
+                                    void* o, float* lse, void* stream) {
+    Plan p;
+    sage_status e = make_plan(desc, cuq, cuk, nseq, cuq != nullptr, &p);
+    if (e != SAGE_OK) return e;
+    if (!b) return SAGE_ERR_NULL;
+    const bool empty = p.S == 0 || p.total_q == 0;
+    if (!empty && (!o || !b->q_codes || !b->q_scale || !b->k_codes || !b->k_scale ||
+                   !b->v_codes || !b->v_scale || (p.smooth_q && !b->delta_s) ||
+                   (p.smooth_v && !b->mu_v)))
+        return SAGE_ERR_NULL;
+    const void* ptrs[] = {o, b->q_codes, b->k_codes, b->v_codes, b->q_scale, b->k_scale,
+                          b->v_scale, b->mu_v, b->delta_s};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return SAGE_ERR_ALIGN;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return SAGE_ERR_ALIGN;
+    if ((e = check_arch()) != SAGE_OK) return e;
+    if (empty) return SAGE_OK;
+    for (const KParams& P : make_params(p))
+        SAGE_TRY(launch_attn(P, desc->dtype, b->q_codes, b->q_scale, b->k_codes, b->k_scale,
+                             b->v_codes, b->v_scale, p.smooth_q ? b->delta_s : nullptr,
+                             p.smooth_v ? b->mu_v : nullptr, o, lse, attn_blocks_host(P),
+                             static_cast<hipStream_t>(stream)));
+    return SAGE_OK;
+}
+
+sage_status sage_debug_qk_int32(const sage_attn_desc* desc, const int32_t* cuq,
+                                const int32_t* cuk, int32_t nseq, const sage_quant_bufs* bufs,
+                                int32_t* s_out, void* stream) {
+    Plan p;
+    sage_status e = make_plan(desc, cuq, cuk, nseq, cuq != nullptr, &p);
+    if (e != SAGE_OK) return e;
+    if (!bufs) return SAGE_ERR_NULL;
+    if (p.S > 0 && (!bufs->q_codes || !bufs->k_codes || !s_out)) return SAGE_ERR_NULL;
+    if (!aligned16(bufs->q_codes) || !aligned16(bufs->k_codes) || !aligned16(s_out))
+        return SAGE_ERR_ALIGN;
+    if ((e = check_arch()) != SAGE_OK) return e;
+    std::vector<int64_t> gbase(p.S + 1, 0);
+    for (int s = 0; s < p.S; ++s) gbase[s + 1] = gbase[s] + (int64_t)p.hq * p.nq[s] * p.nkv[s];
+    for (const KParams& P : make_params(p)) {
+        DumpBase db{};
+        if (!P.tab.uniform)
+            for (int j = 0; j < P.tab.n; ++j) db.base[j] = gbase[P.tab.sid[j]];
+        SAGE_TRY(launch_qk_dump(P, bufs->q_codes, bufs->k_codes, s_out, db, attn_blocks_host(P),
+                                static_cast<hipStream_t>(stream)));
+    }
+    return SAGE_OK;
+}
+
+const char* sage_status_string(sage_status s) {
+    switch (s) {
+        case SAGE_OK: return "ok";
+        case SAGE_ERR_NULL: return "null pointer";
+        case SAGE_ERR_DTYPE: return "unsupported dtype";
+        case SAGE_ERR_LAYOUT: return "unsupported layout";
+        case SAGE_ERR_HEAD_DIM: return "head_dim must be 64, 96 or 128";
+        case SAGE_ERR_SHAPE: return "invalid shape";
+        case SAGE_ERR_GQA: return "hq must be a multiple of hkv";
+        case SAGE_ERR_STRIDE: return "invalid stride";
+        case SAGE_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case SAGE_ERR_WORKSPACE: return "workspace too small";
+        case SAGE_ERR_SEQLENS: return "invalid cu_seqlens";
+        case SAGE_ERR_ARCH: return "device is not gfx950";
+        case SAGE_ERR_HIP: return "HIP runtime error";
+        case SAGE_ERR_FLAGS: return "invalid flag or reserved field";
+    }
+    return "unknown status";
+}
+
+int32_t sage_abi_version(void) { return SAGE_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// sage_internal.h -- shared host/device definitions of libsage (not part of
+// the public ABI).  Kernel arguments are passed by value in `KParams`.
+#pragma once
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+constexpr int QBLK = 64;      // Q/K quantization block (tokens)
+constexpr int KVT = 128;      // key tile of the fused kernel (tokens)
+constexpr int MAXSEQ = 32;    // sequences described per launch
+constexpr int WG = 256;       // threads per workgroup of every kernel
+
+struct Strides {
+    int64_t b, h, n;          // elements; head_dim stride is 1
+};
+
+// Per-launch description of the sequences.  Dense problems use uniform = 1:
+// every sequence has lengths nq[0], nkv[0], lives at batch index s and its
+// padded row bases are s * npq and s * npk.  Variable-length problems list up
+// to MAXSEQ sequences with token offsets into the packed tensors and their
+// own padded row bases.
+struct SeqTab {
+    int32_t n;
+    int32_t uniform;
+    int32_t nq[MAXSEQ], nkv[MAXSEQ];
+    int32_t tq[MAXSEQ], tk[MAXSEQ];     // first token (varlen)
+    int64_t rq[MAXSEQ], rk[MAXSEQ];     // padded row bases in the code buffers
+    int32_t sid[MAXSEQ];                // sequence index for [S][H][d] arrays and lse
+    int64_t lse_base[MAXSEQ];           // first lse element of sequence s (head 0)
+};
+
+struct KParams {
+    int32_t d, hq, hkv, group;          // group = hq / hkv
+    int32_t causal;
+    float sm_scale;                     // natural-log units
+    float sml2;                         // sm_scale * log2(e)
+    Strides qs, ks, vs, os;
+    int64_t lse_hstride;                // elements between heads of lse
+    SeqTab tab;
+};
+
+struct SeqInfo {
+    int nq, nkv, sid;
+    int64_t q_el, k_el, v_el, o_el;     // element offset of (seq, head 0, token 0)
+    int64_t rq, rk;                     // padded row bases
+    int npq, npk;                       // padded lengths
+    int64_t lse0;
+};
+
+__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+__device__ inline SeqInfo seq_info(const KParams& P, int s) {
+    const SeqTab& t = P.tab;
+    SeqInfo r;
+    if (t.uniform) {
+        r.nq = t.nq[0];
+        r.nkv = t.nkv[0];
+        r.sid = s;
+        r.q_el = (int64_t)s * P.qs.b;
+        r.k_el = (int64_t)s * P.ks.b;
+        r.v_el = (int64_t)s * P.vs.b;
+        r.o_el = (int64_t)s * P.os.b;
+        r.npq = round_up(r.nq, QBLK);
+        r.npk = round_up(r.nkv, KVT);
+        r.rq = (int64_t)s * r.npq;
+        r.rk = (int64_t)s * r.npk;
+        r.lse0 = (int64_t)s * P.hq * r.nq;
+    } else {
+        r.nq = t.nq[s];
+        r.nkv = t.nkv[s];
+        r.sid = t.sid[s];
+        r.q_el = (int64_t)t.tq[s] * P.qs.n;
+        r.k_el = (int64_t)t.tk[s] * P.ks.n;
+        r.v_el = (int64_t)t.tk[s] * P.vs.n;
+        r.o_el = (int64_t)t.tq[s] * P.os.n;
+        r.npq = round_up(r.nq, QBLK);
+        r.npk = round_up(r.nkv, KVT);
+        r.rq = t.rq[s];
+        r.rk = t.rk[s];
+        r.lse0 = t.lse_base[s];
+    }
+    return r;
+}
+
+// Locate the sequence that owns linear block `blk` when sequence s owns
+// `per(s)` consecutive blocks.  Returns the sequence and the local index.
+template <typename F>
+__device__ inline int find_seq(const KParams& P, int blk, F per, int* local) {
+    if (P.tab.uniform) {
+        int c = per(0);
+        *local = blk % c;
+        return blk / c;
+    }
+    int s = 0;
+    for (; s < P.tab.n - 1; ++s) {
+        int c = per(s);
+        if (blk < c) break;
+        blk -= c;
+    }
+    *local = blk;
+    return s;
+}
+
+// Workgroup shape of the fused kernel: 4 waves, each 32 query rows of one
+// query head.  hpw = query heads per workgroup (1, 2 or 4 of the GQA group),
+// rows per workgroup = 32 * 4 / hpw.
+__host__ __device__ inline int heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
+
+// ---- launchers (sage_prepass.hip, sage_attn.hip) ----
+enum StatMode { STAT_SUM = 0, STAT_ABSMAX = 1 };
+hipError_t launch_stats(const KParams& P, int dtype, int mode, const void* x, Strides xs,
+                        int which, int heads, const float* mu, float* partial, int nblocks,
+                        hipStream_t st);
+hipError_t launch_finalize(const KParams& P, int mode, bool is_q, int heads,
+                           const float* partial, float* out_mu, float* out_amax,
+                           float* out_scale, int nseq, hipStream_t st);
+hipError_t launch_quant_qk(const KParams& P, int dtype, const void* x, Strides xs, bool is_q,
+                           int heads, const float* mu, int8_t* codes, float* scales,
+                           const float* mu_q, float* delta_s, int nblocks, hipStream_t st);
+hipError_t launch_quant_v(const KParams& P, int dtype, const void* v, const float* mu,
+                          const float* amax, uint8_t* codes, int nblocks, hipStream_t st);
+hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const float* qsc,
+                       const int8_t* kc, const float* ksc, const uint8_t* vc,
+                       const float* vsc, const float* ds, const float* mu_v, void* o,
+                       float* lse, int nblocks, hipStream_t st);
+struct DumpBase {
+    int64_t base[MAXSEQ];               // first element of sequence s in the dump
+};
+hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,
+                          const DumpBase& db, int nblocks, hipStream_t st);
+// workgroups of the fused kernel (and of the Q.K^T dump) for a sequence table
+int attn_blocks_host(const KParams& P);
+
+}  // namespace sage

@@ -1,0 +1,170 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol that
+include/sage.h declares, and its host-side validation returns the documented
+status for each bad argument without touching the GPU (fake, never
+dereferenced device pointers are passed; every case fails before any HIP
+call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_attention_03_amd as qa
+from quantized_attention_03_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "sage.h")
+FAKE = 0x10000          # aligned fake device address (never dereferenced)
+
+
+def _declared():
+    txt = open(HDR).read()
+    return sorted(set(re.findall(r"SAGE_API\s+[\w\s\*]*?\b(sage_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 10, names
+    L = qa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_abi.EXPORTS)
+
+
+def test_version_and_status_strings():
+    L = qa.lib()
+    assert L.sage_abi_version() == 1
+    for code in range(14):
+        assert L.sage_status_string(code)
+    assert L.sage_status_string(999) == b"unknown status"
+
+
+def _desc(**kw):
+    d = _abi.Desc()
+    qa.lib().sage_desc_init(ctypes.byref(d), kw.pop("dtype", 0), kw.pop("layout", 0),
+                            kw.pop("batch", 2), kw.pop("hq", 8), kw.pop("hkv", 2),
+                            kw.pop("nq", 100), kw.pop("nkv", 300), kw.pop("head_dim", 128))
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _fwd(d, q=FAKE, k=FAKE, v=FAKE, o=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    P = ctypes.c_void_p
+    return qa.lib().sage_attn_fwd(ctypes.byref(d), P(q), P(k), P(v), P(o), None, P(ws),
+                                  ws_bytes, None)
+
+
+def _ws(d, cuq=None, cuk=None, n=0):
+    out = ctypes.c_size_t(0)
+    st = qa.lib().sage_workspace_size(ctypes.byref(d) if d is not None else None, cuq, cuk, n,
+                                      ctypes.byref(out))
+    return st, out.value
+
+
+def test_desc_init_defaults():
+    d = _desc()
+    assert (d.smooth_k, d.smooth_q, d.smooth_v, d.is_causal, d.sm_scale) == (1, 0, 0, 0, 0.0)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 7, "SAGE_ERR_DTYPE"),
+    ("layout", 2, "SAGE_ERR_LAYOUT"),
+    ("is_causal", 2, "SAGE_ERR_FLAGS"),
+    ("smooth_v", -1, "SAGE_ERR_FLAGS"),
+    ("head_dim", 80, "SAGE_ERR_HEAD_DIM"),
+    ("head_dim", 256, "SAGE_ERR_HEAD_DIM"),
+    ("hq", 0, "SAGE_ERR_SHAPE"),
+    ("nq", -1, "SAGE_ERR_SHAPE"),
+    ("batch", -3, "SAGE_ERR_SHAPE"),
+    ("hq", 7, "SAGE_ERR_GQA"),
+])
+def test_descriptor_errors(field, value, status):
+    d = _desc(**{field: value})
+    assert _abi.STATUS_NAMES[_fwd(d)] == status
+    assert _abi.STATUS_NAMES[_ws(d)[0]] == status
+
+
+def test_reserved_and_nan_scale_rejected():
+    d = _desc()
+    d.reserved[1] = 5
+    assert _abi.STATUS_NAMES[_fwd(d)] == "SAGE_ERR_FLAGS"
+    d = _desc(sm_scale=float("nan"))
+    assert _abi.STATUS_NAMES[_fwd(d)] == "SAGE_ERR_FLAGS"
+
+
+def test_stride_errors():
+    d = _desc()
+    d.q_stride[0], d.q_stride[1], d.q_stride[2] = 100 * 128, 128, 12   # not a multiple of 8
+    assert _abi.STATUS_NAMES[_fwd(d)] == "SAGE_ERR_STRIDE"
+    d = _desc()
+    d.k_stride[1] = -8
+    assert _abi.STATUS_NAMES[_fwd(d)] == "SAGE_ERR_STRIDE"
+
+
+def test_null_align_workspace_errors():
+    d = _desc()
+    assert _abi.STATUS_NAMES[qa.lib().sage_attn_fwd(None, None, None, None, None, None, None, 0,
+                                                    None)] == "SAGE_ERR_NULL"
+    assert _abi.STATUS_NAMES[_fwd(d, q=0)] == "SAGE_ERR_NULL"
+    assert _abi.STATUS_NAMES[_fwd(d, ws=0)] == "SAGE_ERR_NULL"
+    assert _abi.STATUS_NAMES[_fwd(d, k=FAKE + 4)] == "SAGE_ERR_ALIGN"
+    assert _abi.STATUS_NAMES[_fwd(d, o=FAKE + 8)] == "SAGE_ERR_ALIGN"
+    st, need = _ws(d)
+    assert st == 0 and need > 0
+    assert _abi.STATUS_NAMES[_fwd(d, ws_bytes=need - 1)] == "SAGE_ERR_WORKSPACE"
+
+
+def test_varlen_seqlens_errors():
+    d = _desc(batch=0, nq=0, nkv=0)
+    I = ctypes.c_int32
+    good_q, good_k = (I * 3)(0, 10, 30), (I * 3)(0, 50, 51)
+    bad_start = (I * 3)(1, 10, 30)
+    decreasing = (I * 3)(0, 10, 5)
+    P = ctypes.c_void_p
+    L = qa.lib()
+
+    def run(cq, ck, n=2):
+        return _abi.STATUS_NAMES[L.sage_attn_fwd_varlen(ctypes.byref(d), cq, ck, n, P(FAKE), P(FAKE),
+                                                        P(FAKE), P(FAKE), None, P(FAKE), 1, None)]
+    assert run(None, good_k) == "SAGE_ERR_NULL"
+    assert run(bad_start, good_k) == "SAGE_ERR_SEQLENS"
+    assert run(good_q, decreasing) == "SAGE_ERR_SEQLENS"
+    assert run(good_q, good_k, n=-1) == "SAGE_ERR_SHAPE"
+    assert run(good_q, good_k) == "SAGE_ERR_WORKSPACE"
+
+
+def _pad(x, m):
+    return (x + m - 1) // m * m
+
+
+def test_quant_buf_sizes_follow_documented_layout():
+    d = _desc(smooth_q=1, smooth_v=1)       # B=2, hq=8, hkv=2, nq=100, nkv=300, d=128
+    s = qa.quant_buf_sizes(d)
+    B, hq, hkv, dd = 2, 8, 2, 128
+    npq, npk = _pad(100, 64), _pad(300, 128)
+    assert s["q_codes"] == B * hq * npq * dd
+    assert s["q_scale"] == B * hq * npq // 64 * 4
+    assert s["k_codes"] == B * hkv * npk * dd == s["v_codes"]
+    assert s["k_scale"] == B * hkv * npk // 64 * 4
+    assert s["v_scale"] == B * hkv * dd * 4 == s["mu_k"] == s["mu_v"]
+    assert s["mu_q"] == B * hq * dd * 4
+    assert s["delta_s"] == B * hq * npk * 4
+    d2 = _desc()
+    assert qa.quant_buf_sizes(d2)["delta_s"] == 0 and qa.quant_buf_sizes(d2)["mu_q"] == 0
+    # varlen: sum of per-sequence padded lengths
+    I = ctypes.c_int32
+    dv = _desc(batch=0, nq=0, nkv=0)
+    cq, ck = (I * 4)(0, 1, 65, 65), (I * 4)(0, 129, 130, 130)
+    z = _abi.QuantSizes()
+    assert qa.lib().sage_quant_buf_sizes(ctypes.byref(dv), cq, ck, 3, ctypes.byref(z)) == 0
+    assert z.q_codes == hq * (64 + 64 + 0) * dd          # lengths 1, 64, 0
+    assert z.k_codes == hkv * (256 + 128 + 0) * dd      # lengths 129, 1, 0
+
+
+def test_empty_problem_is_a_no_op():
+    d = _desc(batch=0)
+    # nothing to compute: returns OK after the argument checks (no device call
+    # happens before the arch check, which an empty problem still performs)
+    st = _fwd(d, q=0, k=0, v=0, o=0, ws=0, ws_bytes=0)
+    assert _abi.STATUS_NAMES[st] in ("SAGE_OK", "SAGE_ERR_HIP", "SAGE_ERR_ARCH")

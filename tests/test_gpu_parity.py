@@ -1,0 +1,143 @@
+"""GPU parity of the HIP library against the CPU oracle (calls go through the
+C ABI via the ctypes binding).
+
+Bars: channel means, INT8 codes and scales, E4M3 V codes and scales are
+bit-exact; the int32 Q.K^T (same device code as the fused kernel) is
+bit-exact; the output is within max-abs 2e-2 and cosine >= 0.999 of the
+oracle's same-recipe output and reaches cosine >= 0.99 against exact FP64
+attention.  The max-abs bound is taken against the oracle's FP32 result and
+excludes the final round-to-nearest-even into fp16/bf16 (half an ulp of the
+output dtype), which both sides apply last and which alone exceeds 2e-2 for
+bf16 outputs of magnitude 8 and above.  Sizes here finish in seconds on the oracle yet span several
+64-token blocks, several 128-key tiles and ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import oracle as orc
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+R = synth.scaled_down
+
+CASES = {
+    "tiny": W["tiny"],
+    "llm_prefill_small": R(W["llm_prefill"], B=2, Hq=4, Hkv=4, Nq=300, Nkv=300),
+    "causal_gqa_small": R(W["causal_gqa"], Hq=8, Hkv=2, Nq=520, Nkv=520),
+    "video_dit_small": R(W["video_dit"], Hq=2, Hkv=2, Nq=333, Nkv=333),
+    "varlen_d128_small": R(W["varlen_d128"], Hq=4, Hkv=4,
+                           seqlens_q=[100, 37, 300, 65], seqlens_kv=[700, 37, 130, 1]),
+    "varlen_d96_small": R(W["varlen_d96"], Hq=4, Hkv=2,
+                          seqlens_q=[64, 200, 1], seqlens_kv=[300, 200, 129]),
+    "d96_hnd_ragged": R(W["tiny"], d=96, B=2, Hq=2, Hkv=2, Nq=63, Nkv=65, seed=7),
+    "d64_nq_gt_nkv_causal": R(W["tiny"], Hq=2, Hkv=1, Nq=200, Nkv=70, causal=True, seed=8),
+    "d128_one_query": R(W["tiny"], d=128, Hq=2, Hkv=2, Nq=1, Nkv=257, seed=9),
+    "d128_one_key": R(W["tiny"], d=128, Hq=2, Hkv=2, Nq=129, Nkv=1, smooth_v=True, seed=10),
+    "gqa8_nhd": R(W["causal_gqa"], layout="NHD", Hq=16, Hkv=2, Nq=130, Nkv=300, seed=11),
+    "gqa3_bf16": R(W["llm_prefill"], Hq=6, Hkv=2, B=1, Nq=150, Nkv=150, seed=12, causal=True),
+    "gqa2_smooth_all": R(W["video_dit"], Hq=4, Hkv=2, Nq=190, Nkv=260, d=128, seed=13,
+                         layout="HND"),
+    "no_smoothing": R(W["causal_gqa"], smooth_k=False, Hq=4, Hkv=4, Nq=256, Nkv=256, seed=14),
+    "custom_scale": R(W["tiny"], sm_scale=0.05, Nq=128, Nkv=384, seed=15),
+}
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def case(request):
+    name = request.param
+    w = CASES[name]
+    pu.say(f"[case {name}] {w}")
+    q, k, v, meta = pu.gpu_inputs(w)
+    prob = orc.problem_from_workload(w)
+    ref = orc.prepass(prob, pu.u16(q), pu.u16(k), pu.u16(v))
+    return name, w, q, k, v, meta, prob, ref
+
+
+def test_prepass_bit_exact(case):
+    name, w, q, k, v, meta, prob, ref = case
+    pu.say(f"[prepass {name}]")
+    bufs = pu.run_quant(w, q, k, v, meta)
+    torch.cuda.synchronize()
+    gpu, pads_ok = pu.unpack_quant(w, bufs)
+    assert pads_ok, "padding rows/blocks must be zero"
+    pu.assert_prepass_equal(gpu, ref, w)
+
+
+def test_qk_int32_bit_exact(case):
+    name, w, q, k, v, meta, prob, ref = case
+    pu.say(f"[qk int32 {name}]")
+    bufs = pu.run_quant(w, q, k, v, meta)
+    kw = {}
+    if w.varlen:
+        kw = dict(cu_seqlens_q=meta["cu_seqlens_q"], cu_seqlens_kv=meta["cu_seqlens_kv"])
+    s = pu.qa.sage_debug_qk_int32(bufs, **kw).cpu().numpy()
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    off = 0
+    for si, (nq, nkv) in enumerate(w.seq_lens()):
+        got = s[off:off + w.Hq * nq * nkv].reshape(w.Hq, nq, nkv)
+        off += w.Hq * nq * nkv
+        for h in range(w.Hq):
+            exp = orc.qk_int32(ref.qc[si][h], ref.kc[si][h // G])
+            assert np.array_equal(got[h], exp), (si, h)
+
+
+def test_forward_matches_oracle(case):
+    name, w, q, k, v, meta, prob, ref = case
+    pu.say(f"[forward {name}]")
+    o, lse = pu.run_fwd(w, q, k, v, meta)
+    torch.cuda.synchronize()
+    got = pu.gpu_out_per_seq(w, o, meta)
+    rec, rec_lse = orc.forward_rows(prob, ref, bkv=pu.KVT)
+    ex, _ = orc.exact_rows(prob, pu.u16(q), pu.u16(k), pu.u16(v))
+    lse_h = lse.cpu().numpy()
+    for si, (nq, nkv) in enumerate(w.seq_lens()):
+        g, r, e = got[si], rec[si], ex[si]
+        assert np.all(np.isfinite(g))
+        # max-abs against the oracle's FP32 result, beyond the final rounding
+        # into the output dtype (half an ulp there)
+        err = pu.max_excess(g, r, w.dtype)
+        assert err <= 2e-2, (si, err)
+        assert pu.cos(g, r) >= 0.999, (si, pu.cos(g, r))
+        assert pu.cos(g, e) >= 0.99, (si, pu.cos(g, e))
+        # lse: dense [B, hq, nq]; varlen [hq, T]
+        if w.varlen:
+            t0 = meta["cu_seqlens_q"][si]
+            gl = lse_h[:, t0:t0 + nq]
+        else:
+            gl = lse_h[si]
+        fin = np.isfinite(r_l := rec_lse[si])
+        assert np.array_equal(np.isfinite(gl), fin)
+        if fin.any():
+            assert np.abs(gl[fin] - r_l[fin]).max() < 2e-3 * max(1.0, np.abs(r_l[fin]).max())
+
+
+def test_forward_deterministic(case):
+    name, w, q, k, v, meta, prob, ref = case
+    pu.say(f"[determinism {name}]")
+    o1, l1 = pu.run_fwd(w, q, k, v, meta)
+    o2, l2 = pu.run_fwd(w, q, k, v, meta)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_strided_inputs_match_contiguous():
+    """q/k/v as views into wider tensors (non-contiguous head/token strides)."""
+    w = R(W["llm_prefill"], B=2, Hq=4, Hkv=2, Nq=140, Nkv=200, layout="NHD", seed=21)
+    pu.say("[strided inputs]")
+    q, k, v, meta = pu.gpu_inputs(w)
+    big_q = torch.zeros(2, 140, 6, 128, dtype=q.dtype, device="cuda")
+    big_q[:, :, 1:5] = q
+    big_kv = torch.zeros(2, 200, 2, 2, 128, dtype=q.dtype, device="cuda")
+    big_kv[:, :, :, 0] = k
+    big_kv[:, :, :, 1] = v
+    qv, kv_, vv = big_q[:, :, 1:5], big_kv[:, :, :, 0], big_kv[:, :, :, 1]
+    o_ref = pu.run_fwd(w, q, k, v, meta, return_lse=False)
+    o = pu.run_fwd(w, qv, kv_, vv, meta, return_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
