@@ -25,8 +25,9 @@
 //    relayout); V^T comes from LDS as two 16-byte reads per lane.  The
 //    accumulator layout keeps each lane on its own query row, so the
 //    rescale by alpha and the final 1/l need no cross-lane traffic.
-//  * K and V^T tiles are double-buffered in LDS (rows padded by 16 bytes:
-//    conflict-free 16-byte reads), prefetched into registers one tile ahead.
+//  * K and V^T tiles are double-buffered in LDS and filled one tile ahead by
+//    direct global -> LDS loads (no staging registers); 16-byte slots of each
+//    LDS row are XOR-swizzled so the operand reads are bank-conflict free.
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
 #include "sage_internal.h"
@@ -45,15 +46,79 @@ constexpr float LN2 = 0.6931471805599453f;
 
 template <int D>
 struct Tile {
-    static constexpr int KS = D + 16;           // LDS row stride of K (bytes)
-    static constexpr int VS = KVT + 16;         // LDS row stride of V^T (bytes)
-    static constexpr int KBYTES = KVT * KS;
-    static constexpr int VBYTES = D * VS;
-    static constexpr int DSBYTES = 4 * KVT * 4; // score bias of the tile, per head of the workgroup
-    static constexpr int STAGE = KBYTES + VBYTES + DSBYTES;
-    static constexpr int LDS = 2 * STAGE;
-    static constexpr int NPRE = D / 32;         // 16-byte granules per thread per tensor
+    // LDS image of one 128-key tile.  K rows are 128 bytes (64 for D = 64;
+    // D = 96 leaves two 16-byte slots of a row unused); V^T rows (one per
+    // channel) are 128 bytes.  Rows are dense and their 16-byte slots are
+    // XOR-swizzled (slot = granule ^ swz(row)) so that the MFMA operand reads
+    // of 16 consecutive rows hit distinct banks.
+    static constexpr int KRS = D == 64 ? 64 : 128;
+    static constexpr int KBYTES = KVT * KRS;
+    static constexpr int VBYTES = D * KVT;
+    static constexpr int DSBYTES = 4 * KVT * 4;  // score bias, per head of the workgroup
+    static constexpr int KINSTR = KBYTES / (WG * 16);
+    static constexpr int VINSTR = VBYTES / (WG * 16);
 };
+
+template <int RS>
+__device__ inline int swz(int row) {
+    if constexpr (RS == 128) return (row & 7) ^ ((row >> 3) & 1);
+    else return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+}
+
+// Key held by LDS row r of a tile: within each 32-row block, row i holds key
+// 16*((i/4)%2) + 4*(i/8) + i%4, so that the S^T output register r of lane
+// (row, half) is key 32b + 16*half + r.
+__device__ inline int key_of_row(int r) {
+    const int i = r & 31;
+    return (r & ~31) + 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ inline void dma16(const void* src, uint8_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds_wave_base, 16, 0, 0);
+}
+
+// Issue the global -> LDS copies of key tile t (and V^T, score bias) into one
+// stage.  Every lane moves 16 bytes per instruction; lane L of wave w writes
+// stage + 4096*i + 1024*w + 16*L, and picks the global source so that the
+// swizzled image results.  Completion is awaited with vmcnt before the barrier.
+template <int D, bool WITH_V, bool HAS_DS>
+__device__ inline void stage_tile(uint8_t* stage, const int8_t* kbase, const uint8_t* vbase,
+                                  const float* dsb, int npk, int t, int hpw) {
+    using T = Tile<D>;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < T::KINSTR; ++i) {
+        const int o = i * WG * 16 + w * 1024 + lane * 16;
+        const int row = o / T::KRS, slot = (o % T::KRS) / 16;
+        int lg = slot ^ swz<T::KRS>(row);
+        if (D == 96 && lg >= 6) lg &= 1;           // unused slots: any in-row granule
+        dma16(kbase + (int64_t)(t * KVT + key_of_row(row)) * D + lg * 16,
+              stage + i * WG * 16 + w * 1024);
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+        for (int i = 0; i < T::VINSTR; ++i) {
+            const int o = i * WG * 16 + w * 1024 + lane * 16;
+            const int ch = o / KVT, slot = (o % KVT) / 16;
+            const int lg = slot ^ swz<128>(ch);
+            dma16(vbase + (int64_t)ch * npk + t * KVT + lg * 16,
+                  stage + T::KBYTES + i * WG * 16 + w * 1024);
+        }
+    }
+    if constexpr (HAS_DS) {
+        // hpw heads x 128 floats; waves 0 and 1 cover up to 4 heads
+        if (w * 2 < hpw) {
+            int hs = w * 2 + lane / 32;
+            if (hs >= hpw) hs = hpw - 1;
+            dma16(dsb + (int64_t)hs * npk + t * KVT + (lane % 32) * 4,
+                  stage + T::KBYTES + T::VBYTES + w * 1024);
+        }
+    }
+}
+
+__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Work decomposition shared by the fused kernel and the Q.K^T dump.
 struct Work {
@@ -111,46 +176,6 @@ __device__ inline Work decode_work(const KParams& P) {
     return w;
 }
 
-// Global -> register prefetch of one K tile, one V^T tile (and the score bias).
-template <int D, bool HAS_DS>
-struct Prefetch {
-    uint4 k[Tile<D>::NPRE];
-    uint4 v[Tile<D>::NPRE];
-    uint4 ds;
-
-    // dsb: score bias row of the workgroup's first head; heads are npk apart
-    __device__ inline void load(const int8_t* kbase, const uint8_t* vbase, const float* dsb,
-                                int npk, int t, int hpw) {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < Tile<D>::NPRE; ++i) {
-            const int g = tid + WG * i;
-            const int key = g / (D / 16), col = g % (D / 16);
-            k[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(t * KVT + key) * D + col * 16);
-            const int ch = g / (KVT / 16), kc = g % (KVT / 16);
-            v[i] = *reinterpret_cast<const uint4*>(vbase + (int64_t)ch * npk + t * KVT + kc * 16);
-        }
-        if (HAS_DS && tid < hpw * (KVT / 4))
-            ds = *reinterpret_cast<const uint4*>(dsb + (int64_t)(tid / (KVT / 4)) * npk + t * KVT +
-                                                 (tid % (KVT / 4)) * 4);
-    }
-    __device__ inline void store(uint8_t* stage, int hpw) const {
-        const int tid = threadIdx.x;
-        uint8_t* Ks = stage;
-        uint8_t* Vs = stage + Tile<D>::KBYTES;
-#pragma unroll
-        for (int i = 0; i < Tile<D>::NPRE; ++i) {
-            const int g = tid + WG * i;
-            const int key = g / (D / 16), col = g % (D / 16);
-            *reinterpret_cast<uint4*>(Ks + key * Tile<D>::KS + col * 16) = k[i];
-            const int ch = g / (KVT / 16), kc = g % (KVT / 16);
-            *reinterpret_cast<uint4*>(Vs + ch * Tile<D>::VS + kc * 16) = v[i];
-        }
-        if (HAS_DS && tid < hpw * (KVT / 4))
-            *reinterpret_cast<uint4*>(stage + Tile<D>::KBYTES + Tile<D>::VBYTES + tid * 16) = ds;
-    }
-};
-
 // The wave's Q codes in MFMA B layout: lane (row = lane%32, half = lane/32)
 // holds channels [32c + 16*half, +16) for every 32-channel chunk c.
 template <int D>
@@ -166,18 +191,20 @@ __device__ inline void load_q(const int8_t* qrow, v4i* qf) {
 // (row, half) receive keys 32b + 16*half + r in register r (r = 0..15).
 template <int D>
 __device__ inline void qk_tile(const uint8_t* Ks, const v4i* qf, v16i* sacc) {
+    using T = Tile<D>;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, i = lane & 31;
-    const int krow = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
+        const int row = 32 * b + i;
+        const uint8_t* kr = Ks + row * T::KRS;
+        const int sw = swz<T::KRS>(row);
         v16i acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0;
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
-            const v4i a = *reinterpret_cast<const v4i*>(Ks + (32 * b + krow) * Tile<D>::KS +
-                                                         32 * c + 16 * h);
+            const v4i a = *reinterpret_cast<const v4i*>(kr + (((2 * c + h) ^ sw) << 4));
             acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[c], acc, 0, 0, 0);
         }
         sacc[b] = acc;
@@ -256,18 +283,17 @@ __global__ __launch_bounds__(WG, 2) void k_attn(KParams P, const int8_t* __restr
     const int diag = my_q + nkv - nq;          // last visible key of this row (causal)
     const int wave_diag = w.q0 + nkv - nq;     // ... of the wave's first row
 
-    Prefetch<D, HAS_DS> pf;
-    if (w.nt_wg > 0) {
-        pf.load(kbase, vbase, dsb, si.npk, 0, w.hpw);
-        pf.store(smem, w.hpw);
-    }
+    constexpr int STAGE = T::KBYTES + T::VBYTES + (HAS_DS ? T::DSBYTES : 0);
+    if (w.nt_wg > 0) stage_tile<D, true, HAS_DS>(smem, kbase, vbase, dsb, si.npk, 0, w.hpw);
+    wait_dma();
     __syncthreads();
 
     for (int t = 0; t < w.nt_wg; ++t) {
-        const bool more = t + 1 < w.nt_wg;
-        if (more) pf.load(kbase, vbase, dsb, si.npk, t + 1, w.hpw);
+        if (t + 1 < w.nt_wg)
+            stage_tile<D, true, HAS_DS>(smem + ((t + 1) & 1) * STAGE, kbase, vbase, dsb, si.npk,
+                                        t + 1, w.hpw);
         if (t < w.nt_w) {
-            const uint8_t* stage = smem + (t & 1) * T::STAGE;
+            const uint8_t* stage = smem + (t & 1) * STAGE;
             v16i sacc[4];
             qk_tile<D>(stage, qf, sacc);
 
@@ -367,15 +393,17 @@ __global__ __launch_bounds__(WG, 2) void k_attn(KParams P, const int8_t* __restr
             for (int c = 0; c < D / 32; ++c)
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh) {
-                    const uint8_t* vr = Vs + (32 * c + qi) * T::VS + 64 * kh + 16 * h;
-                    const v4i lo = *reinterpret_cast<const v4i*>(vr);
-                    const v4i hi = *reinterpret_cast<const v4i*>(vr + 32);
+                    const int ch = 32 * c + qi;
+                    const uint8_t* vr = Vs + ch * KVT;
+                    const int sw = swz<128>(ch);
+                    const v4i lo = *reinterpret_cast<const v4i*>(vr + (((4 * kh + h) ^ sw) << 4));
+                    const v4i hi = *reinterpret_cast<const v4i*>(vr + (((4 * kh + 2 + h) ^ sw) << 4));
                     const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb[kh], acc[c], 0,
                                                                               0, 0, 0, 0, 0);
                 }
         }
-        if (more) pf.store(smem + ((t + 1) & 1) * T::STAGE, w.hpw);
+        wait_dma();
         __syncthreads();
     }
 
@@ -415,7 +443,6 @@ __global__ __launch_bounds__(WG, 2) void k_qk_dump(KParams P, const int8_t* __re
                                                    const int8_t* __restrict__ kc,
                                                    int32_t* __restrict__ out, DumpBase db) {
     extern __shared__ __align__(16) uint8_t smem[];
-    using T = Tile<D>;
     const Work w = decode_work(P);
     const SeqInfo& si = w.si;
     const int lane = threadIdx.x & 63;
@@ -436,14 +463,9 @@ __global__ __launch_bounds__(WG, 2) void k_qk_dump(KParams P, const int8_t* __re
     }
     const int64_t base = P.tab.uniform ? (int64_t)w.s * P.hq * nq * nkv : db.base[w.s];
     for (int t = 0; t < nt; ++t) {
-        // stage K only (the same layout as the fused kernel)
-#pragma unroll
-        for (int i = 0; i < T::NPRE; ++i) {
-            const int g = threadIdx.x + WG * i;
-            const int key = g / (D / 16), col = g % (D / 16);
-            *reinterpret_cast<uint4*>(smem + key * T::KS + col * 16) =
-                *reinterpret_cast<const uint4*>(kbase + (int64_t)(t * KVT + key) * D + col * 16);
-        }
+        // stage K only (the same image as the fused kernel)
+        stage_tile<D, false, false>(smem, kbase, nullptr, nullptr, si.npk, t, 1);
+        wait_dma();
         __syncthreads();
         v16i sacc[4];
         qk_tile<D>(smem, qf, sacc);
@@ -464,6 +486,11 @@ __global__ __launch_bounds__(WG, 2) void k_qk_dump(KParams P, const int8_t* __re
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+template <int D, bool HAS_DS>
+constexpr int lds_bytes() {
+    return 2 * (Tile<D>::KBYTES + Tile<D>::VBYTES + (HAS_DS ? Tile<D>::DSBYTES : 0));
+}
+
 int attn_blocks_host(const KParams& P) {
     const int hpw = heads_per_wg(P.group);
     const int rows = 128 / hpw;
@@ -481,11 +508,11 @@ static hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, c
     static bool attr_set = false;   // benign race: the call is idempotent
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D, DT, HAS_DS>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, Tile<D>::LDS);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<D, HAS_DS>());
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_attn<D, DT, HAS_DS><<<nblocks, WG, Tile<D>::LDS, st>>>(
+    k_attn<D, DT, HAS_DS><<<nblocks, WG, lds_bytes<D, HAS_DS>(), st>>>(
         P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, static_cast<uint16_t*>(o), lse);
     return hipGetLastError();
 }
