@@ -358,8 +358,7 @@ sage_status forward(const sage_attn_desc* desc, const int32_t* cuq, const int32_
     if ((e = run_prepass(p, kp, desc->dtype, q, k, v, b, base, w, st)) != SAGE_OK) return e;
     for (const KParams& P : kp)
         SAGE_TRY(launch_attn(P, desc->dtype, b.q_codes, b.q_scale, b.k_codes, b.k_scale,
-                             b.v_codes, b.v_scale, b.delta_s, b.mu_v, o, lse,
-                             attn_blocks_host(P), st));
+                             b.v_codes, b.v_scale, b.delta_s, b.mu_v, o, lse, st));
     return SAGE_OK;
 }
 
@@ -467,7 +466,7 @@ sage_status sage_attn_fwd_quantized(const sage_attn_desc* desc, const int32_t* c
     for (const KParams& P : make_params(p))
         SAGE_TRY(launch_attn(P, desc->dtype, b->q_codes, b->q_scale, b->k_codes, b->k_scale,
                              b->v_codes, b->v_scale, p.smooth_q ? b->delta_s : nullptr,
-                             p.smooth_v ? b->mu_v : nullptr, o, lse, attn_blocks_host(P),
+                             p.smooth_v ? b->mu_v : nullptr, o, lse,
                              static_cast<hipStream_t>(stream)));
     return SAGE_OK;
 }
@@ -489,7 +488,7 @@ sage_status sage_debug_qk_int32(const sage_attn_desc* desc, const int32_t* cuq,
         DumpBase db{};
         if (!P.tab.uniform)
             for (int j = 0; j < P.tab.n; ++j) db.base[j] = gbase[P.tab.sid[j]];
-        SAGE_TRY(launch_qk_dump(P, bufs->q_codes, bufs->k_codes, s_out, db, attn_blocks_host(P),
+        SAGE_TRY(launch_qk_dump(P, bufs->q_codes, bufs->k_codes, s_out, db,
                                 static_cast<hipStream_t>(stream)));
     }
     return SAGE_OK;

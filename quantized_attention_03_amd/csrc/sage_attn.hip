@@ -9,9 +9,9 @@
 //   l accumulated from the FP32 p, o_i = sum p^ v^ * (v_scale / 448) / l (+ mu_v).
 //
 // Design for CDNA4:
-//  * Workgroup = 4 waves; a wave owns 32 query rows of one query head.  With
-//    GQA, the waves of a workgroup take up to 4 query heads of one key/value
-//    head so that every K/V tile staged in LDS feeds 4 heads.
+//  * A wave owns 32 query rows of one query head.  With GQA, the waves of a
+//    workgroup take up to 4 query heads of one key/value head so that every
+//    K/V tile staged in LDS feeds all of them.
 //  * S^T = Kc . Qc^T on v_mfma_i32_32x32x32_i8 (A = key rows from LDS,
 //    B = the wave's Q codes held in VGPRs).  The row max is taken on the
 //    int32 scores (the scale is positive and uniform over a 64-key block);
@@ -25,9 +25,16 @@
 //    relayout); V^T comes from LDS as two 16-byte reads per lane.  The
 //    accumulator layout keeps each lane on its own query row, so the
 //    rescale by alpha and the final 1/l need no cross-lane traffic.
-//  * K and V^T tiles are double-buffered in LDS and filled one tile ahead by
-//    direct global -> LDS loads (no staging registers); 16-byte slots of each
-//    LDS row are XOR-swizzled so the operand reads are bank-conflict free.
+//  * K and V^T tiles are double-buffered in LDS and filled by direct global ->
+//    LDS loads (no staging registers); 16-byte slots of each LDS row are
+//    XOR-swizzled so the operand reads are bank-conflict free.
+//  * Ping-pong: a workgroup has 8 waves in two groups of 4; the two waves
+//    that share a SIMD belong to different groups.  Each group alternates an
+//    MFMA phase (Q.K(t)^T and the P.V of tile t-1) and a softmax phase (VALU
+//    and v_exp_f32), offset by one phase from the other group, with a
+//    workgroup barrier between phases.  So while one wave of a SIMD keeps
+//    the matrix unit busy the other issues the softmax VALU work; the MFMA
+//    phase runs at raised priority.
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
 #include "sage_internal.h"
@@ -43,20 +50,22 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr float LOG2_448 = 8.807354922057604f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr int FWD_WAVES = 8;               // waves per workgroup of the fused kernel
+constexpr int FWD_NT = 64 * FWD_WAVES;
 
 template <int D>
 struct Tile {
     // LDS image of one 128-key tile.  K rows are 128 bytes (64 for D = 64;
     // D = 96 leaves two 16-byte slots of a row unused); V^T rows (one per
-    // channel) are 128 bytes.  Rows are dense and their 16-byte slots are
-    // XOR-swizzled (slot = granule ^ swz(row)) so that the MFMA operand reads
-    // of 16 consecutive rows hit distinct banks.
+    // channel) are 128 bytes, and the V^T stage is padded to 128 rows for
+    // D = 96 so that it is a whole number of 8 KB copies.  Rows are dense and
+    // their 16-byte slots are XOR-swizzled (slot = granule ^ swz(row)) so that
+    // the MFMA operand reads of 16 consecutive rows hit distinct banks.
     static constexpr int KRS = D == 64 ? 64 : 128;
     static constexpr int KBYTES = KVT * KRS;
-    static constexpr int VBYTES = D * KVT;
+    static constexpr int VROWS = D == 96 ? 128 : D;
+    static constexpr int VBYTES = VROWS * KVT;
     static constexpr int DSBYTES = 4 * KVT * 4;  // score bias, per head of the workgroup
-    static constexpr int KINSTR = KBYTES / (WG * 16);
-    static constexpr int VINSTR = VBYTES / (WG * 16);
 };
 
 template <int RS>
@@ -79,70 +88,110 @@ __device__ inline void dma16(const void* src, uint8_t* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds_wave_base, 16, 0, 0);
 }
 
-// Issue the global -> LDS copies of key tile t (and V^T, score bias) into one
-// stage.  Every lane moves 16 bytes per instruction; lane L of wave w writes
-// stage + 4096*i + 1024*w + 16*L, and picks the global source so that the
-// swizzled image results.  Completion is awaited with vmcnt before the barrier.
-template <int D, bool WITH_V, bool HAS_DS>
-__device__ inline void stage_tile(uint8_t* stage, const int8_t* kbase, const uint8_t* vbase,
-                                  const float* dsb, int npk, int t, int hpw) {
-    using T = Tile<D>;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < T::KINSTR; ++i) {
-        const int o = i * WG * 16 + w * 1024 + lane * 16;
+// Wait for this wave's outstanding memory operations (the direct-to-LDS
+// copies included), then the workgroup barrier.
+__device__ inline void bar() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Per-lane source offsets of the global -> LDS tile copies of a workgroup of
+// NT threads.  Copy i moves NT*16 bytes: lane L of wave w writes
+// base + NT*16*i + 1024*w + 16*L, and its source is chosen so that the
+// swizzled LDS image results.  The key permutation and the swizzle repeat
+// every 32 rows and a copy spans a multiple of 32 rows, so copy i's source is
+// copy 0's plus a constant: one offset per tensor suffices.
+template <int D, int NT>
+struct DmaOffsets {
+    static constexpr int KCOPIES = Tile<D>::KBYTES / (NT * 16);
+    static constexpr int VCOPIES = Tile<D>::VBYTES / (NT * 16);
+    static constexpr int KROWS = NT * 16 / Tile<D>::KRS;   // key rows per copy
+    static constexpr int VROWS = NT * 16 / KVT;            // V^T rows per copy
+    static_assert(KCOPIES * NT * 16 == Tile<D>::KBYTES && KROWS % 32 == 0, "K copy shape");
+    static_assert(VCOPIES * NT * 16 == Tile<D>::VBYTES && VROWS % 16 == 0, "V copy shape");
+    int k0;   // bytes from the key tile start (row-major codes)
+    int v0;   // bytes from the V^T tile start (channel rows of npk bytes)
+
+    __device__ inline void init(int npk) {
+        using T = Tile<D>;
+        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const int o = w * 1024 + lane * 16;
         const int row = o / T::KRS, slot = (o % T::KRS) / 16;
         int lg = slot ^ swz<T::KRS>(row);
         if (D == 96 && lg >= 6) lg &= 1;           // unused slots: any in-row granule
-        dma16(kbase + (int64_t)(t * KVT + key_of_row(row)) * D + lg * 16,
-              stage + i * WG * 16 + w * 1024);
+        k0 = key_of_row(row) * D + lg * 16;
+        const int ch = o / KVT, vslot = (o % KVT) / 16;
+        v0 = ch * npk + ((vslot ^ swz<128>(ch)) << 4);
     }
-    if constexpr (WITH_V) {
+};
+
+// Issue this thread's copies of K tile t (and of the per-head score bias of
+// the tile, which has its own stage) into LDS.
+template <int D, int NT, bool HAS_DS>
+__device__ inline void stage_k(uint8_t* kst, uint8_t* dsst, const DmaOffsets<D, NT>& off,
+                               const int8_t* kbase, const float* dsb, int npk, int t, int hpw) {
+    using O = DmaOffsets<D, NT>;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int8_t* kt = kbase + (int64_t)t * KVT * D;
 #pragma unroll
-        for (int i = 0; i < T::VINSTR; ++i) {
-            const int o = i * WG * 16 + w * 1024 + lane * 16;
-            const int ch = o / KVT, slot = (o % KVT) / 16;
-            const int lg = slot ^ swz<128>(ch);
-            dma16(vbase + (int64_t)ch * npk + t * KVT + lg * 16,
-                  stage + T::KBYTES + i * WG * 16 + w * 1024);
-        }
-    }
+    for (int i = 0; i < O::KCOPIES; ++i)
+        dma16(kt + off.k0 + i * O::KROWS * D, kst + i * NT * 16 + w * 1024);
     if constexpr (HAS_DS) {
         // hpw heads x 128 floats; waves 0 and 1 cover up to 4 heads
         if (w * 2 < hpw) {
             int hs = w * 2 + lane / 32;
             if (hs >= hpw) hs = hpw - 1;
-            dma16(dsb + (int64_t)hs * npk + t * KVT + (lane % 32) * 4,
-                  stage + T::KBYTES + T::VBYTES + w * 1024);
+            dma16(dsb + (int64_t)hs * npk + t * KVT + (lane % 32) * 4, dsst + w * 1024);
         }
     }
 }
 
-__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Issue this thread's copies of V^T tile t into LDS.
+template <int D, int NT>
+__device__ inline void stage_v(uint8_t* vst, const DmaOffsets<D, NT>& off, const uint8_t* vbase,
+                               int npk, int t) {
+    using O = DmaOffsets<D, NT>;
+    const int w = threadIdx.x >> 6;
+    const uint8_t* vt = vbase + t * KVT;
+#pragma unroll
+    for (int i = 0; i < O::VCOPIES; ++i) {
+        // D = 96: rows 96..127 of the stage are padding; their copies read
+        // channels 0..31 again (any valid source)
+        const int dst_ch = i * O::VROWS + (threadIdx.x * 16) / KVT;
+        const int64_t rows = (int64_t)i * O::VROWS - ((D == 96 && dst_ch >= 96) ? 96 : 0);
+        dma16(vt + off.v0 + rows * npk, vst + i * NT * 16 + w * 1024);
+    }
+}
 
-// Work decomposition shared by the fused kernel and the Q.K^T dump.
+// Work decomposition shared by the fused kernel and the Q.K^T dump: a
+// workgroup of WAVES waves owns (sequence, kv head, head group, query tile);
+// wave w takes query head head0 + w % hpw and rows q0 .. q0+31.
 struct Work {
     SeqInfo si;
     int s;                    // index of the sequence in the launch's table
     int hkv, head, q0;        // q0 = first query row of this wave
     int head0, hpw;           // first query head of the workgroup, heads per workgroup
-    int wg_row0, wg_rows;
     int nt_wg, nt_w;          // key tiles needed by the workgroup / by this wave
 };
 
+template <int WAVES>
 __device__ inline int wg_count(const KParams& P, int nq) {
     const int hpw = heads_per_wg(P.group);
-    const int rows = 128 / hpw;
+    const int rows = 32 * WAVES / hpw;
     return P.hkv * (P.group / hpw) * ((nq + rows - 1) / rows);
 }
 
+template <int WAVES>
 __device__ inline Work decode_work(const KParams& P) {
     Work w;
     const int hpw = heads_per_wg(P.group);
-    const int rows = 128 / hpw;
+    const int rows = 32 * WAVES / hpw;
     const int nhg = P.group / hpw;
     int local;
-    auto per = [&](int s) { return wg_count(P, P.tab.uniform ? P.tab.nq[0] : P.tab.nq[s]); };
+    auto per = [&](int s) {
+        return wg_count<WAVES>(P, P.tab.uniform ? P.tab.nq[0] : P.tab.nq[s]);
+    };
     const int s = find_seq(P, blockIdx.x, per, &local);
     w.s = s;
     w.si = seq_info(P, s);
@@ -150,7 +199,7 @@ __device__ inline Work decode_work(const KParams& P) {
     // kv head fastest (consecutive workgroups land on different XCDs), then the
     // head group, then query tiles from the heaviest (last) to the lightest
     w.hkv = local % P.hkv;
-    int rest = local / P.hkv;
+    const int rest = local / P.hkv;
     const int hg = rest % nhg;
     const int qt_rev = rest / nhg;
     const int nqt = (nq + rows - 1) / rows;
@@ -160,11 +209,10 @@ __device__ inline Work decode_work(const KParams& P) {
     w.head0 = w.hkv * P.group + hg * hpw;
     w.hpw = hpw;
     w.head = w.head0 + hw;
-    w.wg_row0 = qt * rows;
-    w.wg_rows = rows;
-    w.q0 = w.wg_row0 + rw * 32;
-    const int wg_last = min(w.wg_row0 + rows, nq) - 1;
-    int end_wg = P.causal ? min(nkv, wg_last + nkv - nq + 1) : nkv;
+    const int wg_row0 = qt * rows;
+    w.q0 = wg_row0 + rw * 32;
+    const int wg_last = min(wg_row0 + rows, nq) - 1;
+    const int end_wg = P.causal ? min(nkv, wg_last + nkv - nq + 1) : nkv;
     w.nt_wg = end_wg > 0 ? (end_wg + KVT - 1) / KVT : 0;
     if (w.q0 < nq) {
         const int w_last = min(w.q0 + 31, nq - 1);
@@ -186,29 +234,52 @@ __device__ inline void load_q(const int8_t* qrow, v4i* qf) {
         qf[c] = *reinterpret_cast<const v4i*>(qrow + 32 * c + 16 * h);
 }
 
-// S^T of one 128-key tile: sacc[b] covers keys 32b..32b+31.  The A operand of
-// output row i is key 16*((i/4)%2) + 4*(i/8) + i%4, which makes lane
-// (row, half) receive keys 32b + 16*half + r in register r (r = 0..15).
+// S^T of one 128-key tile: sacc[b] covers keys 32b..32b+31; lane (row,
+// half) receives keys 32b + 16*half + r in register r (r = 0..15).  Chunk-
+// major order keeps consecutive MFMAs independent.
 template <int D>
 __device__ inline void qk_tile(const uint8_t* Ks, const v4i* qf, v16i* sacc) {
     using T = Tile<D>;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, i = lane & 31;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int row = 32 * b + i;
-        const uint8_t* kr = Ks + row * T::KRS;
-        const int sw = swz<T::KRS>(row);
-        v16i acc;
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0;
+        for (int r = 0; r < 16; ++r) sacc[b][r] = 0;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+        v4i a[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int row = 32 * b + i;
+            a[b] = *reinterpret_cast<const v4i*>(Ks + row * T::KRS +
+                                                 (((2 * c + h) ^ swz<T::KRS>(row)) << 4));
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            sacc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[b], qf[c], sacc[b], 0, 0, 0);
+    }
+}
+
+// acc[c] += V^T(channels 32c..32c+31) . P^T for one 128-key tile held in a V
+// stage (two 64-key halves: P bytes pb[kh]).
+template <int D>
+__device__ inline void pv_tile(const uint8_t* Vs, const v8i* pb, v16f* acc) {
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, qi = lane & 31;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
-            const v4i a = *reinterpret_cast<const v4i*>(kr + (((2 * c + h) ^ sw) << 4));
-            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[c], acc, 0, 0, 0);
+            const int ch = 32 * c + qi;
+            const uint8_t* vr = Vs + ch * KVT;
+            const int sw = swz<128>(ch);
+            const v4i lo = *reinterpret_cast<const v4i*>(vr + (((4 * kh + h) ^ sw) << 4));
+            const v4i hi = *reinterpret_cast<const v4i*>(vr + (((4 * kh + 2 + h) ^ sw) << 4));
+            const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb[kh], acc[c], 0, 0, 0, 0,
+                                                                      0, 0);
         }
-        sacc[b] = acc;
-    }
 }
 
 __device__ inline float swap_max(float x) {
@@ -218,6 +289,96 @@ __device__ inline float swap_max(float x) {
 __device__ inline float swap_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Online softmax of one tile: updates the running max and sum, writes P^ in
+// the B layout of the 32x32x64 FP8 MFMA (half kh covers the lane's keys of
+// blocks 2kh and 2kh+1, bytes 0..15 and 16..31) and returns alpha, the
+// factor that moves earlier contributions to the new max.  Keys past `lim`
+// are masked when MASK.
+template <bool MASK, bool HAS_DS>
+__device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, const float* dsl,
+                                     float sml2, int kt0, int lim, float& m_run, float& l_run) {
+    const int h = (threadIdx.x & 63) >> 5;
+    float p[4][16];
+    float m_new;
+    if constexpr (!HAS_DS) {
+        if constexpr (MASK) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sacc[b][r] = kt0 + 32 * b + r > lim ? INT32_MIN : sacc[b][r];
+        }
+        // tree reductions (short dependency chains)
+        int m0[16], m1[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            m0[r] = max(sacc[0][r], sacc[1][r]);
+            m1[r] = max(sacc[2][r], sacc[3][r]);
+        }
+#pragma unroll
+        for (int n = 8; n >= 1; n >>= 1)
+#pragma unroll
+            for (int r = 0; r < n; ++r) {
+                m0[r] = max(m0[r], m0[r + n]);
+                m1[r] = max(m1[r], m1[r + n]);
+            }
+        const int mx0 = m0[0], mx1 = m1[0];
+        const float f0 = mx0 == INT32_MIN ? -INFINITY : (float)mx0 * c0;
+        const float f1 = mx1 == INT32_MIN ? -INFINITY : (float)mx1 * c1;
+        m_new = fmaxf(m_run, swap_max(fmaxf(f0, f1)));
+        const float nm = LOG2_448 - (m_new == -INFINITY ? 0.0f : m_new);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(fmaf((float)sacc[b][r], b < 2 ? c0 : c1, nm));
+                p[b][r] = MASK ? (kt0 + 32 * b + r > lim ? 0.0f : e) : e;
+            }
+    } else {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float c = b < 2 ? c0 : c1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = fmaf((float)sacc[b][r], c, dsl[32 * b + 16 * h + r] * sml2);
+                if (MASK) x = kt0 + 32 * b + r > lim ? -INFINITY : x;
+                p[b][r] = x;
+                mt = fmaxf(mt, x);
+            }
+        }
+        m_new = fmaxf(m_run, swap_max(mt));
+        const float nm = LOG2_448 - (m_new == -INFINITY ? 0.0f : m_new);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[b][r] = __builtin_amdgcn_exp2f(p[b][r] + nm);
+    }
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    // row sum of the FP32 p in 8 interleaved partial sums
+    float ps[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ps[k] = p[0][k];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (b > 0 || r >= 8) ps[r % 8] += p[b][r];
+    const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    l_run = fmaf(alpha, l_run, psum);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int wd = 0; wd < 8; ++wd) {
+            const int b = 2 * kh + wd / 4, r0 = 4 * (wd % 4);
+            uint32_t u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0], p[b][r0 + 1], 0u, false);
+            u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0 + 2], p[b][r0 + 3], u, true);
+            pb[kh][wd] = (int)u;
+        }
+    return alpha;
 }
 
 template <int DT>
@@ -235,25 +396,38 @@ __device__ inline uint32_t f2h_bits(float f) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// The fused forward kernel.
+// The fused forward kernel (8 waves, ping-pong between two groups of 4).
+//
+// Barrier epochs: group 0 runs [MFMA(t)] bar [softmax(t)] bar for t = 0, 1, ...;
+// group 1 runs the same after one extra leading barrier, so in every epoch one
+// group is in its MFMA phase and the other in its softmax phase.
+// MFMA(t) = S(t) = Q.K(t)^T plus acc += V(t-1)^T . P^(t-1)^T; softmax(t) then
+// rescales acc (which now holds tiles < t) and produces P^(t).
+// LDS lifetimes (epochs 2t, 2t+1 read K(t) and V(t-1); softmax(t) of group 1
+// runs in epoch 2t+2 and reads the score bias of tile t):
+//   K(t+1), V(t): copied at the start of MFMA(t) by each group (epochs 2t,
+//   2t+1) into the buffers freed by K(t-1), V(t-2) (last read in 2t-2, 2t-1);
+//   every wave waits for its copies before each barrier.
+//   bias(t): three buffers, as it is read up to epoch 2t+2.
 // ---------------------------------------------------------------------------
 template <int D, int DT, bool HAS_DS>
-__global__ __launch_bounds__(WG, 2) void k_attn(KParams P, const int8_t* __restrict__ qc,
-                                                const float* __restrict__ qsc,
-                                                const int8_t* __restrict__ kc,
-                                                const float* __restrict__ ksc,
-                                                const uint8_t* __restrict__ vc,
-                                                const float* __restrict__ vsc,
-                                                const float* __restrict__ ds,
-                                                const float* __restrict__ mu_v,
-                                                uint16_t* __restrict__ o,
-                                                float* __restrict__ lse) {
+__global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __restrict__ qc,
+                                                 const float* __restrict__ qsc,
+                                                 const int8_t* __restrict__ kc,
+                                                 const float* __restrict__ ksc,
+                                                 const uint8_t* __restrict__ vc,
+                                                 const float* __restrict__ vsc,
+                                                 const float* __restrict__ ds,
+                                                 const float* __restrict__ mu_v,
+                                                 uint16_t* __restrict__ o,
+                                                 float* __restrict__ lse) {
     extern __shared__ __align__(16) uint8_t smem[];
     using T = Tile<D>;
-    const Work w = decode_work(P);
+    const Work w = decode_work<FWD_WAVES>(P);
     const SeqInfo& si = w.si;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, qi = lane & 31;
+    const int grp = (threadIdx.x >> 6) >> 2;
     const int my_q = w.q0 + qi;
     const int nq = si.nq, nkv = si.nkv;
 
@@ -282,130 +456,74 @@ __global__ __launch_bounds__(WG, 2) void k_attn(KParams P, const int8_t* __restr
     float m_run = -INFINITY, l_run = 0.0f;
     const int diag = my_q + nkv - nq;          // last visible key of this row (causal)
     const int wave_diag = w.q0 + nkv - nq;     // ... of the wave's first row
+    const int lim = P.causal ? min(diag, nkv - 1) : nkv - 1;
 
-    constexpr int STAGE = T::KBYTES + T::VBYTES + (HAS_DS ? T::DSBYTES : 0);
-    if (w.nt_wg > 0) stage_tile<D, true, HAS_DS>(smem, kbase, vbase, dsb, si.npk, 0, w.hpw);
-    wait_dma();
-    __syncthreads();
+    uint8_t* kst0 = smem;
+    uint8_t* vst0 = smem + 2 * T::KBYTES;
+    uint8_t* dst0 = vst0 + 2 * T::VBYTES;      // score-bias stages (HAS_DS)
+    DmaOffsets<D, FWD_NT> off;
+    off.init(si.npk);
+
+    // stage tile 0 (K and bias) with every wave, then offset group 1
+    if (w.nt_wg > 0)
+        stage_k<D, FWD_NT, HAS_DS>(kst0, dst0, off, kbase, dsb, si.npk, 0, w.hpw);
+    bar();
+    if (grp == 1) bar();
+
+    v8i pb[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int wd = 0; wd < 8; ++wd) pb[kh][wd] = 0;
+    v16i sacc[4];
 
     for (int t = 0; t < w.nt_wg; ++t) {
+        // ---- MFMA phase ----
+        __builtin_amdgcn_s_setprio(2);
         if (t + 1 < w.nt_wg)
-            stage_tile<D, true, HAS_DS>(smem + ((t + 1) & 1) * STAGE, kbase, vbase, dsb, si.npk,
-                                        t + 1, w.hpw);
+            stage_k<D, FWD_NT, HAS_DS>(kst0 + ((t + 1) & 1) * T::KBYTES,
+                                       dst0 + ((t + 1) % 3) * T::DSBYTES, off, kbase, dsb, si.npk,
+                                       t + 1, w.hpw);
+        stage_v<D, FWD_NT>(vst0 + (t & 1) * T::VBYTES, off, vbase, si.npk, t);
         if (t < w.nt_w) {
-            const uint8_t* stage = smem + (t & 1) * STAGE;
-            v16i sacc[4];
-            qk_tile<D>(stage, qf, sacc);
-
+            qk_tile<D>(kst0 + (t & 1) * T::KBYTES, qf, sacc);
+            if (t > 0) pv_tile<D>(vst0 + ((t - 1) & 1) * T::VBYTES, pb, acc);
+        } else if (t == w.nt_w && t > 0) {
+            // this wave's rows are done: flush its last tile
+            pv_tile<D>(vst0 + ((t - 1) & 1) * T::VBYTES, pb, acc);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        bar();
+        // ---- softmax phase ----
+        if (t < w.nt_w) {
             const float c0 = sq * kscb[2 * t] * P.sml2;
             const float c1 = sq * kscb[2 * t + 1] * P.sml2;
             const int kt0 = t * KVT + 16 * h;     // key of sacc[b][r] = kt0 + 32b + r
-            const bool need_mask = (t + 1) * KVT > nkv || (P.causal && (t + 1) * KVT - 1 > wave_diag);
-            const int lim = P.causal ? min(diag, nkv - 1) : nkv - 1;
-
-            float p[4][16];
-            float m_new;
-            if constexpr (!HAS_DS) {
-                if (need_mask) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if (kt0 + 32 * b + r > lim) sacc[b][r] = INT32_MIN;
-                }
-                int mx0 = INT32_MIN, mx1 = INT32_MIN;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    mx0 = max(mx0, max(sacc[0][r], sacc[1][r]));
-                    mx1 = max(mx1, max(sacc[2][r], sacc[3][r]));
-                }
-                const float f0 = mx0 == INT32_MIN ? -INFINITY : (float)mx0 * c0;
-                const float f1 = mx1 == INT32_MIN ? -INFINITY : (float)mx1 * c1;
-                m_new = fmaxf(m_run, swap_max(fmaxf(f0, f1)));
-                const float nm = LOG2_448 - (m_new == -INFINITY ? 0.0f : m_new);
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        p[b][r] = __builtin_amdgcn_exp2f(fmaf((float)sacc[b][r], b < 2 ? c0 : c1, nm));
-                if (need_mask) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if (kt0 + 32 * b + r > lim) p[b][r] = 0.0f;
-                }
-            } else {
-                // score bias per key: x = S*c + ds*sml2, max over floats
-                const float* dsl = reinterpret_cast<const float*>(stage + T::KBYTES + T::VBYTES) +
-                                   (w.head - w.head0) * KVT;
-                float mt = -INFINITY;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const float c = b < 2 ? c0 : c1;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float bias = dsl[32 * b + 16 * h + r] * P.sml2;
-                        float x = fmaf((float)sacc[b][r], c, bias);
-                        if (need_mask && kt0 + 32 * b + r > lim) x = -INFINITY;
-                        p[b][r] = x;
-                        mt = fmaxf(mt, x);
-                    }
-                }
-                m_new = fmaxf(m_run, swap_max(mt));
-                const float nm = LOG2_448 - (m_new == -INFINITY ? 0.0f : m_new);
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) p[b][r] = __builtin_amdgcn_exp2f(p[b][r] + nm);
-            }
-
-            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            float psum = 0.0f;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) psum += p[b][r];
-            l_run = fmaf(alpha, l_run, psum);
+            const float* dsl = HAS_DS ? reinterpret_cast<const float*>(dst0 + (t % 3) * T::DSBYTES) +
+                                            (w.head - w.head0) * KVT
+                                      : nullptr;
+            const bool need_mask =
+                (t + 1) * KVT > nkv || (P.causal && (t + 1) * KVT - 1 > wave_diag);
+            float alpha;
+            if (need_mask)
+                alpha = softmax_tile<true, HAS_DS>(sacc, pb, c0, c1, dsl, P.sml2, kt0, lim, m_run,
+                                                   l_run);
+            else
+                alpha = softmax_tile<false, HAS_DS>(sacc, pb, c0, c1, dsl, P.sml2, kt0, lim,
+                                                    m_run, l_run);
+            // acc holds the tiles before t, at the previous max
             if (!__all(alpha == 1.0f)) {
 #pragma unroll
                 for (int c = 0; c < D / 32; ++c)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
             }
-
-            // P^ in the B layout of the 32x32x64 FP8 MFMA: half kh covers the
-            // lane's keys of blocks 2kh and 2kh+1 (bytes 0..15 and 16..31).
-            v8i pb[2];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int wd = 0; wd < 8; ++wd) {
-                    const int b = 2 * kh + wd / 4, r0 = 4 * (wd % 4);
-                    uint32_t u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0], p[b][r0 + 1], 0u, false);
-                    u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0 + 2], p[b][r0 + 3], u, true);
-                    pb[kh][wd] = (int)u;
-                }
-
-            const uint8_t* Vs = stage + T::KBYTES;
-#pragma unroll
-            for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-                    const int ch = 32 * c + qi;
-                    const uint8_t* vr = Vs + ch * KVT;
-                    const int sw = swz<128>(ch);
-                    const v4i lo = *reinterpret_cast<const v4i*>(vr + (((4 * kh + h) ^ sw) << 4));
-                    const v4i hi = *reinterpret_cast<const v4i*>(vr + (((4 * kh + 2 + h) ^ sw) << 4));
-                    const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb[kh], acc[c], 0,
-                                                                              0, 0, 0, 0, 0);
-                }
         }
-        wait_dma();
-        __syncthreads();
+        bar();
     }
+    if (w.nt_w > 0 && w.nt_w == w.nt_wg)
+        pv_tile<D>(vst0 + ((w.nt_wg - 1) & 1) * T::VBYTES, pb, acc);
+    if (grp == 0) bar();   // balance group 1's leading barrier
 
     // epilogue: lanes l and l+32 hold the same row's partial sums
     const float l_tot = swap_sum(l_run);
@@ -418,13 +536,16 @@ __global__ __launch_bounds__(WG, 2) void k_attn(KParams P, const int8_t* __restr
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int ch0 = 32 * c + 8 * r4 + 4 * h;
+                const float4 sv = *reinterpret_cast<const float4*>(vsc + vsb + ch0);
+                float4 mv = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (mu_v && l_tot > 0.0f) mv = *reinterpret_cast<const float4*>(mu_v + vsb + ch0);
+                const float vals[4] = {acc[c][4 * r4] * sv.x * inv_l + mv.x,
+                                       acc[c][4 * r4 + 1] * sv.y * inv_l + mv.y,
+                                       acc[c][4 * r4 + 2] * sv.z * inv_l + mv.z,
+                                       acc[c][4 * r4 + 3] * sv.w * inv_l + mv.w};
                 uint32_t bits[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float val = acc[c][4 * r4 + e] * vsc[vsb + ch0 + e] * inv_l;
-                    if (mu_v && l_tot > 0.0f) val += mu_v[vsb + ch0 + e];
-                    bits[e] = f2h_bits<DT>(val);
-                }
+                for (int e = 0; e < 4; ++e) bits[e] = f2h_bits<DT>(vals[e]);
                 *reinterpret_cast<uint2*>(orow + ch0) =
                     make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
             }
@@ -435,15 +556,15 @@ __global__ __launch_bounds__(WG, 2) void k_attn(KParams P, const int8_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Q.K^T dump for tests: the same decomposition, tile staging and qk_tile as
-// the fused kernel; the int32 scores are written instead of used.
+// Q.K^T dump for tests: the same key-tile staging and qk_tile as the fused
+// kernel (4-wave workgroups); the int32 scores are written instead of used.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(WG, 2) void k_qk_dump(KParams P, const int8_t* __restrict__ qc,
-                                                   const int8_t* __restrict__ kc,
-                                                   int32_t* __restrict__ out, DumpBase db) {
+__global__ __launch_bounds__(WG) void k_qk_dump(KParams P, const int8_t* __restrict__ qc,
+                                                const int8_t* __restrict__ kc,
+                                                int32_t* __restrict__ out, DumpBase db) {
     extern __shared__ __align__(16) uint8_t smem[];
-    const Work w = decode_work(P);
+    const Work w = decode_work<4>(P);
     const SeqInfo& si = w.si;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, qi = lane & 31;
@@ -453,6 +574,8 @@ __global__ __launch_bounds__(WG, 2) void k_qk_dump(KParams P, const int8_t* __re
     const int8_t* kbase = kc + krow0 * D;
     // the dump covers every key (no causal cut)
     const int nt = (nkv + KVT - 1) / KVT;
+    DmaOffsets<D, WG> off;
+    off.init(si.npk);
     v4i qf[D / 32];
     if (w.q0 < nq) {
         const int64_t qrow0 = si.rq * P.hq + (int64_t)w.head * si.npq;
@@ -463,10 +586,8 @@ __global__ __launch_bounds__(WG, 2) void k_qk_dump(KParams P, const int8_t* __re
     }
     const int64_t base = P.tab.uniform ? (int64_t)w.s * P.hq * nq * nkv : db.base[w.s];
     for (int t = 0; t < nt; ++t) {
-        // stage K only (the same image as the fused kernel)
-        stage_tile<D, false, false>(smem, kbase, nullptr, nullptr, si.npk, t, 1);
-        wait_dma();
-        __syncthreads();
+        stage_k<D, WG, false>(smem, nullptr, off, kbase, nullptr, si.npk, t, 1);
+        bar();
         v16i sacc[4];
         qk_tile<D>(smem, qf, sacc);
         if (w.q0 < nq && my_q < nq) {
@@ -479,21 +600,18 @@ __global__ __launch_bounds__(WG, 2) void k_qk_dump(KParams P, const int8_t* __re
                         out[base + ((int64_t)w.head * nq + my_q) * nkv + j] = sacc[b][r];
                 }
         }
-        __syncthreads();
+        bar();
     }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int D, bool HAS_DS>
-constexpr int lds_bytes() {
-    return 2 * (Tile<D>::KBYTES + Tile<D>::VBYTES + (HAS_DS ? Tile<D>::DSBYTES : 0));
-}
+namespace {
 
-int attn_blocks_host(const KParams& P) {
+int wg_count_host(const KParams& P, int waves) {
     const int hpw = heads_per_wg(P.group);
-    const int rows = 128 / hpw;
+    const int rows = 32 * waves / hpw;
     const int per_nq = P.hkv * (P.group / hpw);
     if (P.tab.uniform) return P.tab.n * per_nq * ((P.tab.nq[0] + rows - 1) / rows);
     int tot = 0;
@@ -501,30 +619,38 @@ int attn_blocks_host(const KParams& P) {
     return tot;
 }
 
+template <int D, bool HAS_DS>
+constexpr int lds_bytes() {
+    return 2 * Tile<D>::KBYTES + 2 * Tile<D>::VBYTES + (HAS_DS ? 3 * Tile<D>::DSBYTES : 0);
+}
+
 template <int D, int DT, bool HAS_DS>
-static hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const int8_t* kc,
-                         const float* ksc, const uint8_t* vc, const float* vsc, const float* ds,
-                         const float* mu_v, void* o, float* lse, int nblocks, hipStream_t st) {
+hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const int8_t* kc,
+                  const float* ksc, const uint8_t* vc, const float* vsc, const float* ds,
+                  const float* mu_v, void* o, float* lse, hipStream_t st) {
     static bool attr_set = false;   // benign race: the call is idempotent
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D, DT, HAS_DS>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<D, HAS_DS>());
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           lds_bytes<D, HAS_DS>());
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_attn<D, DT, HAS_DS><<<nblocks, WG, lds_bytes<D, HAS_DS>(), st>>>(
+    const int nblocks = wg_count_host(P, FWD_WAVES);
+    if (nblocks <= 0) return hipSuccess;
+    k_attn<D, DT, HAS_DS><<<nblocks, FWD_NT, lds_bytes<D, HAS_DS>(), st>>>(
         P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, static_cast<uint16_t*>(o), lse);
     return hipGetLastError();
 }
 
+}  // namespace
+
 hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const float* qsc,
                        const int8_t* kc, const float* ksc, const uint8_t* vc, const float* vsc,
-                       const float* ds, const float* mu_v, void* o, float* lse, int nblocks,
-                       hipStream_t st) {
-    if (nblocks <= 0) return hipSuccess;
-#define SAGE_A(D, DT)                                                                          \
-    return ds ? attn_d<D, DT, true>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, nblocks, st) \
-              : attn_d<D, DT, false>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, nblocks, st)
+                       const float* ds, const float* mu_v, void* o, float* lse, hipStream_t st) {
+#define SAGE_A(D, DT)                                                                 \
+    return ds ? attn_d<D, DT, true>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st) \
+              : attn_d<D, DT, false>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st)
     if (dtype == 0) {
         if (P.d == 64) { SAGE_A(64, 0); }
         if (P.d == 96) { SAGE_A(96, 0); }
@@ -538,7 +664,8 @@ hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const floa
 }
 
 hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,
-                          const DumpBase& db, int nblocks, hipStream_t st) {
+                          const DumpBase& db, hipStream_t st) {
+    const int nblocks = wg_count_host(P, 4);
     if (nblocks <= 0) return hipSuccess;
     if (P.d == 64)
         k_qk_dump<64><<<nblocks, WG, Tile<64>::KBYTES, st>>>(P, qc, kc, s_out, db);

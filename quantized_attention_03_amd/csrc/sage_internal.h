@@ -103,9 +103,8 @@ __device__ inline int find_seq(const KParams& P, int blk, F per, int* local) {
     return s;
 }
 
-// Workgroup shape of the fused kernel: 4 waves, each 32 query rows of one
-// query head.  hpw = query heads per workgroup (1, 2 or 4 of the GQA group),
-// rows per workgroup = 32 * 4 / hpw.
+// Query heads of one GQA group that share a workgroup (1, 2 or 4); each wave
+// owns 32 query rows of one of them.
 __host__ __device__ inline int heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
 
 // ---- launchers (sage_prepass.hip, sage_attn.hip) ----
@@ -124,13 +123,11 @@ hipError_t launch_quant_v(const KParams& P, int dtype, const void* v, const floa
 hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const float* qsc,
                        const int8_t* kc, const float* ksc, const uint8_t* vc,
                        const float* vsc, const float* ds, const float* mu_v, void* o,
-                       float* lse, int nblocks, hipStream_t st);
+                       float* lse, hipStream_t st);
 struct DumpBase {
     int64_t base[MAXSEQ];               // first element of sequence s in the dump
 };
 hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,
-                          const DumpBase& db, int nblocks, hipStream_t st);
-// workgroups of the fused kernel (and of the Q.K^T dump) for a sequence table
-int attn_blocks_host(const KParams& P);
+                          const DumpBase& db, hipStream_t st);
 
 }  // namespace sage

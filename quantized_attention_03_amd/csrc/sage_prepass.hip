@@ -135,13 +135,20 @@ __global__ __launch_bounds__(WG) void k_finalize(KParams P, int is_q, int heads,
     const int64_t base = (is_q ? si.rq : si.rk) / QBLK * heads +
                          (int64_t)h * ((is_q ? si.npq : si.npk) / QBLK);
     const int64_t o = ((int64_t)si.sid * heads + h) * d + c;
+    // the chunk values are fetched 16 at a time (independent loads in flight)
+    // and then combined strictly in chunk order
     float acc = 0.0f;
-    for (int g = 0; g < nch; ++g) {
-        const float v = partial[(base + g) * d + c];
-        if constexpr (MODE == STAT_SUM) {
-            acc = acc + v;
-        } else {
-            acc = fmaxf(acc, v);
+    const float* src = partial + base * d + c;
+    for (int g0 = 0; g0 < nch; g0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = g0 + j < nch ? src[(int64_t)(g0 + j) * d] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (g0 + j < nch) {
+                if constexpr (MODE == STAT_SUM) acc = acc + v[j];
+                else acc = fmaxf(acc, v[j]);
+            }
         }
     }
     if constexpr (MODE == STAT_SUM) {
