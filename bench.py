@@ -38,7 +38,50 @@ def _parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512, help="oracle rows per query head")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (the reference "
+                         "kernel for scaling the HBM byte counters), then exit")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_causal_gqa_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "quantized_attention_03_amd", "csrc", "sage_attn.hip")
+
+
+def kernel_digest() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary, or None when it is missing, is for another workload, or was
+    taken on a different kernel source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for ln in f:
+                if ":" in ln and not ln.startswith("#"):
+                    k, v = ln.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("workload") != workload or fields.get("kernel_source_sha256_16") != kernel_digest():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}),
+          flush=True)
 
 
 def cpu_baseline(w, q, k, v, rows_per_head: int):
@@ -80,6 +123,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import quantized_attention_03_amd as qa
     import synth
@@ -137,7 +184,7 @@ def main():
     pa, pb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     pa.record(stream)
     for _ in range(args.steps):
-        qa.sage_quant_qkv(q, k, v, **kw, **cu)
+        qa.sage_quant_qkv(q, k, v, **kw, **cu, bufs=bufs)
     pb.record(stream)
     torch.cuda.synchronize()
     pre_ms = pa.elapsed_time(pb) / args.steps
@@ -164,7 +211,8 @@ def main():
                                f"{' causal' if w.causal else ''}",
                    "global_batch": w.B, "seq_len": w.Nq, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TOPS, 4),
+                     "traffic": measured_traffic(w.name),
                      "kernel": "k_attn (fused INT8-QK / softmax / FP8-PV)",
                      "kernel_ms": round(kern_ms, 4), "ops_per_launch": exact},
         "prepass_ms": round(pre_ms, 4),

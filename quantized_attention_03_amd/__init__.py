@@ -116,20 +116,26 @@ _BUF_DT = {"mu_q": torch.float32, "mu_k": torch.float32, "mu_v": torch.float32,
 
 def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
                    smooth_k=True, smooth_v=False, sm_scale=None, cu_seqlens_q=None,
-                   cu_seqlens_kv=None):
+                   cu_seqlens_kv=None, bufs=None):
     """Run the pre-pass alone; returns a dict of flat device tensors laid out as
-    documented for sage_quant_bufs in include/sage.h."""
+    documented for sage_quant_bufs in include/sage.h.  Passing the dict of an
+    earlier call on the same problem as `bufs` reuses its buffers and
+    workspace (nothing is allocated)."""
     varlen = cu_seqlens_q is not None
     desc = make_desc(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
                      sm_scale=sm_scale, varlen=varlen)
-    sizes = quant_buf_sizes(desc, cu_seqlens_q, cu_seqlens_kv)
-    bufs = {name: torch.zeros(max(1, nbytes // torch.empty((), dtype=_BUF_DT[name]).element_size()),
-                              dtype=_BUF_DT[name], device=q.device)
-            for name, nbytes in sizes.items()}
+    if bufs is None:
+        sizes = quant_buf_sizes(desc, cu_seqlens_q, cu_seqlens_kv)
+        bufs = {name: torch.zeros(max(1, nbytes // torch.empty((), dtype=_BUF_DT[name]).element_size()),
+                                  dtype=_BUF_DT[name], device=q.device)
+                for name, nbytes in sizes.items()}
+        ws = torch.empty(workspace_size(desc, cu_seqlens_q, cu_seqlens_kv), dtype=torch.uint8,
+                         device=q.device)
+    else:
+        sizes, ws = bufs["_sizes"], bufs["_workspace"]
+        bufs = {name: bufs[name] for name in sizes}
     qb = _abi.QuantBufs(**{name: (t.data_ptr() if sizes[name] else None) for name, t in bufs.items()})
-    ws = torch.empty(workspace_size(desc, cu_seqlens_q, cu_seqlens_kv), dtype=torch.uint8,
-                     device=q.device)
     cq, n = _cu(cu_seqlens_q)
     ck, _ = _cu(cu_seqlens_kv)
     _abi.check("sage_quant_qkv",

@@ -14,8 +14,10 @@
 //    K/V tile staged in LDS feeds all of them.
 //  * S^T = Kc . Qc^T on v_mfma_i32_32x32x32_i8 (A = key rows from LDS,
 //    B = the wave's Q codes held in VGPRs).  The row max is taken on the
-//    int32 scores (the scale is positive and uniform over a 64-key block);
-//    each score then costs one exact int -> float conversion and one FMA,
+//    int32 scores (the scale is positive and uniform over a 64-key block).
+//    The accumulators start at the bit pattern of 1.5 * 2^23, so that read
+//    as a float the result is exactly 1.5 * 2^23 + S (|S| < 2^22): one exact
+//    subtraction recovers S as a float, and one FMA gives
 //    x = S * (sq*sk*sm_scale*log2 e) - (m - log2 448), rounded once.
 //  * Key rows are fed to the MFMA in a permuted order so that in the output
 //    layout each lane holds 16 consecutive keys of its own query row; lanes l
@@ -49,6 +51,10 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr float LOG2_448 = 8.807354922057604f;
+// Initial value of the Q.K^T accumulators (the bits of 1.5 * 2^23 as a float);
+// as integers the biased scores keep the order of S.
+constexpr int SBIAS_I = 0x4B400000;
+constexpr float SBIAS_F = 12582912.0f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int FWD_WAVES = 8;               // waves per workgroup of the fused kernel
 constexpr int FWD_NT = 64 * FWD_WAVES;
@@ -245,7 +251,7 @@ __device__ inline void qk_tile(const uint8_t* Ks, const v4i* qf, v16i* sacc) {
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[b][r] = 0;
+        for (int r = 0; r < 16; ++r) sacc[b][r] = SBIAS_I;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
         v4i a[4];
@@ -325,15 +331,15 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
                 m1[r] = max(m1[r], m1[r + n]);
             }
         const int mx0 = m0[0], mx1 = m1[0];
-        const float f0 = mx0 == INT32_MIN ? -INFINITY : (float)mx0 * c0;
-        const float f1 = mx1 == INT32_MIN ? -INFINITY : (float)mx1 * c1;
+        const float f0 = mx0 == INT32_MIN ? -INFINITY : (__int_as_float(mx0) - SBIAS_F) * c0;
+        const float f1 = mx1 == INT32_MIN ? -INFINITY : (__int_as_float(mx1) - SBIAS_F) * c1;
         m_new = fmaxf(m_run, swap_max(fmaxf(f0, f1)));
         const float nm = LOG2_448 - (m_new == -INFINITY ? 0.0f : m_new);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(fmaf((float)sacc[b][r], b < 2 ? c0 : c1, nm));
+                const float e = __builtin_amdgcn_exp2f(fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, b < 2 ? c0 : c1, nm));
                 p[b][r] = MASK ? (kt0 + 32 * b + r > lim ? 0.0f : e) : e;
             }
     } else {
@@ -343,7 +349,7 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
             const float c = b < 2 ? c0 : c1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = fmaf((float)sacc[b][r], c, dsl[32 * b + 16 * h + r] * sml2);
+                float x = fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, c, dsl[32 * b + 16 * h + r] * sml2);
                 if (MASK) x = kt0 + 32 * b + r > lim ? -INFINITY : x;
                 p[b][r] = x;
                 mt = fmaxf(mt, x);
@@ -597,7 +603,7 @@ __global__ __launch_bounds__(WG) void k_qk_dump(KParams P, const int8_t* __restr
                 for (int r = 0; r < 16; ++r) {
                     const int j = t * KVT + 32 * b + 16 * h + r;
                     if (j < nkv)
-                        out[base + ((int64_t)w.head * nq + my_q) * nkv + j] = sacc[b][r];
+                        out[base + ((int64_t)w.head * nq + my_q) * nkv + j] = sacc[b][r] - SBIAS_I;
                 }
         }
         bar();
