@@ -37,7 +37,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle rows per query head")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows per query head")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the reference "
                          "kernel for scaling the HBM byte counters), then exit")
@@ -118,7 +118,7 @@ def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the forward pass shards over batch/heads with no exchange; see the design notes)",
+              "(the forward pass shards over batch and heads with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -6,10 +6,10 @@ shared object (built from sage_oracle.c with gcc) and works on numpy arrays.
 
 The per-(sequence, head) functions of the C file do all the arithmetic; this
 module only slices the caller's tensors into per-(sequence, head) [N, d]
-arrays, calls them, and gathers the results.  Layouts (R-19): HND = [B, H, N, d],
+arrays, calls them, and gathers the results.  Layouts: HND = [B, H, N, d],
 NHD = [B, N, H, d]; variable-length inputs are packed over the sequences as
 [T, H, d] (NHD) or [H, T, d] (HND) with int32 prefix offsets cu_seqlens.
-GQA (R-21): query head h reads key/value head h // (Hq // Hkv).
+GQA: query head h reads key/value head h // (Hq // Hkv).
 """
 from __future__ import annotations
 
@@ -25,8 +25,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sage_oracle.c")
 _SO = os.path.join(_HERE, "libsage_oracle.so")
-BLK = 64          # Q/K quantization block (tokens), R-1
-P_SCALE = 448.0   # static P scale before the e4m3 rounding, R-13
+BLK = 64          # Q/K quantization block (tokens)
+P_SCALE = 448.0   # static P scale before the e4m3 rounding
 
 _lib = None
 

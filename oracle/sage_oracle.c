@@ -24,11 +24,10 @@
  *          the method quantizes attention itself.
  *
  * Every step below follows the plainest reading of those pages; where they
- * are silent the reading is named in the comment (R-n numbering of the
- * design notes).  Floating point: the recipe functions use FP32 exactly as
- * the method's GPU arithmetic is specified (so that quantized codes are
- * decided in the same precision on both sides); the exact reference
- * (orc_attn_exact_rows) is FP64 throughout.
+ * are silent the comment says which choice is taken.  Floating point: the
+ * recipe functions use FP32 exactly as the method's GPU arithmetic is
+ * specified (so that quantized codes are decided in the same precision on
+ * both sides); the exact reference (orc_attn_exact_rows) is FP64 throughout.
  *
  * Pins: codecs are checked against numpy/torch conversions and their
  * definitions; the channel mean against closed forms; quantizers against
@@ -113,7 +112,8 @@ ORC_EXPORT float orc_e4m3_decode(uint8_t b) {
     return (float)(s ? -v : v);
 }
 
-/* RNE encode with saturation to +-448 (R-11).  NaN maps to 0x7f. */
+/* RNE encode with saturation to +-448 (OCP e4m3fn, the FP8 flavour gfx950
+   converts to natively; the pages say only "FP8").  NaN maps to 0x7f. */
 ORC_EXPORT uint8_t orc_e4m3_encode_sat(float f) {
     if (isnan(f)) return 0x7f;
     uint8_t sign = (f2u(f) >> 31) ? 0x80 : 0x00;
@@ -151,7 +151,8 @@ ORC_EXPORT void orc_encode_e4m3(const float* in, uint8_t* out, int64_t n) {
 /* Pre-pass: smoothing and quantization ([PKG], [BLOG] item 2, [SA2] item 2) */
 /* ------------------------------------------------------------------------ */
 
-/* Per-channel mean over the n tokens of one (sequence, head) (R-6, R-7).
+/* Per-channel mean over all n tokens of one (sequence, head) -- the pages
+   fix neither the scope nor the summation order; this order is a reading.
    x is [n][d] row-major FP32 (exactly decoded inputs).  Order: tokens are
    grouped in chunks of 64 aligned to the sequence start; each chunk is summed
    token by token in FP32, the chunk sums are added in chunk order in FP32,
@@ -169,7 +170,8 @@ ORC_EXPORT void orc_channel_mean(const float* x, int64_t n, int d, float* mu) {
     }
 }
 
-/* x_s = fl32(x - mu) per element (R-8: the smoothed value stays FP32).
+/* x_s = fl32(x - mu) per element (the smoothed value stays FP32; it is not
+   re-rounded to the input dtype).
    mu == NULL means no smoothing (x_s = x). */
 ORC_EXPORT void orc_smooth(const float* x, const float* mu, int64_t n, int d, float* xs) {
     for (int64_t t = 0; t < n; ++t)
@@ -177,7 +179,8 @@ ORC_EXPORT void orc_smooth(const float* x, const float* mu, int64_t n, int d, fl
             xs[t * d + c] = mu ? x[t * d + c] - mu[c] : x[t * d + c];
 }
 
-/* Per-block symmetric INT8 quantization (R-1..R-5): blocks of `blk` tokens
+/* Per-block symmetric INT8 quantization (block size, absmax scale, rounding
+   and the zero block are readings where the pages are silent): blocks of `blk` tokens
    aligned to the sequence start (the last one may be short).  a = max |x_s|
    over the block; a == 0 gives scale 0 and zero codes; otherwise
    inv = fl32(127/a), scale = fl32(a/127), code = clamp(rne(fl32(x_s*inv)),
@@ -203,7 +206,7 @@ ORC_EXPORT void orc_quant_int8_blocks(const float* xs, int64_t n, int d, int blk
         for (int64_t t = b0; t < b1; ++t)
             for (int c = 0; c < d; ++c) {
                 float y = xs[t * d + c] * inv;
-                float r = nearbyintf(y);                      /* RNE (R-3)   */
+                float r = nearbyintf(y);                      /* RNE         */
                 if (r > 127.0f) r = 127.0f;
                 if (r < -127.0f) r = -127.0f;
                 codes[t * d + c] = (int8_t)r;
@@ -211,7 +214,8 @@ ORC_EXPORT void orc_quant_int8_blocks(const float* xs, int64_t n, int d, int blk
     }
 }
 
-/* Per-channel FP8 E4M3 quantization of (smoothed) V (R-11, R-12): per
+/* Per-channel FP8 E4M3 quantization of (smoothed) V (per channel: a V scale
+   must be constant along the contracted token axis): per
    channel c, a = max over the n tokens of |v_s|; a == 0 gives scale 0 and
    zero codes; otherwise inv = fl32(448/a), scale = fl32(a/448) and
    code = e4m3_rne_sat(fl32(v_s*inv)).  codes: [n][d]; scales: [d].          */
@@ -235,7 +239,7 @@ ORC_EXPORT void orc_quant_fp8_channels(const float* vs, int64_t n, int d,
     }
 }
 
-/* Score bias that compensates Q smoothing (R-9): subtracting mu_q from every
+/* Score bias that compensates Q smoothing: subtracting mu_q from every
    query changes each score q_i.k_j by mu_q.k_j, which depends on j, so it is
    added back: ds_j = sum_c mu_q[c] * k_s[j][c], accumulated in FP32 in
    ascending c.  k_s: [n_kv][d]; ds: [n_kv].                                 */
@@ -265,7 +269,7 @@ ORC_EXPORT void orc_qk_int32(const int8_t* qc, const int8_t* kc, int64_t nq, int
 }
 
 /* Last key index visible to query row i (inclusive), or nkv-1 if not causal.
-   Causal masking is aligned bottom-right (R-16): row i sees j <= i + nkv - nq. */
+   Causal masking is aligned bottom-right: row i sees j <= i + nkv - nq. */
 static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
     if (!causal) return nkv - 1;
     int64_t lim = i + nkv - nq;
@@ -277,14 +281,14 @@ static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
  *   kc, k_scale : int8 codes [nkv][d], FP32 scale per 64-token block
  *   vc, v_scale : e4m3 codes [nkv][d] (logical row-major), FP32 scale per channel
  *   delta_s     : FP32 [nkv] Q-smoothing compensation, or NULL
- *   mu_v        : FP32 [d] V mean to add back at the output, or NULL (R-10)
- *   bkv         : key-tile width of the online softmax (R-15)
+ *   mu_v        : FP32 [d] V mean to add back at the output, or NULL
+ *   bkv         : key-tile width of the online softmax (p^ depends on it)
  *   rows[nrows] : query rows to compute; out [nrows][d] FP32, lse [nrows]
  * Steps: s = fl32(S)*(sq*sk*sm_scale) (+ ds_j*sm_scale); for each key tile in
  * order: m' = max(m, max s), alpha = e^(m-m'), p = e^(s-m') (FP32),
- * l = alpha*l + sum p (FP32 p, R-14), p^ = e4m3(p*448) (R-13),
+ * l = alpha*l + sum p (from the FP32 p), p^ = e4m3(p*448) (static scale 448),
  * acc = alpha*acc + sum p^ * v^; finally o = acc*(v_scale/448)/l (+ mu_v).
- * A row that sees no key gives o = 0 and lse = -inf (R-17).  LSE is the
+ * A row that sees no key gives o = 0 and lse = -inf.  LSE is the
  * natural log of sum_j e^(s_j) over the scores as the recipe forms them. */
 ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
                                      const int8_t* kc, const float* k_scale,
