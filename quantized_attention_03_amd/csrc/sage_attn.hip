@@ -14,10 +14,8 @@
 //    K/V tile staged in LDS feeds all of them.
 //  * S^T = Kc . Qc^T on v_mfma_i32_32x32x32_i8 (A = key rows from LDS,
 //    B = the wave's Q codes held in VGPRs).  The row max is taken on the
-//    int32 scores (the scale is positive and uniform over a 64-key block).
-//    The accumulators start at the bit pattern of 1.5 * 2^23, so that read
-//    as a float the result is exactly 1.5 * 2^23 + S (|S| < 2^22): one exact
-//    subtraction recovers S as a float, and one FMA gives
+//    int32 scores (the scale is positive and uniform over a 64-key block);
+//    each score then costs one exact int -> float conversion and one FMA,
 //    x = S * (sq*sk*sm_scale*log2 e) - (m - log2 448), rounded once.
 //  * Key rows are fed to the MFMA in a permuted order so that in the output
 //    layout each lane holds 16 consecutive keys of its own query row; lanes l
@@ -51,8 +49,6 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr float LOG2_448 = 8.807354922057604f;
-// Initial value of the Q.K^T accumulators (the bits of 1.5 * 2^23 as a float);
-// as integers the biased scores keep the order of S.
 constexpr int SBIAS_I = 0x4B400000;
 constexpr float SBIAS_F = 12582912.0f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -297,6 +293,22 @@ __device__ inline float swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Max of the 32 integers of two accumulator blocks, as a tree of 3-input
+// maxima (16 operations).
+__device__ inline int max32(const v16i& a, const v16i& b) {
+    int l1[12];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) l1[i] = max(max(a[3 * i], a[3 * i + 1]), a[3 * i + 2]);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) l1[5 + i] = max(max(b[3 * i], b[3 * i + 1]), b[3 * i + 2]);
+    l1[10] = max(a[15], b[15]);
+    int l2[4];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) l2[i] = max(max(l1[3 * i], l1[3 * i + 1]), l1[3 * i + 2]);
+    l2[3] = l1[9];
+    return max(max(max(l2[0], l2[1]), l2[2]), max(l2[3], l1[10]));
+}
+
 // Online softmax of one tile: updates the running max and sum, writes P^ in
 // the B layout of the 32x32x64 FP8 MFMA (half kh covers the lane's keys of
 // blocks 2kh and 2kh+1, bytes 0..15 and 16..31) and returns alpha, the
@@ -316,21 +328,8 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
                 for (int r = 0; r < 16; ++r)
                     sacc[b][r] = kt0 + 32 * b + r > lim ? INT32_MIN : sacc[b][r];
         }
-        // tree reductions (short dependency chains)
-        int m0[16], m1[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            m0[r] = max(sacc[0][r], sacc[1][r]);
-            m1[r] = max(sacc[2][r], sacc[3][r]);
-        }
-#pragma unroll
-        for (int n = 8; n >= 1; n >>= 1)
-#pragma unroll
-            for (int r = 0; r < n; ++r) {
-                m0[r] = max(m0[r], m0[r + n]);
-                m1[r] = max(m1[r], m1[r + n]);
-            }
-        const int mx0 = m0[0], mx1 = m1[0];
+        // three-input max trees (v_max3_i32), one per 64-key half
+        const int mx0 = max32(sacc[0], sacc[1]), mx1 = max32(sacc[2], sacc[3]);
         const float f0 = mx0 == INT32_MIN ? -INFINITY : (__int_as_float(mx0) - SBIAS_F) * c0;
         const float f1 = mx1 == INT32_MIN ? -INFINITY : (__int_as_float(mx1) - SBIAS_F) * c1;
         m_new = fmaxf(m_run, swap_max(fmaxf(f0, f1)));
@@ -385,6 +384,16 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
             pb[kh][wd] = (int)u;
         }
     return alpha;
+}
+
+template <int D>
+__device__ inline void rescale(v16f* acc, float alpha) {
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
+    }
 }
 
 template <int DT>
@@ -482,6 +491,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
 #pragma unroll
         for (int wd = 0; wd < 8; ++wd) pb[kh][wd] = 0;
     v16i sacc[4];
+    float alpha_prev = 1.0f;   // rescale owed to acc before its next P.V
 
     for (int t = 0; t < w.nt_wg; ++t) {
         // ---- MFMA phase ----
@@ -493,17 +503,22 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         stage_v<D, FWD_NT>(vst0 + (t & 1) * T::VBYTES, off, vbase, si.npk, t);
         if (t < w.nt_w) {
             qk_tile<D>(kst0 + (t & 1) * T::KBYTES, qf, sacc);
-            if (t > 0) pv_tile<D>(vst0 + ((t - 1) & 1) * T::VBYTES, pb, acc);
+            if (t > 0) {
+                rescale<D>(acc, alpha_prev);
+                pv_tile<D>(vst0 + ((t - 1) & 1) * T::VBYTES, pb, acc);
+            }
         } else if (t == w.nt_w && t > 0) {
             // this wave's rows are done: flush its last tile
+            rescale<D>(acc, alpha_prev);
             pv_tile<D>(vst0 + ((t - 1) & 1) * T::VBYTES, pb, acc);
         }
+        // the tile's score scales, loaded ahead of the softmax phase
+        const float c0 = sq * kscb[2 * t] * P.sml2;
+        const float c1 = sq * kscb[2 * t + 1] * P.sml2;
         __builtin_amdgcn_s_setprio(0);
         bar();
         // ---- softmax phase ----
         if (t < w.nt_w) {
-            const float c0 = sq * kscb[2 * t] * P.sml2;
-            const float c1 = sq * kscb[2 * t + 1] * P.sml2;
             const int kt0 = t * KVT + 16 * h;     // key of sacc[b][r] = kt0 + 32b + r
             const float* dsl = HAS_DS ? reinterpret_cast<const float*>(dst0 + (t % 3) * T::DSBYTES) +
                                             (w.head - w.head0) * KVT
@@ -517,18 +532,16 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
             else
                 alpha = softmax_tile<false, HAS_DS>(sacc, pb, c0, c1, dsl, P.sml2, kt0, lim,
                                                     m_run, l_run);
-            // acc holds the tiles before t, at the previous max
-            if (!__all(alpha == 1.0f)) {
-#pragma unroll
-                for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
-            }
+            // acc (the tiles before t, at the previous max) is rescaled in
+            // the next MFMA phase, before the P.V of tile t
+            alpha_prev = alpha;
         }
         bar();
     }
-    if (w.nt_w > 0 && w.nt_w == w.nt_wg)
+    if (w.nt_w > 0 && w.nt_w == w.nt_wg) {
+        rescale<D>(acc, alpha_prev);
         pv_tile<D>(vst0 + ((w.nt_wg - 1) & 1) * T::VBYTES, pb, acc);
+    }
     if (grp == 0) bar();   // balance group 1's leading barrier
 
     // epilogue: lanes l and l+32 hold the same row's partial sums
