@@ -280,38 +280,66 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
     float* part_vmax = reinterpret_cast<float*>(sc + w.part_vmax);
     float* v_amax = reinterpret_cast<float*>(sc + w.v_amax);
     for (const KParams& P : kp) {
+        const int kblocks = chunk_blocks(P, false, p.hkv, false);
+        const int qblocks = chunk_blocks(P, true, p.hq, false);
+        const int nseq = tab_seqs(P);
+        // 1. chunk statistics: the means that are needed, and the absolute
+        //    maxima of V when V is not smoothed (else they need mu_v first)
+        StatJobs sj{};
+        FinJobs fj{};
+        int n = 0;
         if (p.smooth_k) {
-            SAGE_TRY(launch_stats(P, dtype, STAT_SUM, k, P.ks, 1, p.hkv, nullptr, part_k,
-                                  chunk_blocks(P, false, p.hkv, false), st));
-            SAGE_TRY(launch_finalize(P, STAT_SUM, false, p.hkv, part_k, b.mu_k, nullptr, nullptr,
-                                     tab_seqs(P), st));
+            sj.j[n] = StatJob{static_cast<const uint16_t*>(k), P.ks, nullptr, part_k, 1, p.hkv,
+                              STAT_SUM, kblocks};
+            fj.j[n++] = FinJob{part_k, b.mu_k, nullptr, nullptr, 0, p.hkv, STAT_SUM, nseq * p.hkv};
         }
         if (p.smooth_q) {
-            SAGE_TRY(launch_stats(P, dtype, STAT_SUM, q, P.qs, 0, p.hq, nullptr, part_q,
-                                  chunk_blocks(P, true, p.hq, false), st));
-            SAGE_TRY(launch_finalize(P, STAT_SUM, true, p.hq, part_q, b.mu_q, nullptr, nullptr,
-                                     tab_seqs(P), st));
+            sj.j[n] = StatJob{static_cast<const uint16_t*>(q), P.qs, nullptr, part_q, 0, p.hq,
+                              STAT_SUM, qblocks};
+            fj.j[n++] = FinJob{part_q, b.mu_q, nullptr, nullptr, 1, p.hq, STAT_SUM, nseq * p.hq};
         }
         if (p.smooth_v) {
-            SAGE_TRY(launch_stats(P, dtype, STAT_SUM, v, P.vs, 2, p.hkv, nullptr, part_v,
-                                  chunk_blocks(P, false, p.hkv, false), st));
-            SAGE_TRY(launch_finalize(P, STAT_SUM, false, p.hkv, part_v, b.mu_v, nullptr, nullptr,
-                                     tab_seqs(P), st));
+            sj.j[n] = StatJob{static_cast<const uint16_t*>(v), P.vs, nullptr, part_v, 2, p.hkv,
+                              STAT_SUM, kblocks};
+            fj.j[n++] = FinJob{part_v, b.mu_v, nullptr, nullptr, 0, p.hkv, STAT_SUM, nseq * p.hkv};
+        } else {
+            sj.j[n] = StatJob{static_cast<const uint16_t*>(v), P.vs, nullptr, part_vmax, 2, p.hkv,
+                              STAT_ABSMAX, kblocks};
+            fj.j[n++] = FinJob{part_vmax, nullptr, v_amax, b.v_scale, 0, p.hkv, STAT_ABSMAX,
+                               nseq * p.hkv};
         }
-        SAGE_TRY(launch_stats(P, dtype, STAT_ABSMAX, v, P.vs, 2, p.hkv,
-                              p.smooth_v ? b.mu_v : nullptr, part_vmax,
-                              chunk_blocks(P, false, p.hkv, false), st));
-        SAGE_TRY(launch_finalize(P, STAT_ABSMAX, false, p.hkv, part_vmax, nullptr, v_amax,
-                                 b.v_scale, tab_seqs(P), st));
-        SAGE_TRY(launch_quant_qk(P, dtype, q, P.qs, true, p.hq, p.smooth_q ? b.mu_q : nullptr,
-                                 b.q_codes, b.q_scale, nullptr, nullptr,
-                                 chunk_blocks(P, true, p.hq, true), st));
-        SAGE_TRY(launch_quant_qk(P, dtype, k, P.ks, false, p.hkv, p.smooth_k ? b.mu_k : nullptr,
-                                 b.k_codes, b.k_scale, p.smooth_q ? b.mu_q : nullptr,
-                                 p.smooth_q ? b.delta_s : nullptr,
-                                 chunk_blocks(P, false, p.hkv, true), st));
-        SAGE_TRY(launch_quant_v(P, dtype, v, p.smooth_v ? b.mu_v : nullptr, v_amax, b.v_codes,
-                                chunk_blocks(P, false, p.hkv, true), st));
+        SAGE_TRY(launch_stats(P, dtype, sj, st));
+        SAGE_TRY(launch_finalize(P, fj, st));
+        if (p.smooth_v) {
+            // 2. absolute maxima of V - mu_v
+            StatJobs sv{};
+            sv.j[0] = StatJob{static_cast<const uint16_t*>(v), P.vs, b.mu_v, part_vmax, 2, p.hkv,
+                              STAT_ABSMAX, kblocks};
+            FinJobs fv{};
+            fv.j[0] = FinJob{part_vmax, nullptr, v_amax, b.v_scale, 0, p.hkv, STAT_ABSMAX,
+                             nseq * p.hkv};
+            SAGE_TRY(launch_stats(P, dtype, sv, st));
+            SAGE_TRY(launch_finalize(P, fv, st));
+        }
+        // 3. every code and scale in one launch
+        QuantArgs qa{};
+        qa.q = static_cast<const uint16_t*>(q);
+        qa.k = static_cast<const uint16_t*>(k);
+        qa.v = static_cast<const uint16_t*>(v);
+        qa.mu_q = p.smooth_q ? b.mu_q : nullptr;
+        qa.mu_k = p.smooth_k ? b.mu_k : nullptr;
+        qa.mu_v = p.smooth_v ? b.mu_v : nullptr;
+        qa.v_amax = v_amax;
+        qa.q_codes = b.q_codes;
+        qa.k_codes = b.k_codes;
+        qa.v_codes = b.v_codes;
+        qa.q_scale = b.q_scale;
+        qa.k_scale = b.k_scale;
+        qa.delta_s = p.smooth_q ? b.delta_s : nullptr;
+        qa.nq = chunk_blocks(P, true, p.hq, true);
+        qa.nk = chunk_blocks(P, false, p.hkv, true);
+        qa.nv = chunk_blocks(P, false, p.hkv, true);
+        SAGE_TRY(launch_quant(P, dtype, qa, st));
     }
     return SAGE_OK;
 }

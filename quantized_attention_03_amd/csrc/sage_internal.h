@@ -109,17 +109,44 @@ __host__ __device__ inline int heads_per_wg(int group) { return group % 4 == 0 ?
 
 // ---- launchers (sage_prepass.hip, sage_attn.hip) ----
 enum StatMode { STAT_SUM = 0, STAT_ABSMAX = 1 };
-hipError_t launch_stats(const KParams& P, int dtype, int mode, const void* x, Strides xs,
-                        int which, int heads, const float* mu, float* partial, int nblocks,
-                        hipStream_t st);
-hipError_t launch_finalize(const KParams& P, int mode, bool is_q, int heads,
-                           const float* partial, float* out_mu, float* out_amax,
-                           float* out_scale, int nseq, hipStream_t st);
-hipError_t launch_quant_qk(const KParams& P, int dtype, const void* x, Strides xs, bool is_q,
-                           int heads, const float* mu, int8_t* codes, float* scales,
-                           const float* mu_q, float* delta_s, int nblocks, hipStream_t st);
-hipError_t launch_quant_v(const KParams& P, int dtype, const void* v, const float* mu,
-                          const float* amax, uint8_t* codes, int nblocks, hipStream_t st);
+
+// One statistics job of the pre-pass: per-chunk channel sums (STAT_SUM) or
+// absolute maxima of x - mu (STAT_ABSMAX) of one tensor (which: 0 q, 1 k, 2 v)
+// into `partial`; nblocks = chunks x heads over the launch's sequences.
+struct StatJob {
+    const uint16_t* x;
+    Strides xs;
+    const float* mu;
+    float* partial;
+    int32_t which, heads, mode, nblocks;
+};
+struct StatJobs {
+    StatJob j[3];   // unused entries have nblocks = 0
+};
+// One finalize job: per (sequence, head, channel) the mean (STAT_SUM, into
+// out_mu) or the absolute maximum and its E4M3 scale (STAT_ABSMAX).
+struct FinJob {
+    const float* partial;
+    float* out_mu;
+    float* out_amax;
+    float* out_scale;
+    int32_t is_q, heads, mode, nblocks;
+};
+struct FinJobs {
+    FinJob j[3];
+};
+// Everything the one-launch quantization needs.
+struct QuantArgs {
+    const uint16_t *q, *k, *v;
+    const float *mu_q, *mu_k, *mu_v, *v_amax;
+    int8_t *q_codes, *k_codes;
+    uint8_t* v_codes;
+    float *q_scale, *k_scale, *delta_s;
+    int32_t nq, nk, nv;   // workgroups: Q blocks, K blocks, V chunks
+};
+hipError_t launch_stats(const KParams& P, int dtype, const StatJobs& J, hipStream_t st);
+hipError_t launch_finalize(const KParams& P, const FinJobs& J, hipStream_t st);
+hipError_t launch_quant(const KParams& P, int dtype, const QuantArgs& A, hipStream_t st);
 hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const float* qsc,
                        const int8_t* kc, const float* ksc, const uint8_t* vc,
                        const float* vsc, const float* ds, const float* mu_v, void* o,

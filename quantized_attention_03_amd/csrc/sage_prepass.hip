@@ -80,83 +80,114 @@ struct ChunkCount {
 // partial (s,h,g,c) at (((r_s/64)*heads + h*(np_s/64) + g)*d + c).
 // ---------------------------------------------------------------------------
 template <int DT, int MODE>
-__global__ __launch_bounds__(WG) void k_stats(KParams P, const uint16_t* __restrict__ x,
-                                              Strides xs, int which, int heads,
-                                              const float* __restrict__ mu,
-                                              float* __restrict__ partial) {
-    const bool is_q = which == 0;     // 0 = q, 1 = k, 2 = v
+__device__ inline void stats_chunk(const KParams& P, const StatJob& J, int blk) {
+    const bool is_q = J.which == 0;     // 0 = q, 1 = k, 2 = v
     int local;
-    ChunkCount cnt{&P, is_q, heads, 0};
-    const int s = find_seq(P, blockIdx.x, cnt, &local);
+    ChunkCount cnt{&P, is_q, J.heads, 0};
+    const int s = find_seq(P, blk, cnt, &local);
     const SeqInfo si = seq_info(P, s);
     const int n = is_q ? si.nq : si.nkv;
     const int nch = (n + QBLK - 1) / QBLK;
     const int h = local / nch, g = local % nch;
     const int d = P.d;
-    const int64_t el0 = which == 0 ? si.q_el : (which == 1 ? si.k_el : si.v_el);
-    const int64_t base = (is_q ? si.rq : si.rk) / QBLK * heads +
+    const int64_t el0 = J.which == 0 ? si.q_el : (J.which == 1 ? si.k_el : si.v_el);
+    const int64_t base = (is_q ? si.rq : si.rk) / QBLK * J.heads +
                          (int64_t)h * ((is_q ? si.npq : si.npk) / QBLK) + g;
     const int c = threadIdx.x;
     if (c >= d) return;
-    const int64_t off = el0 + (int64_t)h * xs.h + c;
+    const uint16_t* x = J.x;
+    const int64_t off = el0 + (int64_t)h * J.xs.h + c;
     const int t0 = g * QBLK, t1 = min(t0 + QBLK, n);
-    const float m = (MODE == STAT_ABSMAX && mu) ? mu[((int64_t)si.sid * heads + h) * d + c] : 0.0f;
+    const float m = (MODE == STAT_ABSMAX && J.mu) ? J.mu[((int64_t)si.sid * J.heads + h) * d + c]
+                                                  : 0.0f;
     float acc = 0.0f;
 #pragma unroll 16
     for (int t = t0; t < t1; ++t) {
-        const float v = h2f<DT>(x[off + (int64_t)t * xs.n]);
+        const float v = h2f<DT>(x[off + (int64_t)t * J.xs.n]);
         if constexpr (MODE == STAT_SUM) {
             acc = acc + v;
         } else {
             acc = fmaxf(acc, fabsf(v - m));
         }
     }
-    partial[base * d + c] = acc;
+    J.partial[base * d + c] = acc;
+}
+
+template <int DT>
+__device__ inline void stats_job(const KParams& P, const StatJob& J, int blk) {
+    if (J.mode == STAT_SUM) stats_chunk<DT, STAT_SUM>(P, J, blk);
+    else stats_chunk<DT, STAT_ABSMAX>(P, J, blk);
+}
+
+// Up to three statistics jobs in one launch; the grid is their block counts
+// back to back.
+template <int DT>
+__global__ __launch_bounds__(WG) void k_stats(KParams P, StatJobs J) {
+    int blk = blockIdx.x;
+    if (blk < J.j[0].nblocks) { stats_job<DT>(P, J.j[0], blk); return; }
+    blk -= J.j[0].nblocks;
+    if (blk < J.j[1].nblocks) { stats_job<DT>(P, J.j[1], blk); return; }
+    blk -= J.j[1].nblocks;
+    stats_job<DT>(P, J.j[2], blk);
 }
 
 // ---------------------------------------------------------------------------
 // Finalize per (sequence, head, channel).  STAT_SUM: mu = (chunk sums added in
 // chunk order) / n.  STAT_ABSMAX: amax = max of the chunk maxima and
-// scale = amax / 448.
+// scale = amax / 448.  The workgroup first copies up to 64 chunks of partials
+// into LDS (all loads in flight at once); thread c then combines its
+// channel's values strictly in chunk order.
 // ---------------------------------------------------------------------------
+constexpr int FIN_CHUNKS = 64;
+
 template <int MODE>
-__global__ __launch_bounds__(WG) void k_finalize(KParams P, int is_q, int heads,
-                                                 const float* __restrict__ partial,
-                                                 float* __restrict__ out_mu,
-                                                 float* __restrict__ out_amax,
-                                                 float* __restrict__ out_scale) {
-    const int s = blockIdx.x / heads, h = blockIdx.x % heads;
+__device__ inline void finalize_one(const KParams& P, const FinJob& J, int blk, float* lds) {
+    const int s = blk / J.heads, h = blk % J.heads;
     const int c = threadIdx.x;
     const int d = P.d;
-    if (c >= d) return;
     const SeqInfo si = seq_info(P, s);
-    const int n = is_q ? si.nq : si.nkv;
+    const int n = J.is_q ? si.nq : si.nkv;
     const int nch = (n + QBLK - 1) / QBLK;
-    const int64_t base = (is_q ? si.rq : si.rk) / QBLK * heads +
-                         (int64_t)h * ((is_q ? si.npq : si.npk) / QBLK);
-    const int64_t o = ((int64_t)si.sid * heads + h) * d + c;
-    // the chunk values are fetched 16 at a time (independent loads in flight)
-    // and then combined strictly in chunk order
+    const int64_t base = (J.is_q ? si.rq : si.rk) / QBLK * J.heads +
+                         (int64_t)h * ((J.is_q ? si.npq : si.npk) / QBLK);
+    const float4* src = reinterpret_cast<const float4*>(J.partial + base * d);
     float acc = 0.0f;
-    const float* src = partial + base * d + c;
-    for (int g0 = 0; g0 < nch; g0 += 16) {
-        float v[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = g0 + j < nch ? src[(int64_t)(g0 + j) * d] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            if (g0 + j < nch) {
-                if constexpr (MODE == STAT_SUM) acc = acc + v[j];
-                else acc = fmaxf(acc, v[j]);
+    for (int g0 = 0; g0 < nch; g0 += FIN_CHUNKS) {
+        const int cnt = min(FIN_CHUNKS, nch - g0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < cnt * d / 4; i += WG) reinterpret_cast<float4*>(lds)[i] = src[g0 * d / 4 + i];
+        __syncthreads();
+        if (c < d) {
+            for (int j = 0; j < cnt; ++j) {
+                if constexpr (MODE == STAT_SUM) acc = acc + lds[j * d + c];
+                else acc = fmaxf(acc, lds[j * d + c]);
             }
         }
     }
+    if (c >= d) return;
+    const int64_t o = ((int64_t)si.sid * J.heads + h) * d + c;
     if constexpr (MODE == STAT_SUM) {
-        out_mu[o] = n > 0 ? acc / (float)n : 0.0f;
+        J.out_mu[o] = n > 0 ? acc / (float)n : 0.0f;
     } else {
-        out_amax[o] = acc;
-        out_scale[o] = acc / 448.0f;
+        J.out_amax[o] = acc;
+        J.out_scale[o] = acc / 448.0f;
     }
+}
+
+__device__ inline void finalize_job(const KParams& P, const FinJob& J, int blk, float* lds) {
+    if (J.mode == STAT_SUM) finalize_one<STAT_SUM>(P, J, blk, lds);
+    else finalize_one<STAT_ABSMAX>(P, J, blk, lds);
+}
+
+// Up to three finalize jobs (one workgroup per sequence and head each).
+__global__ __launch_bounds__(WG) void k_finalize(KParams P, FinJobs J) {
+    __shared__ __align__(16) float lds[FIN_CHUNKS * 128];
+    int blk = blockIdx.x;
+    if (blk < J.j[0].nblocks) { finalize_job(P, J.j[0], blk, lds); return; }
+    blk -= J.j[0].nblocks;
+    if (blk < J.j[1].nblocks) { finalize_job(P, J.j[1], blk, lds); return; }
+    blk -= J.j[1].nblocks;
+    finalize_job(P, J.j[2], blk, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -170,22 +201,21 @@ __global__ __launch_bounds__(WG) void k_finalize(KParams P, int is_q, int heads,
 // FP32) is written for every query head of the group.
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool DELTA>
-__global__ __launch_bounds__(WG) void k_quant_qk(KParams P, const uint16_t* __restrict__ x,
-                                                 Strides xs, int is_q, int heads,
-                                                 const float* __restrict__ mu,
-                                                 int8_t* __restrict__ codes,
-                                                 float* __restrict__ scales,
-                                                 const float* __restrict__ mu_q,
-                                                 float* __restrict__ delta_s) {
+__device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restrict__ x,
+                                      Strides xs, int is_q, int heads,
+                                      const float* __restrict__ mu, int8_t* __restrict__ codes,
+                                      float* __restrict__ scales,
+                                      const float* __restrict__ mu_q,
+                                      float* __restrict__ delta_s, int blkid, float* smf) {
     constexpr int GPR = D / 8;              // granules per token row
     constexpr int NG = QBLK * GPR;          // granules per block
     constexpr int PER = (NG + WG - 1) / WG; // granules per thread
-    __shared__ float red[WG / 64];
-    __shared__ float ks_lds[DELTA ? QBLK * D : 1];
+    float* red = smf;                       // WG / 64 floats
+    float* ks_lds = smf + WG / 64;          // QBLK * D floats (DELTA)
 
     int local;
     ChunkCount cnt{&P, is_q != 0, heads, 1};
-    const int s = find_seq(P, blockIdx.x, cnt, &local);
+    const int s = find_seq(P, blkid, cnt, &local);
     const SeqInfo si = seq_info(P, s);
     const int n = is_q ? si.nq : si.nkv;
     const int np = is_q ? si.npq : si.npk;
@@ -267,20 +297,22 @@ __global__ __launch_bounds__(WG) void k_quant_qk(KParams P, const uint16_t* __re
 // Codes pass through LDS for the transpose; chunks past the sequence end and
 // tokens past it get zero codes.
 // ---------------------------------------------------------------------------
+template <int D>
+constexpr int quant_v_lds_bytes() { return D * (QBLK + 4); }
+
 template <int DT, int D>
-__global__ __launch_bounds__(WG) void k_quant_v(KParams P, const uint16_t* __restrict__ v,
-                                                const float* __restrict__ mu,
-                                                const float* __restrict__ amax,
-                                                uint8_t* __restrict__ codes) {
+__device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restrict__ v,
+                                     const float* __restrict__ mu,
+                                     const float* __restrict__ amax,
+                                     uint8_t* __restrict__ codes, int blkid, uint8_t* tr) {
     constexpr int GPR = D / 8;
     constexpr int NG = QBLK * GPR;
     constexpr int PER = (NG + WG - 1) / WG;
     constexpr int TS = QBLK + 4;            // LDS row stride (bytes) of the transpose
-    __shared__ uint8_t tr[D * TS];
 
     int local;
     ChunkCount cnt{&P, false, P.hkv, 1};
-    const int s = find_seq(P, blockIdx.x, cnt, &local);
+    const int s = find_seq(P, blkid, cnt, &local);
     const SeqInfo si = seq_info(P, s);
     const int n = si.nkv;
     const int nch = si.npk / QBLK;
@@ -334,75 +366,64 @@ __global__ __launch_bounds__(WG) void k_quant_v(KParams P, const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// All quantization of a problem in one launch: the Q blocks, then the K
+// blocks (with the score bias when Q is smoothed), then the V chunks.
+// ---------------------------------------------------------------------------
+template <int DT, int D, bool DELTA>
+__global__ __launch_bounds__(WG) void k_quant(KParams P, QuantArgs A) {
+    constexpr int QK_LDS = (WG / 64 + (DELTA ? QBLK * D : 0)) * 4;
+    constexpr int LDS = QK_LDS > quant_v_lds_bytes<D>() ? QK_LDS : quant_v_lds_bytes<D>();
+    __shared__ __align__(16) uint8_t sm[LDS];
+    int blk = blockIdx.x;
+    if (blk < A.nq) {
+        quant_qk_block<DT, D, false>(P, A.q, P.qs, 1, P.hq, A.mu_q, A.q_codes, A.q_scale,
+                                     nullptr, nullptr, blk, reinterpret_cast<float*>(sm));
+        return;
+    }
+    blk -= A.nq;
+    if (blk < A.nk) {
+        quant_qk_block<DT, D, DELTA>(P, A.k, P.ks, 0, P.hkv, A.mu_k, A.k_codes, A.k_scale,
+                                     A.mu_q, A.delta_s, blk, reinterpret_cast<float*>(sm));
+        return;
+    }
+    blk -= A.nk;
+    quant_v_chunk<DT, D>(P, A.v, A.mu_v, A.v_amax, A.v_codes, blk, sm);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_stats(const KParams& P, int dtype, int mode, const void* x, Strides xs,
-                        int which, int heads, const float* mu, float* partial, int nblocks,
-                        hipStream_t st) {
-    if (nblocks <= 0) return hipSuccess;
-    const uint16_t* xp = static_cast<const uint16_t*>(x);
-    if (dtype == 0 && mode == STAT_SUM)
-        k_stats<0, STAT_SUM><<<nblocks, WG, 0, st>>>(P, xp, xs, which, heads, mu, partial);
-    else if (dtype == 0)
-        k_stats<0, STAT_ABSMAX><<<nblocks, WG, 0, st>>>(P, xp, xs, which, heads, mu, partial);
-    else if (mode == STAT_SUM)
-        k_stats<1, STAT_SUM><<<nblocks, WG, 0, st>>>(P, xp, xs, which, heads, mu, partial);
-    else
-        k_stats<1, STAT_ABSMAX><<<nblocks, WG, 0, st>>>(P, xp, xs, which, heads, mu, partial);
+hipError_t launch_stats(const KParams& P, int dtype, const StatJobs& J, hipStream_t st) {
+    const int nb = J.j[0].nblocks + J.j[1].nblocks + J.j[2].nblocks;
+    if (nb <= 0) return hipSuccess;
+    if (dtype == 0) k_stats<0><<<nb, WG, 0, st>>>(P, J);
+    else k_stats<1><<<nb, WG, 0, st>>>(P, J);
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const KParams& P, int mode, bool is_q, int heads,
-                           const float* partial, float* out_mu, float* out_amax,
-                           float* out_scale, int nseq, hipStream_t st) {
-    if (nseq <= 0) return hipSuccess;
-    if (mode == STAT_SUM)
-        k_finalize<STAT_SUM><<<nseq * heads, WG, 0, st>>>(P, is_q, heads, partial, out_mu,
-                                                           out_amax, out_scale);
-    else
-        k_finalize<STAT_ABSMAX><<<nseq * heads, WG, 0, st>>>(P, is_q, heads, partial, out_mu,
-                                                              out_amax, out_scale);
+hipError_t launch_finalize(const KParams& P, const FinJobs& J, hipStream_t st) {
+    const int nb = J.j[0].nblocks + J.j[1].nblocks + J.j[2].nblocks;
+    if (nb <= 0) return hipSuccess;
+    k_finalize<<<nb, WG, 0, st>>>(P, J);
     return hipGetLastError();
 }
 
 template <int DT, int D>
-static void quant_qk_d(const KParams& P, const uint16_t* x, Strides xs, bool is_q, int heads,
-                       const float* mu, int8_t* codes, float* scales, const float* mu_q,
-                       float* delta_s, int nblocks, hipStream_t st) {
-    if (delta_s)
-        k_quant_qk<DT, D, true><<<nblocks, WG, 0, st>>>(P, x, xs, is_q, heads, mu, codes, scales,
-                                                        mu_q, delta_s);
-    else
-        k_quant_qk<DT, D, false><<<nblocks, WG, 0, st>>>(P, x, xs, is_q, heads, mu, codes,
-                                                         scales, mu_q, delta_s);
+static void quant_d(const KParams& P, const QuantArgs& A, int nb, hipStream_t st) {
+    if (A.delta_s) k_quant<DT, D, true><<<nb, WG, 0, st>>>(P, A);
+    else k_quant<DT, D, false><<<nb, WG, 0, st>>>(P, A);
 }
 
-hipError_t launch_quant_qk(const KParams& P, int dtype, const void* x, Strides xs, bool is_q,
-                           int heads, const float* mu, int8_t* codes, float* scales,
-                           const float* mu_q, float* delta_s, int nblocks, hipStream_t st) {
-    if (nblocks <= 0) return hipSuccess;
-    const uint16_t* xp = static_cast<const uint16_t*>(x);
-#define SAGE_QQ(DT, D) quant_qk_d<DT, D>(P, xp, xs, is_q, heads, mu, codes, scales, mu_q, delta_s, nblocks, st)
+hipError_t launch_quant(const KParams& P, int dtype, const QuantArgs& A, hipStream_t st) {
+    const int nb = A.nq + A.nk + A.nv;
+    if (nb <= 0) return hipSuccess;
+#define SAGE_QA(DT, D) quant_d<DT, D>(P, A, nb, st)
     if (dtype == 0) {
-        if (P.d == 64) SAGE_QQ(0, 64); else if (P.d == 96) SAGE_QQ(0, 96); else SAGE_QQ(0, 128);
+        if (P.d == 64) SAGE_QA(0, 64); else if (P.d == 96) SAGE_QA(0, 96); else SAGE_QA(0, 128);
     } else {
-        if (P.d == 64) SAGE_QQ(1, 64); else if (P.d == 96) SAGE_QQ(1, 96); else SAGE_QQ(1, 128);
+        if (P.d == 64) SAGE_QA(1, 64); else if (P.d == 96) SAGE_QA(1, 96); else SAGE_QA(1, 128);
     }
-#undef SAGE_QQ
-    return hipGetLastError();
-}
-
-hipError_t launch_quant_v(const KParams& P, int dtype, const void* v, const float* mu,
-                          const float* amax, uint8_t* codes, int nblocks, hipStream_t st) {
-    if (nblocks <= 0) return hipSuccess;
-    const uint16_t* vp = static_cast<const uint16_t*>(v);
-#define SAGE_QV(DT, D) k_quant_v<DT, D><<<nblocks, WG, 0, st>>>(P, vp, mu, amax, codes)
-    if (dtype == 0) {
-        if (P.d == 64) SAGE_QV(0, 64); else if (P.d == 96) SAGE_QV(0, 96); else SAGE_QV(0, 128);
-    } else {
-        if (P.d == 64) SAGE_QV(1, 64); else if (P.d == 96) SAGE_QV(1, 96); else SAGE_QV(1, 128);
-    }
-#undef SAGE_QV
+#undef SAGE_QA
     return hipGetLastError();
 }
 
