@@ -265,6 +265,19 @@ int chunk_blocks(const KParams& k, bool is_q, int heads, bool padded) {
 
 int tab_seqs(const KParams& k) { return k.tab.n; }
 
+// Workgroups of a statistics job over Q (is_q) or K/V.
+int stat_blocks(const KParams& k, bool is_q, int heads) {
+    const int cpw = stat_chunks_per_wg(k.d);
+    int tot = 0;
+    const int n = k.tab.uniform ? 1 : k.tab.n;
+    for (int s = 0; s < n; ++s) {
+        const int len = is_q ? k.tab.nq[s] : k.tab.nkv[s];
+        const int nch = (len + QBLK - 1) / QBLK;
+        tot += heads * ((nch + cpw - 1) / cpw);
+    }
+    return k.tab.uniform ? tot * k.tab.n : tot;
+}
+
 #define SAGE_TRY(x)                                  \
     do {                                             \
         if ((x) != hipSuccess) return SAGE_ERR_HIP;  \
@@ -280,8 +293,8 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
     float* part_vmax = reinterpret_cast<float*>(sc + w.part_vmax);
     float* v_amax = reinterpret_cast<float*>(sc + w.v_amax);
     for (const KParams& P : kp) {
-        const int kblocks = chunk_blocks(P, false, p.hkv, false);
-        const int qblocks = chunk_blocks(P, true, p.hq, false);
+        const int kblocks = stat_blocks(P, false, p.hkv);
+        const int qblocks = stat_blocks(P, true, p.hq);
         const int nseq = tab_seqs(P);
         // 1. chunk statistics: the means that are needed, and the absolute
         //    maxima of V when V is not smoothed (else they need mu_v first)

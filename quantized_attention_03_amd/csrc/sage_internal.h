@@ -144,6 +144,9 @@ struct QuantArgs {
     float *q_scale, *k_scale, *delta_s;
     int32_t nq, nk, nv;   // workgroups: Q blocks, K blocks, V chunks
 };
+// Chunks of 64 tokens one statistics workgroup covers (per sequence and head
+// the launch needs ceil(chunks / this) workgroups).
+int stat_chunks_per_wg(int d);
 hipError_t launch_stats(const KParams& P, int dtype, const StatJobs& J, hipStream_t st);
 hipError_t launch_finalize(const KParams& P, const FinJobs& J, hipStream_t st);
 hipError_t launch_quant(const KParams& P, int dtype, const QuantArgs& A, hipStream_t st);

@@ -74,61 +74,103 @@ struct ChunkCount {
 
 // ---------------------------------------------------------------------------
 // Per-chunk channel statistics: STAT_SUM gives the in-order FP32 sum of the
-// chunk's tokens, STAT_ABSMAX the max of |x - mu| (mu may be null).  One
-// workgroup per (sequence, head, 64-token chunk); thread c < d owns channel c
-// and walks the chunk's tokens in order (each step is a coalesced row read).
+// chunk's tokens, STAT_ABSMAX the max of |x - mu| (mu may be null).  A
+// workgroup covers up to CPW consecutive 64-token chunks of one (sequence,
+// head); thread (chunk j, granule e) owns channels 8e .. 8e+7 of chunk j and
+// walks its tokens in order with 16-byte row reads.
 // partial (s,h,g,c) at (((r_s/64)*heads + h*(np_s/64) + g)*d + c).
 // ---------------------------------------------------------------------------
-template <int DT, int MODE>
-__device__ inline void stats_chunk(const KParams& P, const StatJob& J, int blk) {
+template <int D>
+struct StatShape {
+    static constexpr int GPR = D / 8;        // 16-byte granules per token row
+    static constexpr int CPW = WG / GPR;     // chunks per workgroup
+};
+
+// Workgroups sequence s owns in a statistics launch.
+template <int D>
+struct StatCount {
+    const KParams* P;
+    bool is_q;
+    int heads;
+    __device__ int operator()(int s) const {
+        const int n = P->tab.uniform ? (is_q ? P->tab.nq[0] : P->tab.nkv[0])
+                                     : (is_q ? P->tab.nq[s] : P->tab.nkv[s]);
+        const int nch = (n + QBLK - 1) / QBLK;
+        return heads * ((nch + StatShape<D>::CPW - 1) / StatShape<D>::CPW);
+    }
+};
+
+template <int DT, int D, int MODE>
+__device__ inline void stats_chunks(const KParams& P, const StatJob& J, int blk) {
+    using SS = StatShape<D>;
     const bool is_q = J.which == 0;     // 0 = q, 1 = k, 2 = v
     int local;
-    ChunkCount cnt{&P, is_q, J.heads, 0};
+    StatCount<D> cnt{&P, is_q, J.heads};
     const int s = find_seq(P, blk, cnt, &local);
     const SeqInfo si = seq_info(P, s);
     const int n = is_q ? si.nq : si.nkv;
     const int nch = (n + QBLK - 1) / QBLK;
-    const int h = local / nch, g = local % nch;
-    const int d = P.d;
+    const int ngrp = (nch + SS::CPW - 1) / SS::CPW;
+    const int h = local / ngrp, grp = local % ngrp;
+    const int j = threadIdx.x / SS::GPR, e = threadIdx.x % SS::GPR;
+    const int g = grp * SS::CPW + j;                 // chunk of this thread
+    if (j >= SS::CPW || g >= nch) return;
     const int64_t el0 = J.which == 0 ? si.q_el : (J.which == 1 ? si.k_el : si.v_el);
     const int64_t base = (is_q ? si.rq : si.rk) / QBLK * J.heads +
                          (int64_t)h * ((is_q ? si.npq : si.npk) / QBLK) + g;
-    const int c = threadIdx.x;
-    if (c >= d) return;
-    const uint16_t* x = J.x;
-    const int64_t off = el0 + (int64_t)h * J.xs.h + c;
+    const uint16_t* x = J.x + el0 + (int64_t)h * J.xs.h + 8 * e;
     const int t0 = g * QBLK, t1 = min(t0 + QBLK, n);
-    const float m = (MODE == STAT_ABSMAX && J.mu) ? J.mu[((int64_t)si.sid * J.heads + h) * d + c]
-                                                  : 0.0f;
-    float acc = 0.0f;
-#pragma unroll 16
-    for (int t = t0; t < t1; ++t) {
-        const float v = h2f<DT>(x[off + (int64_t)t * J.xs.n]);
-        if constexpr (MODE == STAT_SUM) {
-            acc = acc + v;
-        } else {
-            acc = fmaxf(acc, fabsf(v - m));
+    float m[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        m[k] = (MODE == STAT_ABSMAX && J.mu) ? J.mu[((int64_t)si.sid * J.heads + h) * D + 8 * e + k]
+                                             : 0.0f;
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    int t = t0;
+    for (; t + 8 <= t1; t += 8) {
+        float v[8][8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) load8<DT>(x + (int64_t)(t + u) * J.xs.n, v[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if constexpr (MODE == STAT_SUM) acc[k] = acc[k] + v[u][k];
+                else acc[k] = fmaxf(acc[k], fabsf(v[u][k] - m[k]));
+            }
+    }
+    for (; t < t1; ++t) {
+        float v[8];
+        load8<DT>(x + (int64_t)t * J.xs.n, v);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if constexpr (MODE == STAT_SUM) acc[k] = acc[k] + v[k];
+            else acc[k] = fmaxf(acc[k], fabsf(v[k] - m[k]));
         }
     }
-    J.partial[base * d + c] = acc;
+    float4* dst = reinterpret_cast<float4*>(J.partial + base * D + 8 * e);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
-template <int DT>
-__device__ inline void stats_job(const KParams& P, const StatJob& J, int blk) {
-    if (J.mode == STAT_SUM) stats_chunk<DT, STAT_SUM>(P, J, blk);
-    else stats_chunk<DT, STAT_ABSMAX>(P, J, blk);
+template <int DT, int D>
+__device__ inline void stats_job_d(const KParams& P, const StatJob& J, int blk) {
+    if (J.mode == STAT_SUM) stats_chunks<DT, D, STAT_SUM>(P, J, blk);
+    else stats_chunks<DT, D, STAT_ABSMAX>(P, J, blk);
 }
 
 // Up to three statistics jobs in one launch; the grid is their block counts
 // back to back.
-template <int DT>
+template <int DT, int D>
 __global__ __launch_bounds__(WG) void k_stats(KParams P, StatJobs J) {
     int blk = blockIdx.x;
-    if (blk < J.j[0].nblocks) { stats_job<DT>(P, J.j[0], blk); return; }
+    if (blk < J.j[0].nblocks) { stats_job_d<DT, D>(P, J.j[0], blk); return; }
     blk -= J.j[0].nblocks;
-    if (blk < J.j[1].nblocks) { stats_job<DT>(P, J.j[1], blk); return; }
+    if (blk < J.j[1].nblocks) { stats_job_d<DT, D>(P, J.j[1], blk); return; }
     blk -= J.j[1].nblocks;
-    stats_job<DT>(P, J.j[2], blk);
+    stats_job_d<DT, D>(P, J.j[2], blk);
 }
 
 // ---------------------------------------------------------------------------
@@ -305,10 +347,9 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
                                      const float* __restrict__ mu,
                                      const float* __restrict__ amax,
                                      uint8_t* __restrict__ codes, int blkid, uint8_t* tr) {
-    constexpr int GPR = D / 8;
-    constexpr int NG = QBLK * GPR;
-    constexpr int PER = (NG + WG - 1) / WG;
-    constexpr int TS = QBLK + 4;            // LDS row stride (bytes) of the transpose
+    constexpr int GPR = D / 8;               // 8-channel granules of a token row
+    constexpr int TASKS = GPR * (QBLK / 4);  // (granule, group of 4 tokens) pairs
+    constexpr int TS = QBLK + 4;             // LDS bytes per channel row of the transpose
 
     int local;
     ChunkCount cnt{&P, false, P.hkv, 1};
@@ -321,47 +362,50 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
     const float* muh = mu ? mu + ((int64_t)si.sid * P.hkv + h) * D : nullptr;
     const float* amh = amax + ((int64_t)si.sid * P.hkv + h) * D;
 
+    // Each task reads 4 consecutive tokens of one granule (the 16 granules of
+    // a row are read by consecutive lanes) and leaves, per channel, the 4
+    // codes as one 32-bit word of the channel's LDS row.
+    for (int task = threadIdx.x; task < TASKS; task += WG) {
+        const int cg = 8 * (task % GPR), tq = task / GPR;
+        float inv[8], m8[8];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int gi = threadIdx.x + i * WG;
-        if (gi >= NG) continue;
-        const int r = gi / GPR, cg = (gi % GPR) * 8;
-        const int t = chk * QBLK + r;
-        float val[8];
-        uint8_t b[8];
-        if (t < n) {
+        for (int e = 0; e < 8; ++e) {
+            const float a = amh[cg + e];
+            inv[e] = a > 0.0f ? 448.0f / a : 0.0f;
+            m8[e] = muh ? muh[cg + e] : 0.0f;
+        }
+        uint32_t word[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) word[e] = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = chk * QBLK + 4 * tq + u;
+            if (t >= n) continue;                  // tokens past the end: zero codes
+            float val[8];
             load8<DT>(v + el0 + (int64_t)t * P.vs.n + cg, val);
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                float x0 = muh ? val[e] - muh[cg + e] : val[e];
-                float x1 = muh ? val[e + 1] - muh[cg + e + 1] : val[e + 1];
-                const float a0 = amh[cg + e], a1 = amh[cg + e + 1];
-                x0 = a0 > 0.0f ? x0 * (448.0f / a0) : 0.0f;
-                x1 = a1 > 0.0f ? x1 * (448.0f / a1) : 0.0f;
-                const uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0u, false);
-                b[e] = (uint8_t)(pk & 0xff);
-                b[e + 1] = (uint8_t)((pk >> 8) & 0xff);
+                const float x0 = muh ? val[e] - m8[e] : val[e];
+                const float x1 = muh ? val[e + 1] - m8[e + 1] : val[e + 1];
+                // a zero scale gives +0 codes (never the -0 of a negative x * 0)
+                const float y0 = inv[e] > 0.0f ? x0 * inv[e] : 0.0f;
+                const float y1 = inv[e + 1] > 0.0f ? x1 * inv[e + 1] : 0.0f;
+                const uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0u, false);
+                word[e] |= (pk & 0xffu) << (8 * u);
+                word[e + 1] |= ((pk >> 8) & 0xffu) << (8 * u);
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = 0;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tr[(cg + e) * TS + r] = b[e];
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(tr + (cg + e) * TS + 4 * tq) = word[e];
     }
     __syncthreads();
     // store: channel c, 64 bytes = 4 x 16 B
     const int64_t vrow = (si.rk * P.hkv + (int64_t)h * si.npk) * D;
     for (int idx = threadIdx.x; idx < D * 4; idx += WG) {
         const int c = idx / 4, part = idx % 4;
-        const uint8_t* src = tr + c * TS + part * 16;
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            w[k] = (uint32_t)src[4 * k] | ((uint32_t)src[4 * k + 1] << 8) |
-                   ((uint32_t)src[4 * k + 2] << 16) | ((uint32_t)src[4 * k + 3] << 24);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(tr + c * TS + part * 16);
         *reinterpret_cast<uint4*>(codes + vrow + (int64_t)c * si.npk + chk * QBLK + part * 16) =
-            make_uint4(w[0], w[1], w[2], w[3]);
+            make_uint4(src[0], src[1], src[2], src[3]);
     }
 }
 
@@ -393,11 +437,18 @@ __global__ __launch_bounds__(WG) void k_quant(KParams P, QuantArgs A) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+int stat_chunks_per_wg(int d) { return WG / (d / 8); }
+
 hipError_t launch_stats(const KParams& P, int dtype, const StatJobs& J, hipStream_t st) {
     const int nb = J.j[0].nblocks + J.j[1].nblocks + J.j[2].nblocks;
     if (nb <= 0) return hipSuccess;
-    if (dtype == 0) k_stats<0><<<nb, WG, 0, st>>>(P, J);
-    else k_stats<1><<<nb, WG, 0, st>>>(P, J);
+#define SAGE_ST(DT, D) k_stats<DT, D><<<nb, WG, 0, st>>>(P, J)
+    if (dtype == 0) {
+        if (P.d == 64) SAGE_ST(0, 64); else if (P.d == 96) SAGE_ST(0, 96); else SAGE_ST(0, 128);
+    } else {
+        if (P.d == 64) SAGE_ST(1, 64); else if (P.d == 96) SAGE_ST(1, 96); else SAGE_ST(1, 128);
+    }
+#undef SAGE_ST
     return hipGetLastError();
 }
 
