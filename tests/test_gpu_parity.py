@@ -43,6 +43,11 @@ CASES = {
                          layout="HND"),
     "no_smoothing": R(W["causal_gqa"], smooth_k=False, Hq=4, Hkv=4, Nq=256, Nkv=256, seed=14),
     "custom_scale": R(W["tiny"], sm_scale=0.05, Nq=128, Nkv=384, seed=15),
+    # empty sequences: no queries (nothing to write), no keys (O = 0, LSE = -inf)
+    "varlen_empty_seqs": R(W["varlen_d128"], Hq=4, Hkv=2,
+                           seqlens_q=[5, 0, 70, 33], seqlens_kv=[0, 40, 129, 1]),
+    "varlen_empty_smooth_all": R(W["varlen_d96"], Hq=2, Hkv=2, smooth_q=True, smooth_v=True,
+                                 causal=False, seqlens_q=[0, 17, 64], seqlens_kv=[9, 0, 200]),
 }
 
 
