@@ -544,33 +544,65 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     }
     if (grp == 0) bar();   // balance group 1's leading barrier
 
-    // epilogue: lanes l and l+32 hold the same row's partial sums
+    // epilogue: lanes l and l+32 hold the same row's partial sums.  The
+    // wave's 32 output rows are assembled in LDS (rows of RS bytes, 16-byte
+    // granules XOR-swizzled by row) and then written as whole rows, 16 bytes
+    // per lane.
     const float l_tot = swap_sum(l_run);
-    if (w.q0 < nq && my_q < nq) {
+    constexpr int RS = D == 64 ? 128 : 256;    // LDS bytes per staged row
+    constexpr int NGR = RS / 16;               // granules per staged row
+    static_assert(FWD_WAVES * 32 * RS <= 2 * T::KBYTES + 2 * T::VBYTES, "staging fits the stages");
+    __syncthreads();                           // every wave is done with the tile stages
+    uint8_t* stg = smem + (threadIdx.x >> 6) * 32 * RS;
+    if (w.q0 < nq) {
         const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         const int64_t vsb = ((int64_t)si.sid * P.hkv + w.hkv) * D;
-        uint16_t* orow = o + si.o_el + (int64_t)w.head * P.os.h + (int64_t)my_q * P.os.n;
+        // all scale (and mean) loads go out before the first use
+        float4 sv[D / 32][4], mv[D / 32][4];
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                sv[c][r4] = *reinterpret_cast<const float4*>(vsc + vsb + 32 * c + 8 * r4 + 4 * h);
+        const bool add_mu = mu_v && l_tot > 0.0f;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                mv[c][r4] = add_mu ? *reinterpret_cast<const float4*>(mu_v + vsb + 32 * c + 8 * r4 + 4 * h)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        uint8_t* mine = stg + qi * RS;
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int ch0 = 32 * c + 8 * r4 + 4 * h;
-                const float4 sv = *reinterpret_cast<const float4*>(vsc + vsb + ch0);
-                float4 mv = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (mu_v && l_tot > 0.0f) mv = *reinterpret_cast<const float4*>(mu_v + vsb + ch0);
-                const float vals[4] = {acc[c][4 * r4] * sv.x * inv_l + mv.x,
-                                       acc[c][4 * r4 + 1] * sv.y * inv_l + mv.y,
-                                       acc[c][4 * r4 + 2] * sv.z * inv_l + mv.z,
-                                       acc[c][4 * r4 + 3] * sv.w * inv_l + mv.w};
+                const float4 s4 = sv[c][r4], m4 = mv[c][r4];
+                const float vals[4] = {acc[c][4 * r4] * s4.x * inv_l + m4.x,
+                                       acc[c][4 * r4 + 1] * s4.y * inv_l + m4.y,
+                                       acc[c][4 * r4 + 2] * s4.z * inv_l + m4.z,
+                                       acc[c][4 * r4 + 3] * s4.w * inv_l + m4.w};
                 uint32_t bits[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) bits[e] = f2h_bits<DT>(vals[e]);
-                *reinterpret_cast<uint2*>(orow + ch0) =
+                const int byte = 2 * ch0;              // 8-byte half of granule byte / 16
+                *reinterpret_cast<uint2*>(mine + ((((byte >> 4) ^ (qi % NGR)) << 4) | (byte & 15))) =
                     make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
             }
-        if (lse && h == 0)
+        if (lse && h == 0 && my_q < nq)
             lse[si.lse0 + (int64_t)w.head * P.lse_hstride + my_q] =
                 l_tot > 0.0f ? (m_run + __log2f(l_tot) - LOG2_448) * LN2 : -INFINITY;
+        // whole rows: D/8 granules of 16 bytes per row, 32 rows
+        uint16_t* obase = o + si.o_el + (int64_t)w.head * P.os.h;
+        constexpr int GPRW = D / 8;
+#pragma unroll
+        for (int i = 0; i < 32 * GPRW / 64; ++i) {
+            const int idx = lane + 64 * i;
+            const int row = idx / GPRW, gr = idx % GPRW;
+            const int q = w.q0 + row;
+            const uint4 val = *reinterpret_cast<const uint4*>(stg + row * RS + ((gr ^ (row % NGR)) << 4));
+            if (q < nq) *reinterpret_cast<uint4*>(obase + (int64_t)q * P.os.n + 8 * gr) = val;
+        }
     }
 }
 
