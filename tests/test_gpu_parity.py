@@ -146,3 +146,21 @@ def test_strided_inputs_match_contiguous():
     o = pu.run_fwd(w, qv, kv_, vv, meta, return_lse=False)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+
+
+def test_quantized_entry_matches_full_call(case):
+    """sage_attn_fwd_quantized on sage_quant_qkv's buffers gives the same bits
+    as the full sage_attn_fwd / sage_attn_fwd_varlen call."""
+    name, w, q, k, v, meta, prob, ref = case
+    pu.say(f"[quantized entry {name}]")
+    o_full, lse_full = pu.run_fwd(w, q, k, v, meta)
+    bufs = pu.run_quant(w, q, k, v, meta)
+    o2 = torch.zeros_like(q)
+    lse2 = torch.zeros_like(lse_full)
+    kw = {}
+    if w.varlen:
+        kw = dict(cu_seqlens_q=meta["cu_seqlens_q"], cu_seqlens_kv=meta["cu_seqlens_kv"])
+    pu.qa.sage_attn_fwd_quantized(bufs, o2, lse=lse2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o_full.view(torch.int16))
+    assert torch.equal(lse2.view(torch.int32), lse_full.view(torch.int32))
