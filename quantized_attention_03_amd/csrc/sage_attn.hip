@@ -512,9 +512,11 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
             rescale<D>(acc, alpha_prev);
             pv_tile<D>(vst0 + ((t - 1) & 1) * T::VBYTES, pb, acc);
         }
-        // the tile's score scales, loaded ahead of the softmax phase
-        const float c0 = sq * kscb[2 * t] * P.sml2;
-        const float c1 = sq * kscb[2 * t + 1] * P.sml2;
+        // the tile's score scales, loaded ahead of the softmax phase (the
+        // empty asm keeps the compiler from sinking the loads past the barrier)
+        float c0 = sq * kscb[2 * t] * P.sml2;
+        float c1 = sq * kscb[2 * t + 1] * P.sml2;
+        asm volatile("" : "+v"(c0), "+v"(c1));
         __builtin_amdgcn_s_setprio(0);
         bar();
         // ---- softmax phase ----
