@@ -37,6 +37,8 @@
 //    phase runs at raised priority.
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
+#include <cfloat>
+
 #include "sage_internal.h"
 
 namespace sage {
@@ -51,6 +53,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr float LOG2_448 = 8.807354922057604f;
 constexpr int SBIAS_I = 0x4B400000;
 constexpr float SBIAS_F = 12582912.0f;
+constexpr int NEG_INF_BITS = (int)0xFF800000u;   // -inf as a float, negative as an integer
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int FWD_WAVES = 8;               // waves per workgroup of the fused kernel
 constexpr int FWD_NT = 64 * FWD_WAVES;
@@ -322,25 +325,26 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
     float m_new;
     if constexpr (!HAS_DS) {
         if constexpr (MASK) {
+            // masked keys get the bits of -inf: as integers below every
+            // biased score, as floats they give 2^-inf = 0 below (c > 0)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    sacc[b][r] = kt0 + 32 * b + r > lim ? INT32_MIN : sacc[b][r];
+                    sacc[b][r] = kt0 + 32 * b + r > lim ? NEG_INF_BITS : sacc[b][r];
         }
         // three-input max trees (v_max3_i32), one per 64-key half
         const int mx0 = max32(sacc[0], sacc[1]), mx1 = max32(sacc[2], sacc[3]);
-        const float f0 = mx0 == INT32_MIN ? -INFINITY : (__int_as_float(mx0) - SBIAS_F) * c0;
-        const float f1 = mx1 == INT32_MIN ? -INFINITY : (__int_as_float(mx1) - SBIAS_F) * c1;
+        const float f0 = mx0 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx0) - SBIAS_F) * c0;
+        const float f1 = mx1 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx1) - SBIAS_F) * c1;
         m_new = fmaxf(m_run, swap_max(fmaxf(f0, f1)));
         const float nm = LOG2_448 - (m_new == -INFINITY ? 0.0f : m_new);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, b < 2 ? c0 : c1, nm));
-                p[b][r] = MASK ? (kt0 + 32 * b + r > lim ? 0.0f : e) : e;
-            }
+            for (int r = 0; r < 16; ++r)
+                p[b][r] = __builtin_amdgcn_exp2f(
+                    fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, b < 2 ? c0 : c1, nm));
     } else {
         float mt = -INFINITY;
 #pragma unroll
@@ -379,7 +383,11 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
 #pragma unroll
         for (int wd = 0; wd < 8; ++wd) {
             const int b = 2 * kh + wd / 4, r0 = 4 * (wd % 4);
-            uint32_t u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0], p[b][r0 + 1], 0u, false);
+            // the first convert fills the low half of the word and the second
+            // the high half, so the word's prior contents do not matter: it is
+            // seeded with a value that dies here (no zeroing move)
+            uint32_t u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0], p[b][r0 + 1],
+                                                         __float_as_uint(p[b][r0]), false);
             u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0 + 2], p[b][r0 + 3], u, true);
             pb[kh][wd] = (int)u;
         }
@@ -514,8 +522,11 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         }
         // the tile's score scales, loaded ahead of the softmax phase (the
         // empty asm keeps the compiler from sinking the loads past the barrier)
-        float c0 = sq * kscb[2 * t] * P.sml2;
-        float c1 = sq * kscb[2 * t + 1] * P.sml2;
+        // (a zero scale -- an all-zero block -- is raised to the smallest
+        // normal float, which leaves every score unchanged after rounding and
+        // keeps a masked key's -inf * c at -inf)
+        float c0 = fmaxf(sq * kscb[2 * t] * P.sml2, FLT_MIN);
+        float c1 = fmaxf(sq * kscb[2 * t + 1] * P.sml2, FLT_MIN);
         asm volatile("" : "+v"(c0), "+v"(c1));
         __builtin_amdgcn_s_setprio(0);
         bar();
