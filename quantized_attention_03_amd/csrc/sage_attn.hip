@@ -346,24 +346,27 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
                 p[b][r] = __builtin_amdgcn_exp2f(
                     fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, b < 2 ? c0 : c1, nm));
     } else {
+        // here c0, c1 leave out sm_scale*log2(e): y = S*sq*sk + dS is formed
+        // first (its maximum taken), and the base-2 factor is applied inside
+        // the exponent's FMA
         float mt = -INFINITY;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float c = b < 2 ? c0 : c1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, c, dsl[32 * b + 16 * h + r] * sml2);
-                if (MASK) x = kt0 + 32 * b + r > lim ? -INFINITY : x;
-                p[b][r] = x;
-                mt = fmaxf(mt, x);
+                float y = fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, c, dsl[32 * b + 16 * h + r]);
+                if (MASK) y = kt0 + 32 * b + r > lim ? -INFINITY : y;
+                p[b][r] = y;
+                mt = fmaxf(mt, y);
             }
         }
-        m_new = fmaxf(m_run, swap_max(mt));
+        m_new = fmaxf(m_run, swap_max(mt) * sml2);
         const float nm = LOG2_448 - (m_new == -INFINITY ? 0.0f : m_new);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) p[b][r] = __builtin_amdgcn_exp2f(p[b][r] + nm);
+            for (int r = 0; r < 16; ++r) p[b][r] = __builtin_amdgcn_exp2f(fmaf(p[b][r], sml2, nm));
     }
     const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -525,8 +528,8 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         // (a zero scale -- an all-zero block -- is raised to the smallest
         // normal float, which leaves every score unchanged after rounding and
         // keeps a masked key's -inf * c at -inf)
-        float c0 = fmaxf(sq * kscb[2 * t] * P.sml2, FLT_MIN);
-        float c1 = fmaxf(sq * kscb[2 * t + 1] * P.sml2, FLT_MIN);
+        float c0 = fmaxf(HAS_DS ? sq * kscb[2 * t] : sq * kscb[2 * t] * P.sml2, FLT_MIN);
+        float c1 = fmaxf(HAS_DS ? sq * kscb[2 * t + 1] : sq * kscb[2 * t + 1] * P.sml2, FLT_MIN);
         asm volatile("" : "+v"(c0), "+v"(c1));
         __builtin_amdgcn_s_setprio(0);
         bar();
