@@ -68,6 +68,8 @@ def lib():
         "orc_qk_int32": (None, [P, P, i64, i64, i32, P]),
         "orc_attn_recipe_rows": (None, [P, P, P, P, P, P, P, P, i64, i64, i32, f32,
                                         i32, i32, i32, P, i64, P, P]),
+        "orc_attn_recipe_half_rows": (None, [P, P, P, P, P, i32, P, P, i64, i64, i32, f32,
+                                             i32, i32, i32, P, i64, P, P]),
         "orc_attn_exact_rows": (None, [P, P, P, i64, i64, i32, f64, i32, P, i64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -185,6 +187,23 @@ def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, ro
     return out, lse
 
 
+def attn_recipe_half_rows(qc, qs, kc, ks, vh, dtype, ds, mu_v, sm_scale, causal, bkv, rows):
+    """The 16-bit P.V variant: vh [nkv, d] fp16/bf16 bit patterns of the V
+    operand; p^ is p rounded to the same type."""
+    qc, kc, vh = _c(qc, np.int8), _c(kc, np.int8), _c(vh, np.uint16)
+    nq, d = qc.shape
+    nkv = kc.shape[0]
+    rows = _c(rows, np.int64)
+    out = np.empty((rows.size, d), np.float32)
+    lse = np.empty(rows.size, np.float32)
+    lib().orc_attn_recipe_half_rows(
+        _p(qc), _p(_c(qs, np.float32)), _p(kc), _p(_c(ks, np.float32)), _p(vh),
+        1 if dtype == "bf16" else 0, _p(None if ds is None else _c(ds, np.float32)),
+        _p(None if mu_v is None else _c(mu_v, np.float32)), nq, nkv, d,
+        float(sm_scale), int(causal), int(bkv), BLK, _p(rows), rows.size, _p(out), _p(lse))
+    return out, lse
+
+
 def attn_exact_rows(q, k, v, sm_scale, causal, rows):
     q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
     nq, d = q.shape
@@ -214,15 +233,16 @@ class Problem:
     smooth_k: bool = True
     smooth_v: bool = False
     sm_scale: float | None = None
+    pv_mode: str = "fp8"        # "fp8" (SageAttention2) | "half" (16-bit P.V)
 
     @property
     def scale(self) -> float:
         return self.sm_scale if self.sm_scale else 1.0 / math.sqrt(self.d)
 
 
-def problem_from_workload(w) -> Problem:
+def problem_from_workload(w, pv_mode: str = "fp8") -> Problem:
     return Problem(w.dtype, w.layout, w.Hq, w.Hkv, w.d, w.seq_lens(), w.varlen, w.causal,
-                   w.smooth_q, w.smooth_k, w.smooth_v, w.sm_scale)
+                   w.smooth_q, w.smooth_k, w.smooth_v, w.sm_scale, pv_mode)
 
 
 def split_heads(prob: Problem, x, which: str):
@@ -264,8 +284,9 @@ class Prepass:
     qs: list = field(default_factory=list)       # [Hq, ceil(nq/64)] FP32
     kc: list = field(default_factory=list)       # [Hkv, nkv, d] int8
     ks: list = field(default_factory=list)       # [Hkv, ceil(nkv/64)] FP32
-    vc: list = field(default_factory=list)       # [Hkv, nkv, d] e4m3 bytes
-    vs: list = field(default_factory=list)       # [Hkv, d] FP32
+    vc: list = field(default_factory=list)       # [Hkv, nkv, d] e4m3 bytes, or
+                                                 # 16-bit patterns (pv_mode "half")
+    vs: list = field(default_factory=list)       # [Hkv, d] FP32 (None for "half")
     ds: list = field(default_factory=list)       # [Hq, nkv] FP32 or None
 
 
@@ -283,7 +304,11 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
         mu_v = channel_mean(vf) if prob.smooth_v else None
         k_s = smooth(kf, mu_k)
         kc, ks = quant_int8_blocks(k_s)
-        vc, vs = quant_fp8_channels(smooth(vf, mu_v))
+        if prob.pv_mode == "half":
+            # the V operand stays 16-bit: v (or v - mu_v rounded to the type)
+            vc, vs = encode16(smooth(vf, mu_v), prob.dtype), None
+        else:
+            vc, vs = quant_fp8_channels(smooth(vf, mu_v))
         return mu_k, mu_v, k_s, kc, ks, vc, vs
 
     def q_unit(u, k_s):
@@ -307,7 +332,7 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
         R.kc.append(np.stack([x[3] for x in ks_]))
         R.ks.append(np.stack([x[4] for x in ks_]))
         R.vc.append(np.stack([x[5] for x in ks_]))
-        R.vs.append(np.stack([x[6] for x in ks_]))
+        R.vs.append(np.stack([x[6] for x in ks_]) if prob.pv_mode != "half" else None)
         R.mu_q.append(np.stack([x[0] for x in qs_]) if prob.smooth_q else None)
         R.qc.append(np.stack([x[1] for x in qs_]))
         R.qs.append(np.stack([x[2] for x in qs_]))
@@ -328,10 +353,14 @@ def forward_rows(prob: Problem, pre: Prepass, rows=None, bkv: int = 128,
         nq = prob.seqs[s][0]
         r = np.arange(nq) if rows is None else np.asarray(rows[s])
         hk = h // G
+        ds = None if pre.ds[s] is None else pre.ds[s][h]
+        mu_v = None if pre.mu_v[s] is None else pre.mu_v[s][hk]
+        if prob.pv_mode == "half":
+            return attn_recipe_half_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk],
+                                         pre.ks[s][hk], pre.vc[s][hk], prob.dtype, ds, mu_v,
+                                         prob.scale, prob.causal, bkv, r)
         return attn_recipe_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk], pre.ks[s][hk],
-                                pre.vc[s][hk], pre.vs[s][hk],
-                                None if pre.ds[s] is None else pre.ds[s][h],
-                                None if pre.mu_v[s] is None else pre.mu_v[s][hk],
+                                pre.vc[s][hk], pre.vs[s][hk], ds, mu_v,
                                 prob.scale, prob.causal, bkv, r)
 
     with ThreadPoolExecutor(max_workers=threads or os.cpu_count()) as ex:

@@ -1,6 +1,7 @@
 /*
  * sage_oracle.c -- plain, slow, scalar CPU oracle for the SageAttention /
- * SageAttention2 quantized attention forward pass (INT8 Q.K^T, FP8 P.V).
+ * SageAttention2 quantized attention forward pass (INT8 Q.K^T; FP8 P.V, or
+ * 16-bit P.V in the first SageAttention's variant).
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the independent checker of the HIP
  * library: only the tests, the smoke check and the CPU-baseline leg of the
@@ -22,6 +23,9 @@
  *          before quantization; item 3: the INT8+FP8 precision branch.
  *  [SA1]   SA1 abstract (llama.cpp discussion #9901): attention is O(N^2) and
  *          the method quantizes attention itself.
+ *  [GUIDE] "SageAttention量化加速框架" install guide, section 3.1 (benchmark
+ *          scripts): the qk_int8_pv_fp16 kernel, INT8 Q.K^T with a 16-bit
+ *          P.V; [PKG] "What it is and what it does": FP16 accumulators.
  *
  * Every step below follows the plainest reading of those pages; where they
  * are silent the comment says which choice is taken.  Floating point: the
@@ -279,30 +283,36 @@ static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
 /* Same-recipe forward for selected query rows of one (sequence, q-head).
  *   qc, q_scale : int8 codes [nq][d], FP32 scale per 64-token block
  *   kc, k_scale : int8 codes [nkv][d], FP32 scale per 64-token block
- *   vc, v_scale : e4m3 codes [nkv][d] (logical row-major), FP32 scale per channel
+ *   vdec        : the decoded V operand [nkv][d] (exact in FP32)
+ *   out_scale   : FP32 [d] factor applied to acc at the end, or NULL (1)
+ *   p_mode      : how p becomes the P.V operand (P_FP8 or P_F16 / P_BF16)
  *   delta_s     : FP32 [nkv] Q-smoothing compensation, or NULL
  *   mu_v        : FP32 [d] V mean to add back at the output, or NULL
  *   bkv         : key-tile width of the online softmax (p^ depends on it)
  *   rows[nrows] : query rows to compute; out [nrows][d] FP32, lse [nrows]
  * Steps: s = fl32(S)*(sq*sk*sm_scale) (+ ds_j*sm_scale); for each key tile in
  * order: m' = max(m, max s), alpha = e^(m-m'), p = e^(s-m') (FP32),
- * l = alpha*l + sum p (from the FP32 p), p^ = e4m3(p*448) (static scale 448),
- * acc = alpha*acc + sum p^ * v^; finally o = acc*(v_scale/448)/l (+ mu_v).
+ * l = alpha*l + sum p (from the FP32 p), p^ = the P.V operand made from p,
+ * acc = alpha*acc + sum p^ * v; finally o = acc*out_scale/l (+ mu_v).
  * A row that sees no key gives o = 0 and lse = -inf.  LSE is the
  * natural log of sum_j e^(s_j) over the scores as the recipe forms them. */
-ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
-                                     const int8_t* kc, const float* k_scale,
-                                     const uint8_t* vc, const float* v_scale,
-                                     const float* delta_s, const float* mu_v,
-                                     int64_t nq, int64_t nkv, int d, float sm_scale,
-                                     int causal, int bkv, int blk,
-                                     const int64_t* rows, int64_t nrows,
-                                     float* out, float* lse) {
+enum { P_FP8 = 0, P_F16 = 1, P_BF16 = 2 };
+
+static float p_operand(float p, int p_mode) {
+    switch (p_mode) {
+    case P_FP8: return orc_e4m3_decode(orc_e4m3_encode_sat(p * 448.0f));
+    case P_F16: return orc_f16_decode(orc_f16_encode(p));
+    default:    return orc_bf16_decode(orc_bf16_encode(p));
+    }
+}
+
+static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc,
+                        const float* k_scale, const float* vdec, const float* out_scale,
+                        int p_mode, const float* delta_s, const float* mu_v, int64_t nq,
+                        int64_t nkv, int d, float sm_scale, int causal, int bkv, int blk,
+                        const int64_t* rows, int64_t nrows, float* out, float* lse) {
     float* s = (float*)malloc(sizeof(float) * (size_t)(bkv > 0 ? bkv : 1));
     float* acc = (float*)malloc(sizeof(float) * (size_t)d);
-    /* decode every V code once; dec(v^) is exact in FP32 */
-    float* vdec = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1) * (size_t)d);
-    for (int64_t j = 0; j < nkv * d; ++j) vdec[j] = orc_e4m3_decode(vc[j]);
     for (int64_t r = 0; r < nrows; ++r) {
         int64_t i = rows[r];
         int64_t jmax = last_visible(i, nq, nkv, causal);
@@ -330,7 +340,7 @@ ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
             for (int64_t jj = 0; jj < nt; ++jj) {
                 float p = (float)exp((double)(s[jj] - mn));
                 psum = psum + p;
-                float ph = orc_e4m3_decode(orc_e4m3_encode_sat(p * 448.0f));
+                float ph = p_operand(p, p_mode);
                 if (ph == 0.0f) continue;     /* a zero product leaves acc as is */
                 const float* vrow = vdec + (t0 + jj) * d;
                 for (int c = 0; c < d; ++c) acc[c] = acc[c] + ph * vrow[c];
@@ -345,7 +355,7 @@ ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
             continue;
         }
         for (int c = 0; c < d; ++c) {
-            float val = acc[c] * (v_scale[c] / 448.0f) / l;
+            float val = (out_scale ? acc[c] * out_scale[c] : acc[c]) / l;
             if (mu_v) val = val + mu_v[c];
             o[c] = val;
         }
@@ -353,6 +363,51 @@ ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
     }
     free(s);
     free(acc);
+}
+
+/* The INT8-QK / FP8-PV recipe ([BLOG] item 2, [SA2] item 3):
+ *   vc, v_scale : e4m3 codes [nkv][d] (logical row-major), FP32 scale per
+ *                 channel; p^ = e4m3(p*448) (static scale 448), and the end
+ *                 factor is v_scale/448. */
+ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
+                                     const int8_t* kc, const float* k_scale,
+                                     const uint8_t* vc, const float* v_scale,
+                                     const float* delta_s, const float* mu_v,
+                                     int64_t nq, int64_t nkv, int d, float sm_scale,
+                                     int causal, int bkv, int blk,
+                                     const int64_t* rows, int64_t nrows,
+                                     float* out, float* lse) {
+    /* decode every V code once; dec(v^) is exact in FP32 */
+    float* vdec = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1) * (size_t)d);
+    float* fac = (float*)malloc(sizeof(float) * (size_t)d);
+    for (int64_t j = 0; j < nkv * d; ++j) vdec[j] = orc_e4m3_decode(vc[j]);
+    for (int c = 0; c < d; ++c) fac[c] = v_scale[c] / 448.0f;
+    recipe_rows(qc, q_scale, kc, k_scale, vdec, fac, P_FP8, delta_s, mu_v, nq, nkv, d, sm_scale,
+                causal, bkv, blk, rows, nrows, out, lse);
+    free(vdec);
+    free(fac);
+}
+
+/* The INT8-QK / 16-bit-PV recipe of the first SageAttention (package page
+ * "What it is and what it does": FP16 accumulators; the install guide's
+ * benchmark section names the qk_int8_pv_fp16 kernel):
+ *   vh   : V operand [nkv][d] as fp16 (bf16 = 0) or bf16 (bf16 = 1) bit
+ *          patterns (the input V, or v - mu_v rounded to that type);
+ *   p^ = p rounded to the same 16-bit type (no scale: p <= 1), and no end
+ *   factor. */
+ORC_EXPORT void orc_attn_recipe_half_rows(const int8_t* qc, const float* q_scale,
+                                          const int8_t* kc, const float* k_scale,
+                                          const uint16_t* vh, int bf16,
+                                          const float* delta_s, const float* mu_v,
+                                          int64_t nq, int64_t nkv, int d, float sm_scale,
+                                          int causal, int bkv, int blk,
+                                          const int64_t* rows, int64_t nrows,
+                                          float* out, float* lse) {
+    float* vdec = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1) * (size_t)d);
+    for (int64_t j = 0; j < nkv * d; ++j)
+        vdec[j] = bf16 ? orc_bf16_decode(vh[j]) : orc_f16_decode(vh[j]);
+    recipe_rows(qc, q_scale, kc, k_scale, vdec, NULL, bf16 ? P_BF16 : P_F16, delta_s, mu_v, nq,
+                nkv, d, sm_scale, causal, bkv, blk, rows, nrows, out, lse);
     free(vdec);
 }
 

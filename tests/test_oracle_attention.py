@@ -7,7 +7,12 @@
 * the same-recipe forward on textbook special cases (one key, uniform weights,
   a dominant key, rows with no visible key), against exact FP64 attention on
   tiny inputs of every head dim, its LSE, and its independence of the tile
-  width up to FP8 rounding.
+  width up to FP8 rounding;
+* the 16-bit P.V variant (pv_mode "half"): one key gives v exactly, uniform
+  weights give the plain mean of V, one tile equals the textbook softmax with
+  p rounded by numpy's float16 / torch's bfloat16 conversion (library
+  routines), its V operand is the input (or v - mu_v rounded by numpy), and it
+  is closer to exact attention than the FP8 recipe.
 """
 import math
 
@@ -224,3 +229,117 @@ def test_dequantized_score_bound(orc):
     bound = (np.abs(q) @ np.ones((d, n))) * sk[None, :] / 2 \
         + (np.ones((n, d)) @ np.abs(ks).T) * sq[:, None] / 2 + d * sq[:, None] * sk[None, :] / 4
     assert np.all(np.abs(s - t) <= bound * (1 + 1e-6))
+
+
+# ------------------------------------------------- 16-bit P.V variant ---
+
+def _bf16(x):
+    t = torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _enc(x, dtype):
+    return _f16(x) if dtype == "f16" else _bf16(x)
+
+
+def _round_p(p, dtype):
+    """p rounded to the 16-bit type by the libraries' own conversions."""
+    if dtype == "f16":
+        return np.asarray(p, np.float32).astype(np.float16).astype(np.float64)
+    return torch.from_numpy(np.asarray(p, np.float32)).to(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_half_one_key_returns_v(orc, dtype):
+    rng = np.random.default_rng(21)
+    d = 96
+    q = _enc(rng.normal(0, 1, (1, 1, 7, d)), dtype)
+    k = _enc(rng.normal(0, 1, (1, 1, 1, d)), dtype)
+    v = _enc(rng.normal(0, 1, (1, 1, 1, d)), dtype)
+    vf = orc.decode16(v, dtype)[0, 0, 0]
+    for smooth_v in (False, True):
+        prob = orc.Problem(dtype, "HND", 1, 1, d, [(7, 1)], smooth_v=smooth_v, pv_mode="half")
+        pre = orc.prepass(prob, q, k, v)
+        out, _ = orc.forward_rows(prob, pre)
+        # p = 1 is exact in 16 bits and l = 1: o = v with no rounding at all
+        assert np.array_equal(out[0][0], np.broadcast_to(vf, (7, d)))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_half_uniform_weights(orc, dtype):
+    rng = np.random.default_rng(22)
+    d, n = 64, 200
+    v = _enc(rng.normal(0, 1, (1, 1, n, d)), dtype)
+    k = _enc(np.broadcast_to(rng.normal(0, 1, (1, 1, 1, d)), (1, 1, n, d)), dtype)
+    q = _enc(rng.normal(0, 1, (1, 1, n, d)), dtype)
+    vf = orc.decode16(v, dtype)[0, 0].astype(np.float64)
+    for causal in (False, True):
+        prob = orc.Problem(dtype, "HND", 1, 1, d, [(n, n)], causal=causal, pv_mode="half")
+        out, _ = orc.forward_rows(prob, orc.prepass(prob, q, k, v))
+        for i in (0, 1, 127, 128, 199):
+            m = (i + 1) if causal else n
+            # every p is exactly 1: o is the plain mean of the visible rows
+            assert np.max(np.abs(out[0][0][i] - vf[:m].mean(0))) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("smooth_q", [False, True])
+def test_half_one_tile_is_textbook_softmax(orc, dtype, smooth_q):
+    """With one key tile the online softmax is the plain one: o = sum_j
+    r(p_j) v_j / sum_j p_j, p_j = e^(s_j - max s) (difference in FP32, as the
+    recipe forms it), where r is the 16-bit
+    rounding done here by numpy / torch.  Dropping the rounding, rounding to
+    the other type or normalising by sum r(p) all miss the 1e-6 bar."""
+    rng = np.random.default_rng(23 + smooth_q)
+    d, nq, nkv = 64, 9, 100
+    q = _enc(rng.normal(0, 1, (1, 1, nq, d)) + (1.0 if smooth_q else 0.0), dtype)
+    k = _enc(rng.normal(0, 1, (1, 1, nkv, d)), dtype)
+    v = _enc(rng.normal(0, 1, (1, 1, nkv, d)), dtype)
+    prob = orc.Problem(dtype, "HND", 1, 1, d, [(nq, nkv)], smooth_q=smooth_q, pv_mode="half")
+    pre = orc.prepass(prob, q, k, v)
+    out, _ = orc.forward_rows(prob, pre, bkv=128)
+    S = orc.qk_int32(pre.qc[0][0], pre.kc[0][0]).astype(np.float64)
+    sq = np.repeat(pre.qs[0][0], 64)[:nq]
+    sk = np.repeat(pre.ks[0][0], 64)[:nkv]
+    vf = orc.decode16(v, dtype)[0, 0].astype(np.float64)
+    for i in range(nq):
+        comb = np.float32(np.float32(sq[i]) * sk) * np.float32(prob.scale)
+        s = (np.float32(S[i]) * comb).astype(np.float32)
+        if smooth_q:
+            s = (s + (pre.ds[0][0] * np.float32(prob.scale)).astype(np.float32)).astype(np.float32)
+        p = np.exp((s - s.max()).astype(np.float64)).astype(np.float32)   # s - m in FP32
+        want = (_round_p(p, dtype) @ vf) / p.astype(np.float64).sum()
+        assert np.max(np.abs(out[0][0][i] - want)) < 1e-6 * max(1.0, np.abs(want).max())
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_half_v_operand(orc, dtype):
+    rng = np.random.default_rng(24)
+    d, n = 128, 70
+    q, k = (_enc(rng.normal(0, 1, (1, 1, n, d)), dtype) for _ in range(2))
+    v = _enc(rng.normal(0, 1, (1, 1, n, d)) + rng.normal(0, 2, (1, 1, 1, d)), dtype)
+    prob = orc.Problem(dtype, "HND", 1, 1, d, [(n, n)], pv_mode="half")
+    pre = orc.prepass(prob, q, k, v)
+    assert pre.vs[0] is None and np.array_equal(pre.vc[0][0], v[0, 0])
+    prob = orc.Problem(dtype, "HND", 1, 1, d, [(n, n)], smooth_v=True, pv_mode="half")
+    pre = orc.prepass(prob, q, k, v)
+    vf = orc.decode16(v, dtype)[0, 0]
+    vs = (vf - pre.mu_v[0][0]).astype(np.float32)       # FP32 difference
+    assert np.array_equal(pre.vc[0][0], _enc(vs, dtype))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_half_closer_to_exact_than_fp8(orc, d):
+    rng = np.random.default_rng(25 + d)
+    nq, nkv = 70, 300
+    q = _f16(rng.normal(0, 1, (1, 2, nq, d)))
+    k = _f16(rng.normal(0, 1, (1, 1, nkv, d)) + rng.normal(0, 3, (1, 1, 1, d)))
+    v = _f16(rng.normal(0, 1, (1, 1, nkv, d)))
+    errs = {}
+    for mode in ("fp8", "half"):
+        prob = orc.Problem("f16", "HND", 2, 1, d, [(nq, nkv)], causal=True, pv_mode=mode)
+        out, _ = orc.forward_rows(prob, orc.prepass(prob, q, k, v))
+        ex, _ = orc.exact_rows(prob, q, k, v)
+        errs[mode] = float(np.abs(out[0] - ex[0]).max())
+        assert _cos(out[0], ex[0]) >= (0.9999 if mode == "half" else 0.999)
+    assert errs["half"] < 0.5 * errs["fp8"]
