@@ -30,6 +30,15 @@
  *   s_ij      = (qc_i . kc_j) * sq * sk * sm_scale (+ ds[j] * sm_scale);
  *   online softmax over 128-key tiles with p^ = e4m3(448 * e^(s - m)),
  *   l summed from the FP32 p, o = sum p^ v^ * (v_scale/448) / l (+ mu_v).
+ *
+ * The 16-bit P.V variant (pv_mode = SAGE_PV_HALF), the first SageAttention's
+ * INT8-QK / 16-bit-PV kernel (install guide "SageAttention量化加速框架",
+ * section 3.1, the qk_int8_pv_fp16 benchmark; package page "What it is and
+ * what it does": FP16 accumulators), changes only the P.V operands:
+ *   V         : kept in the input's 16-bit type (v, or v - mu_v rounded to
+ *               nearest even into that type), no scale;
+ *   p^        = e^(s - m) rounded to nearest even into the same type,
+ *   o = sum p^ v / l (+ mu_v), accumulated in FP32 (the MFMA's accumulator).
  *   Causal masking is aligned bottom-right: row i sees keys j <= i + Nkv - Nq;
  *   a row that sees no key gives o = 0 and lse = -inf.
  *
@@ -55,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 1
+#define SAGE_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SAGE_API __attribute__((visibility("default")))
@@ -86,6 +95,10 @@ typedef enum {
 
 typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1 } sage_dtype;
 
+/* Operands of P.V: E4M3 P^ and V^ (SageAttention2, the default) or P^ and V
+ * in the input's 16-bit type (the first SageAttention's variant). */
+typedef enum { SAGE_PV_FP8 = 0, SAGE_PV_HALF = 1 } sage_pv_mode;
+
 /* HND = [batch, heads, tokens, head_dim]; NHD = [batch, tokens, heads, head_dim].
  * Variable-length inputs are packed over the sequences: NHD = [tokens, heads,
  * head_dim], HND = [heads, tokens, head_dim]. */
@@ -111,7 +124,8 @@ typedef struct {
     int32_t smooth_k;        /* 0/1 (default 1)                                   */
     int32_t smooth_v;        /* 0/1 (SA2-style V smoothing, mean added back)     */
     float sm_scale;          /* <= 0 selects 1/sqrt(head_dim)                     */
-    int32_t reserved[3];     /* must be zero                                      */
+    int32_t pv_mode;         /* sage_pv_mode (default SAGE_PV_FP8)                */
+    int32_t reserved[2];     /* must be zero                                      */
 } sage_attn_desc;
 
 /* Fill `desc` for a dense, contiguous problem with the API defaults
@@ -133,8 +147,10 @@ SAGE_API void sage_desc_init(sage_attn_desc* desc, int32_t dtype, int32_t layout
  *   k_codes int8: (s,h,n,c) at ((rk_s*hkv + h*npk_s + n)*d + c), pad rows zero
  *   k_scale FP32: (s,h,blk) at (rk_s*hkv + h*npk_s)/64 + blk (pad blocks 0)
  *   v_codes OCP E4M3 bytes, channel-major: (s,h,n,c) at
- *           ((rk_s*hkv + h*npk_s)*d + c*npk_s + n), pad tokens zero
- *   v_scale FP32 [S][hkv][d]
+ *           ((rk_s*hkv + h*npk_s)*d + c*npk_s + n), pad tokens zero;
+ *           with SAGE_PV_HALF the same index counts 16-bit elements of the
+ *           input's type (v, or v - mu_v rounded into that type)
+ *   v_scale FP32 [S][hkv][d] (unused with SAGE_PV_HALF: size 0, may be NULL)
  *   delta_s FP32: (s,h,n) at rk_s*hq + h*npk_s + n, only if smooth_q
  * All pointers 16-byte aligned.
  */
@@ -171,8 +187,9 @@ SAGE_API sage_status sage_workspace_size(const sage_attn_desc* desc, const int32
 
 /*
  * sage_quant_qkv -- the pre-pass alone: channel means, smoothing, INT8 Q/K
- * per-block codes and scales, E4M3 V codes and per-channel scales, and the
- * Q-smoothing score bias, written to `out` in the layout above.  Dense when
+ * per-block codes and scales, E4M3 V codes and per-channel scales (or the
+ * 16-bit V operand with SAGE_PV_HALF), and the Q-smoothing score bias,
+ * written to `out` in the layout above.  Dense when
  * cu_seqlens_q == NULL; otherwise varlen with host cu_seqlens_q/kv
  * (nseq + 1 int32 prefix offsets starting at 0, non-decreasing) and packed
  * q/k/v.  Sources: package page "What it is and what it does" (smoothing,
@@ -188,7 +205,7 @@ SAGE_API sage_status sage_quant_qkv(const sage_attn_desc* desc, const void* q, c
 
 /*
  * sage_attn_fwd -- full forward pass for dense inputs: pre-pass, then the
- * fused INT8-QK / online-softmax / FP8-PV kernel.  q [B,hq,nq,d] (HND) or
+ * fused INT8-QK / online-softmax / FP8-PV (or 16-bit-PV) kernel.  q [B,hq,nq,d] (HND) or
  * [B,nq,hq,d] (NHD) with the descriptor's strides; k, v likewise with hkv,
  * nkv; o has q's shape.  lse (nullable) receives FP32 [B][hq][nq], the natural
  * log of sum_j e^(s_ij) over the scores as formed above (after smoothing).

@@ -8,6 +8,9 @@ raises (there is no CPU or eager fallback).
     o = sageattn(q, k, v, tensor_layout="HND", is_causal=False, smooth_k=True)
 
 mirrors the `sageattn` call of the "sageattention" package page (Quickstart).
+Every entry point takes pv_mode="fp8" (E4M3 P and V, SageAttention2; the
+default) or pv_mode="half" (P and V in the input's 16-bit type, the first
+SageAttention's INT8-QK / 16-bit-PV kernel).
 """
 from __future__ import annotations
 
@@ -41,13 +44,16 @@ def _strides(t: torch.Tensor, layout: str, varlen: bool):
 
 
 def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q=False,
-              smooth_k=True, smooth_v=False, sm_scale=None, varlen=False) -> _abi.Desc:
+              smooth_k=True, smooth_v=False, sm_scale=None, varlen=False,
+              pv_mode="fp8") -> _abi.Desc:
     """Descriptor for q/k/v torch tensors (dense [B,H,N,d] / [B,N,H,d], or packed
     varlen [T,H,d] / [H,T,d])."""
     if tensor_layout not in ("HND", "NHD"):
         raise ValueError(f"tensor_layout must be 'HND' or 'NHD', got {tensor_layout!r}")
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    if pv_mode not in _abi.PV_MODES:
+        raise ValueError(f"pv_mode must be 'fp8' or 'half', got {pv_mode!r}")
     d = _abi.Desc()
     lay = NHD if tensor_layout == "NHD" else HND
     hd = q.shape[-1]
@@ -71,6 +77,7 @@ def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q
     d.smooth_k = int(bool(smooth_k))
     d.smooth_v = int(bool(smooth_v))
     d.sm_scale = float(sm_scale) if sm_scale else 0.0
+    d.pv_mode = _abi.PV_MODES[pv_mode]
     return d
 
 
@@ -116,7 +123,7 @@ _BUF_DT = {"mu_q": torch.float32, "mu_k": torch.float32, "mu_v": torch.float32,
 
 def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
                    smooth_k=True, smooth_v=False, sm_scale=None, cu_seqlens_q=None,
-                   cu_seqlens_kv=None, bufs=None):
+                   cu_seqlens_kv=None, bufs=None, pv_mode="fp8"):
     """Run the pre-pass alone; returns a dict of flat device tensors laid out as
     documented for sage_quant_bufs in include/sage.h.  Passing the dict of an
     earlier call on the same problem as `bufs` reuses its buffers and
@@ -124,7 +131,7 @@ def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=Fa
     varlen = cu_seqlens_q is not None
     desc = make_desc(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                     sm_scale=sm_scale, varlen=varlen)
+                     sm_scale=sm_scale, varlen=varlen, pv_mode=pv_mode)
     if bufs is None:
         sizes = quant_buf_sizes(desc, cu_seqlens_q, cu_seqlens_kv)
         bufs = {name: torch.zeros(max(1, nbytes // torch.empty((), dtype=_BUF_DT[name]).element_size()),
@@ -189,12 +196,12 @@ def sage_debug_qk_int32(bufs, *, cu_seqlens_q=None, cu_seqlens_kv=None, device=N
 
 def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
                   smooth_k=True, smooth_v=False, sm_scale=None, return_lse=False,
-                  out=None, workspace=None):
+                  out=None, workspace=None, pv_mode="fp8"):
     """Dense forward pass.  Returns o (and lse [B, hq, nq] FP32 if asked)."""
     o = torch.empty_like(q) if out is None else out
     desc = make_desc(q, k, v, o, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                     sm_scale=sm_scale)
+                     sm_scale=sm_scale, pv_mode=pv_mode)
     lse = None
     if return_lse:
         lse = torch.empty((desc.batch, desc.hq, desc.nq), dtype=torch.float32, device=q.device)
@@ -209,13 +216,14 @@ def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=Fal
 
 def sage_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, tensor_layout="NHD",
                          is_causal=False, smooth_q=False, smooth_k=True, smooth_v=False,
-                         sm_scale=None, return_lse=False, out=None, workspace=None):
+                         sm_scale=None, return_lse=False, out=None, workspace=None,
+                         pv_mode="fp8"):
     """Packed variable-length forward pass (q [T,H,d] for NHD or [H,T,d] for
     HND; cu_seqlens are host int32 prefix offsets).  lse is [hq, T_q]."""
     o = torch.empty_like(q) if out is None else out
     desc = make_desc(q, k, v, o, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                     sm_scale=sm_scale, varlen=True)
+                     sm_scale=sm_scale, varlen=True, pv_mode=pv_mode)
     cq, n = _cu(cu_seqlens_q)
     ck, nk = _cu(cu_seqlens_kv)
     if nk != n:
@@ -235,8 +243,8 @@ def sage_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, tensor_layout=
 
 
 def sageattn(q, k, v, tensor_layout="HND", is_causal=False, smooth_k=True, sm_scale=None,
-             smooth_q=False, smooth_v=False, return_lse=False):
+             smooth_q=False, smooth_v=False, return_lse=False, pv_mode="fp8"):
     """The package page's call: attention output of the quantized forward pass."""
     return sage_attn_fwd(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal,
                          smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                         sm_scale=sm_scale, return_lse=return_lse)
+                         sm_scale=sm_scale, return_lse=return_lse, pv_mode=pv_mode)

@@ -15,6 +15,8 @@ STATUS_NAMES = {
     12: "SAGE_ERR_HIP", 13: "SAGE_ERR_FLAGS",
 }
 F16, BF16 = 0, 1
+PV_FP8, PV_HALF = 0, 1
+PV_MODES = {"fp8": PV_FP8, "half": PV_HALF}
 HND, NHD = 0, 1
 QK_BLOCK, KV_TILE = 64, 128
 
@@ -33,7 +35,8 @@ class Desc(ctypes.Structure):
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
         ("is_causal", ctypes.c_int32), ("smooth_q", ctypes.c_int32),
         ("smooth_k", ctypes.c_int32), ("smooth_v", ctypes.c_int32),
-        ("sm_scale", ctypes.c_float), ("reserved", ctypes.c_int32 * 3),
+        ("sm_scale", ctypes.c_float), ("pv_mode", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 

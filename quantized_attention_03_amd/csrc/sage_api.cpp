@@ -30,6 +30,7 @@ struct Plan {
     Strides qs{}, ks{}, vs{}, os{};
     float sm_scale = 0.0f;
     bool causal = false, smooth_q = false, smooth_k = false, smooth_v = false;
+    bool pv_half = false;             // 16-bit P.V operands (SAGE_PV_HALF)
 };
 
 // Byte offsets of everything placed in a workspace (quantized tensors first,
@@ -51,8 +52,8 @@ sage_quant_sizes quant_sizes(const Plan& p) {
     z.q_scale = (size_t)p.rows_q * p.hq / QBLK * 4;
     z.k_codes = (size_t)p.rows_k * p.hkv * d;
     z.k_scale = (size_t)p.rows_k * p.hkv / QBLK * 4;
-    z.v_codes = (size_t)p.rows_k * p.hkv * d;
-    z.v_scale = S * p.hkv * d * 4;
+    z.v_codes = (size_t)p.rows_k * p.hkv * d * (p.pv_half ? 2 : 1);
+    z.v_scale = p.pv_half ? 0 : S * p.hkv * d * 4;
     z.delta_s = p.smooth_q ? (size_t)p.rows_k * p.hq * 4 : 0;
     return z;
 }
@@ -82,8 +83,8 @@ WsLayout ws_layout(const Plan& p, bool quant_in_ws) {
     w.part_q = take(p.smooth_q ? (size_t)p.rows_q / QBLK * p.hq * d * 4 : 0);
     w.part_k = take(p.smooth_k ? (size_t)p.rows_k / QBLK * p.hkv * d * 4 : 0);
     w.part_v = take(p.smooth_v ? (size_t)p.rows_k / QBLK * p.hkv * d * 4 : 0);
-    w.part_vmax = take((size_t)p.rows_k / QBLK * p.hkv * d * 4);
-    w.v_amax = take((size_t)p.S * p.hkv * d * 4);
+    w.part_vmax = take(p.pv_half ? 0 : (size_t)p.rows_k / QBLK * p.hkv * d * 4);
+    w.v_amax = take(p.pv_half ? 0 : (size_t)p.S * p.hkv * d * 4);
     w.total = off + ALIGN;   // slack so that an unaligned base can be rounded up
     return w;
 }
@@ -101,8 +102,8 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
     if (D.dtype != SAGE_F16 && D.dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
     if (D.layout != SAGE_HND && D.layout != SAGE_NHD) return SAGE_ERR_LAYOUT;
     if (!flag_ok(D.is_causal) || !flag_ok(D.smooth_q) || !flag_ok(D.smooth_k) ||
-        !flag_ok(D.smooth_v) || D.reserved[0] || D.reserved[1] || D.reserved[2] ||
-        !std::isfinite(D.sm_scale))
+        !flag_ok(D.smooth_v) || (D.pv_mode != SAGE_PV_FP8 && D.pv_mode != SAGE_PV_HALF) ||
+        D.reserved[0] || D.reserved[1] || !std::isfinite(D.sm_scale))
         return SAGE_ERR_FLAGS;
     if (D.head_dim != 64 && D.head_dim != 96 && D.head_dim != 128) return SAGE_ERR_HEAD_DIM;
     if (D.hq < 1 || D.hkv < 1 || D.hq > 65536 || D.hkv > 65536) return SAGE_ERR_SHAPE;
@@ -126,6 +127,7 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
     p.smooth_q = D.smooth_q;
     p.smooth_k = D.smooth_k;
     p.smooth_v = D.smooth_v;
+    p.pv_half = D.pv_mode == SAGE_PV_HALF;
     p.sm_scale = D.sm_scale > 0.0f ? D.sm_scale : 1.0f / std::sqrt((float)D.head_dim);
     if (varlen) {
         if (cuq[0] != 0 || cuk[0] != 0) return SAGE_ERR_SEQLENS;
@@ -205,6 +207,7 @@ std::vector<KParams> make_params(const Plan& p) {
     base.hkv = p.hkv;
     base.group = p.group;
     base.causal = p.causal;
+    base.pv_half = p.pv_half;
     base.sm_scale = p.sm_scale;
     base.sml2 = (float)((double)p.sm_scale * 1.4426950408889634);
     base.qs = p.qs;
@@ -315,7 +318,7 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
             sj.j[n] = StatJob{static_cast<const uint16_t*>(v), P.vs, nullptr, part_v, 2, p.hkv,
                               STAT_SUM, kblocks};
             fj.j[n++] = FinJob{part_v, b.mu_v, nullptr, nullptr, 0, p.hkv, STAT_SUM, nseq * p.hkv};
-        } else {
+        } else if (!p.pv_half) {
             sj.j[n] = StatJob{static_cast<const uint16_t*>(v), P.vs, nullptr, part_vmax, 2, p.hkv,
                               STAT_ABSMAX, kblocks};
             fj.j[n++] = FinJob{part_vmax, nullptr, v_amax, b.v_scale, 0, p.hkv, STAT_ABSMAX,
@@ -323,7 +326,7 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
         }
         SAGE_TRY(launch_stats(P, dtype, sj, st));
         SAGE_TRY(launch_finalize(P, fj, st));
-        if (p.smooth_v) {
+        if (p.smooth_v && !p.pv_half) {
             // 2. absolute maxima of V - mu_v
             StatJobs sv{};
             sv.j[0] = StatJob{static_cast<const uint16_t*>(v), P.vs, b.mu_v, part_vmax, 2, p.hkv,
@@ -352,6 +355,7 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
         qa.nq = chunk_blocks(P, true, p.hq, true);
         qa.nk = chunk_blocks(P, false, p.hkv, true);
         qa.nv = chunk_blocks(P, false, p.hkv, true);
+        qa.v_half = p.pv_half;
         SAGE_TRY(launch_quant(P, dtype, qa, st));
     }
     return SAGE_OK;
@@ -372,7 +376,7 @@ sage_quant_bufs bufs_in_ws(const Plan& p, uint8_t* ws, const WsLayout& w) {
     b.k_codes = reinterpret_cast<int8_t*>(ws + w.k_codes);
     b.k_scale = reinterpret_cast<float*>(ws + w.k_scale);
     b.v_codes = reinterpret_cast<uint8_t*>(ws + w.v_codes);
-    b.v_scale = reinterpret_cast<float*>(ws + w.v_scale);
+    b.v_scale = p.pv_half ? nullptr : reinterpret_cast<float*>(ws + w.v_scale);
     b.delta_s = p.smooth_q ? reinterpret_cast<float*>(ws + w.delta_s) : nullptr;
     return b;
 }
@@ -453,7 +457,8 @@ sage_status sage_quant_qkv(const sage_attn_desc* desc, const void* q, const void
     const bool empty = p.S == 0;
     if (!empty) {
         if (!q || !k || !v || !ws || !out->q_codes || !out->q_scale || !out->k_codes ||
-            !out->k_scale || !out->v_codes || !out->v_scale || (p.smooth_q && !out->mu_q) ||
+            !out->k_scale || !out->v_codes || (!p.pv_half && !out->v_scale) ||
+            (p.smooth_q && !out->mu_q) ||
             (p.smooth_k && !out->mu_k) || (p.smooth_v && !out->mu_v) ||
             (p.smooth_q && !out->delta_s))
             return SAGE_ERR_NULL;
@@ -494,7 +499,7 @@ sage_status sage_attn_fwd_quantized(const sage_attn_desc* desc, const int32_t* c
     if (!b) return SAGE_ERR_NULL;
     const bool empty = p.S == 0 || p.total_q == 0;
     if (!empty && (!o || !b->q_codes || !b->q_scale || !b->k_codes || !b->k_scale ||
-                   !b->v_codes || !b->v_scale || (p.smooth_q && !b->delta_s) ||
+                   !b->v_codes || (!p.pv_half && !b->v_scale) || (p.smooth_q && !b->delta_s) ||
                    (p.smooth_v && !b->mu_v)))
         return SAGE_ERR_NULL;
     const void* ptrs[] = {o, b->q_codes, b->k_codes, b->v_codes, b->q_scale, b->k_scale,
@@ -550,7 +555,7 @@ const char* sage_status_string(sage_status s) {
         case SAGE_ERR_SEQLENS: return "invalid cu_seqlens";
         case SAGE_ERR_ARCH: return "device is not gfx950";
         case SAGE_ERR_HIP: return "HIP runtime error";
-        case SAGE_ERR_FLAGS: return "invalid flag or reserved field";
+        case SAGE_ERR_FLAGS: return "invalid flag, pv_mode or reserved field";
     }
     return "unknown status";
 }

@@ -49,6 +49,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr float LOG2_448 = 8.807354922057604f;
 constexpr int SBIAS_I = 0x4B400000;
@@ -58,7 +60,7 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr int FWD_WAVES = 8;               // waves per workgroup of the fused kernel
 constexpr int FWD_NT = 64 * FWD_WAVES;
 
-template <int D>
+template <int D, bool PVH = false>
 struct Tile {
     // LDS image of one 128-key tile.  K rows are 128 bytes (64 for D = 64;
     // D = 96 leaves two 16-byte slots of a row unused); V^T rows (one per
@@ -66,16 +68,20 @@ struct Tile {
     // D = 96 so that it is a whole number of 8 KB copies.  Rows are dense and
     // their 16-byte slots are XOR-swizzled (slot = granule ^ swz(row)) so that
     // the MFMA operand reads of 16 consecutive rows hit distinct banks.
+    // With 16-bit P.V operands (PVH) a V^T row holds 128 two-byte values.
     static constexpr int KRS = D == 64 ? 64 : 128;
     static constexpr int KBYTES = KVT * KRS;
     static constexpr int VROWS = D == 96 ? 128 : D;
-    static constexpr int VBYTES = VROWS * KVT;
+    static constexpr int VES = PVH ? 2 : 1;           // bytes per V element
+    static constexpr int VRB = KVT * VES;             // bytes per V^T row
+    static constexpr int VBYTES = VROWS * VRB;
     static constexpr int DSBYTES = 4 * KVT * 4;  // score bias, per head of the workgroup
 };
 
 template <int RS>
 __device__ inline int swz(int row) {
-    if constexpr (RS == 128) return (row & 7) ^ ((row >> 3) & 1);
+    if constexpr (RS == 256) return row & 15;
+    else if constexpr (RS == 128) return (row & 7) ^ ((row >> 3) & 1);
     else return ((row >> 1) & 3) ^ ((row >> 3) & 1);
 }
 
@@ -107,36 +113,37 @@ __device__ inline void bar() {
 // swizzled LDS image results.  The key permutation and the swizzle repeat
 // every 32 rows and a copy spans a multiple of 32 rows, so copy i's source is
 // copy 0's plus a constant: one offset per tensor suffices.
-template <int D, int NT>
+template <int D, int NT, bool PVH = false>
 struct DmaOffsets {
-    static constexpr int KCOPIES = Tile<D>::KBYTES / (NT * 16);
-    static constexpr int VCOPIES = Tile<D>::VBYTES / (NT * 16);
-    static constexpr int KROWS = NT * 16 / Tile<D>::KRS;   // key rows per copy
-    static constexpr int VROWS = NT * 16 / KVT;            // V^T rows per copy
-    static_assert(KCOPIES * NT * 16 == Tile<D>::KBYTES && KROWS % 32 == 0, "K copy shape");
-    static_assert(VCOPIES * NT * 16 == Tile<D>::VBYTES && VROWS % 16 == 0, "V copy shape");
+    using TT = Tile<D, PVH>;
+    static constexpr int KCOPIES = TT::KBYTES / (NT * 16);
+    static constexpr int VCOPIES = TT::VBYTES / (NT * 16);
+    static constexpr int KROWS = NT * 16 / TT::KRS;        // key rows per copy
+    static constexpr int VROWS = NT * 16 / TT::VRB;        // V^T rows per copy
+    static_assert(KCOPIES * NT * 16 == TT::KBYTES && KROWS % 32 == 0, "K copy shape");
+    static_assert(VCOPIES * NT * 16 == TT::VBYTES && VROWS % 16 == 0, "V copy shape");
     int k0;   // bytes from the key tile start (row-major codes)
-    int v0;   // bytes from the V^T tile start (channel rows of npk bytes)
+    int v0;   // bytes from the V^T tile start (channel rows of npk elements)
 
     __device__ inline void init(int npk) {
-        using T = Tile<D>;
+        using T = TT;
         const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
         const int o = w * 1024 + lane * 16;
         const int row = o / T::KRS, slot = (o % T::KRS) / 16;
         int lg = slot ^ swz<T::KRS>(row);
         if (D == 96 && lg >= 6) lg &= 1;           // unused slots: any in-row granule
         k0 = key_of_row(row) * D + lg * 16;
-        const int ch = o / KVT, vslot = (o % KVT) / 16;
-        v0 = ch * npk + ((vslot ^ swz<128>(ch)) << 4);
+        const int ch = o / T::VRB, vslot = (o % T::VRB) / 16;
+        v0 = ch * npk * T::VES + ((vslot ^ swz<T::VRB>(ch)) << 4);
     }
 };
 
 // Issue this thread's copies of K tile t (and of the per-head score bias of
 // the tile, which has its own stage) into LDS.
-template <int D, int NT, bool HAS_DS>
-__device__ inline void stage_k(uint8_t* kst, uint8_t* dsst, const DmaOffsets<D, NT>& off,
+template <int D, int NT, bool HAS_DS, bool PVH = false>
+__device__ inline void stage_k(uint8_t* kst, uint8_t* dsst, const DmaOffsets<D, NT, PVH>& off,
                                const int8_t* kbase, const float* dsb, int npk, int t, int hpw) {
-    using O = DmaOffsets<D, NT>;
+    using O = DmaOffsets<D, NT, PVH>;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int8_t* kt = kbase + (int64_t)t * KVT * D;
 #pragma unroll
@@ -153,19 +160,20 @@ __device__ inline void stage_k(uint8_t* kst, uint8_t* dsst, const DmaOffsets<D, 
 }
 
 // Issue this thread's copies of V^T tile t into LDS.
-template <int D, int NT>
-__device__ inline void stage_v(uint8_t* vst, const DmaOffsets<D, NT>& off, const uint8_t* vbase,
-                               int npk, int t) {
-    using O = DmaOffsets<D, NT>;
+template <int D, int NT, bool PVH = false>
+__device__ inline void stage_v(uint8_t* vst, const DmaOffsets<D, NT, PVH>& off,
+                               const uint8_t* vbase, int npk, int t) {
+    using O = DmaOffsets<D, NT, PVH>;
+    using T = Tile<D, PVH>;
     const int w = threadIdx.x >> 6;
-    const uint8_t* vt = vbase + t * KVT;
+    const uint8_t* vt = vbase + (int64_t)t * KVT * T::VES;
 #pragma unroll
     for (int i = 0; i < O::VCOPIES; ++i) {
         // D = 96: rows 96..127 of the stage are padding; their copies read
         // channels 0..31 again (any valid source)
-        const int dst_ch = i * O::VROWS + (threadIdx.x * 16) / KVT;
+        const int dst_ch = i * O::VROWS + (threadIdx.x * 16) / T::VRB;
         const int64_t rows = (int64_t)i * O::VROWS - ((D == 96 && dst_ch >= 96) ? 96 : 0);
-        dma16(vt + off.v0 + rows * npk, vst + i * NT * 16 + w * 1024);
+        dma16(vt + off.v0 + rows * npk * T::VES, vst + i * NT * 16 + w * 1024);
     }
 }
 
@@ -287,6 +295,54 @@ __device__ inline void pv_tile(const uint8_t* Vs, const v8i* pb, v16f* acc) {
         }
 }
 
+// The 16-bit variant: acc[c] += V^T(channels 32c..32c+31) . P^T with the
+// 32x32x16 f16 / bf16 MFMA.  Step (b, j) sums 16 keys: lane half h supplies
+// keys 32b + 16h + 8j .. +7 of both operands (the summation index only has
+// to agree between them), V^T as one 16-byte granule of its 256-byte row and
+// P as ph[2b + j].
+template <int D, int DT>
+__device__ inline void pv_tile_h(const uint8_t* Vs, const v4i* ph, v16f* acc) {
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, qi = lane & 31;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // one 32-key block at a time keeps the operand reads in flight (and
+        // their registers) to one block's worth
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c) {
+                const int ch = 32 * c + qi;
+                const int g = 4 * b + 2 * h + j;
+                const v4i a = *reinterpret_cast<const v4i*>(Vs + ch * (2 * KVT) +
+                                                            ((g ^ swz<256>(ch)) << 4));
+                if constexpr (DT == 0)
+                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, ph[2 * b + j]), acc[c],
+                        0, 0, 0);
+                else
+                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, ph[2 * b + j]),
+                        acc[c], 0, 0, 0);
+            }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Two FP32 values rounded to nearest even into the 16-bit type DT (0 fp16,
+// 1 bf16), packed low | high << 16.
+template <int DT>
+__device__ inline uint32_t pack16(float lo, float hi) {
+    if constexpr (DT == 0) {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    } else {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+    }
+}
+
 __device__ inline float swap_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -314,12 +370,17 @@ __device__ inline int max32(const v16i& a, const v16i& b) {
 
 // Online softmax of one tile: updates the running max and sum, writes P^ in
 // the B layout of the 32x32x64 FP8 MFMA (half kh covers the lane's keys of
-// blocks 2kh and 2kh+1, bytes 0..15 and 16..31) and returns alpha, the
-// factor that moves earlier contributions to the new max.  Keys past `lim`
-// are masked when MASK.
-template <bool MASK, bool HAS_DS>
-__device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, const float* dsl,
-                                     float sml2, int kt0, int lim, float& m_run, float& l_run) {
+// blocks 2kh and 2kh+1, bytes 0..15 and 16..31) -- or, with 16-bit operands
+// (PVH), p itself rounded into the type DT, eight keys per ph entry as
+// pv_tile_h reads them -- and returns alpha, the factor that moves earlier
+// contributions to the new max.  Keys past `lim` are masked when MASK.
+// The FP8 P^ carries the static scale 448 (folded into the exponent); the
+// 16-bit p does not.
+template <bool MASK, bool HAS_DS, bool PVH = false, int DT = 0>
+__device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, float c1,
+                                     const float* dsl, float sml2, int kt0, int lim, float& m_run,
+                                     float& l_run) {
+    constexpr float POFF = PVH ? 0.0f : LOG2_448;
     const int h = (threadIdx.x & 63) >> 5;
     float p[4][16];
     float m_new;
@@ -338,7 +399,7 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
         const float f0 = mx0 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx0) - SBIAS_F) * c0;
         const float f1 = mx1 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx1) - SBIAS_F) * c1;
         m_new = fmaxf(m_run, swap_max(fmaxf(f0, f1)));
-        const float nm = LOG2_448 - (m_new == -INFINITY ? 0.0f : m_new);
+        const float nm = POFF - (m_new == -INFINITY ? 0.0f : m_new);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -362,7 +423,7 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
             }
         }
         m_new = fmaxf(m_run, swap_max(mt) * sml2);
-        const float nm = LOG2_448 - (m_new == -INFINITY ? 0.0f : m_new);
+        const float nm = POFF - (m_new == -INFINITY ? 0.0f : m_new);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -381,19 +442,31 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, float c0, float c1, co
             if (b > 0 || r >= 8) ps[r % 8] += p[b][r];
     const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
     l_run = fmaf(alpha, l_run, psum);
+    if constexpr (PVH) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int wd = 0; wd < 8; ++wd) {
-            const int b = 2 * kh + wd / 4, r0 = 4 * (wd % 4);
-            // the first convert fills the low half of the word and the second
-            // the high half, so the word's prior contents do not matter: it is
-            // seeded with a value that dies here (no zeroing move)
-            uint32_t u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0], p[b][r0 + 1],
-                                                         __float_as_uint(p[b][r0]), false);
-            u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0 + 2], p[b][r0 + 3], u, true);
-            pb[kh][wd] = (int)u;
-        }
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd)
+                    ph[2 * b + j][wd] =
+                        (int)pack16<DT>(p[b][8 * j + 2 * wd], p[b][8 * j + 2 * wd + 1]);
+    } else {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int wd = 0; wd < 8; ++wd) {
+                const int b = 2 * kh + wd / 4, r0 = 4 * (wd % 4);
+                // the first convert fills the low half of the word and the
+                // second the high half, so the word's prior contents do not
+                // matter: it is seeded with a value that dies here (no zeroing
+                // move)
+                uint32_t u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0], p[b][r0 + 1],
+                                                             __float_as_uint(p[b][r0]), false);
+                u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0 + 2], p[b][r0 + 3], u, true);
+                pb[kh][wd] = (int)u;
+            }
+    }
     return alpha;
 }
 
@@ -436,7 +509,7 @@ __device__ inline uint32_t f2h_bits(float f) {
 //   every wave waits for its copies before each barrier.
 //   bias(t): three buffers, as it is read up to epoch 2t+2.
 // ---------------------------------------------------------------------------
-template <int D, int DT, bool HAS_DS>
+template <int D, int DT, bool HAS_DS, bool PVH>
 __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __restrict__ qc,
                                                  const float* __restrict__ qsc,
                                                  const int8_t* __restrict__ kc,
@@ -448,7 +521,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                                                  uint16_t* __restrict__ o,
                                                  float* __restrict__ lse) {
     extern __shared__ __align__(16) uint8_t smem[];
-    using T = Tile<D>;
+    using T = Tile<D, PVH>;
     const Work w = decode_work<FWD_WAVES>(P);
     const SeqInfo& si = w.si;
     const int lane = threadIdx.x & 63;
@@ -459,7 +532,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
 
     const int64_t krow0 = (si.rk * P.hkv + (int64_t)w.hkv * si.npk);
     const int8_t* kbase = kc + krow0 * D;
-    const uint8_t* vbase = vc + krow0 * D;
+    const uint8_t* vbase = vc + krow0 * D * T::VES;
     const float* kscb = ksc + krow0 / QBLK;
     const float* dsb = HAS_DS ? ds + si.rk * P.hq + (int64_t)w.head0 * si.npk : nullptr;
 
@@ -487,20 +560,29 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     uint8_t* kst0 = smem;
     uint8_t* vst0 = smem + 2 * T::KBYTES;
     uint8_t* dst0 = vst0 + 2 * T::VBYTES;      // score-bias stages (HAS_DS)
-    DmaOffsets<D, FWD_NT> off;
+    DmaOffsets<D, FWD_NT, PVH> off;
     off.init(si.npk);
 
     // stage tile 0 (K and bias) with every wave, then offset group 1
     if (w.nt_wg > 0)
-        stage_k<D, FWD_NT, HAS_DS>(kst0, dst0, off, kbase, dsb, si.npk, 0, w.hpw);
+        stage_k<D, FWD_NT, HAS_DS, PVH>(kst0, dst0, off, kbase, dsb, si.npk, 0, w.hpw);
     bar();
     if (grp == 1) bar();
 
-    v8i pb[2];
+    v8i pb[2];                  // P^ of the previous tile (E4M3)
+    v4i ph[PVH ? 8 : 1];        // ... or its 16-bit p (PVH)
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int wd = 0; wd < 8; ++wd) pb[kh][wd] = 0;
+#pragma unroll
+    for (int i = 0; i < (PVH ? 8 : 1); ++i) ph[i] = v4i{0, 0, 0, 0};
+    // acc += V(t)^T . P^(t)^T in either operand type
+    auto pv = [&](int tt) {
+        const uint8_t* vs_ = vst0 + (tt & 1) * T::VBYTES;
+        if constexpr (PVH) pv_tile_h<D, DT>(vs_, ph, acc);
+        else pv_tile<D>(vs_, pb, acc);
+    };
     v16i sacc[4];
     float alpha_prev = 1.0f;   // rescale owed to acc before its next P.V
 
@@ -508,20 +590,29 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         // ---- MFMA phase ----
         __builtin_amdgcn_s_setprio(2);
         if (t + 1 < w.nt_wg)
-            stage_k<D, FWD_NT, HAS_DS>(kst0 + ((t + 1) & 1) * T::KBYTES,
-                                       dst0 + ((t + 1) % 3) * T::DSBYTES, off, kbase, dsb, si.npk,
-                                       t + 1, w.hpw);
-        stage_v<D, FWD_NT>(vst0 + (t & 1) * T::VBYTES, off, vbase, si.npk, t);
+            stage_k<D, FWD_NT, HAS_DS, PVH>(kst0 + ((t + 1) & 1) * T::KBYTES,
+                                            dst0 + ((t + 1) % 3) * T::DSBYTES, off, kbase, dsb,
+                                            si.npk, t + 1, w.hpw);
+        stage_v<D, FWD_NT, PVH>(vst0 + (t & 1) * T::VBYTES, off, vbase, si.npk, t);
         if (t < w.nt_w) {
-            qk_tile<D>(kst0 + (t & 1) * T::KBYTES, qf, sacc);
-            if (t > 0) {
-                rescale<D>(acc, alpha_prev);
-                pv_tile<D>(vst0 + ((t - 1) & 1) * T::VBYTES, pb, acc);
+            if constexpr (PVH) {
+                // P.V first: the 16-bit P^ then dies before S(t) is formed
+                if (t > 0) {
+                    rescale<D>(acc, alpha_prev);
+                    pv(t - 1);
+                }
+                qk_tile<D>(kst0 + (t & 1) * T::KBYTES, qf, sacc);
+            } else {
+                qk_tile<D>(kst0 + (t & 1) * T::KBYTES, qf, sacc);
+                if (t > 0) {
+                    rescale<D>(acc, alpha_prev);
+                    pv(t - 1);
+                }
             }
         } else if (t == w.nt_w && t > 0) {
             // this wave's rows are done: flush its last tile
             rescale<D>(acc, alpha_prev);
-            pv_tile<D>(vst0 + ((t - 1) & 1) * T::VBYTES, pb, acc);
+            pv(t - 1);
         }
         // the tile's score scales, loaded ahead of the softmax phase (the
         // empty asm keeps the compiler from sinking the loads past the barrier)
@@ -543,11 +634,11 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                 (t + 1) * KVT > nkv || (P.causal && (t + 1) * KVT - 1 > wave_diag);
             float alpha;
             if (need_mask)
-                alpha = softmax_tile<true, HAS_DS>(sacc, pb, c0, c1, dsl, P.sml2, kt0, lim, m_run,
-                                                   l_run);
+                alpha = softmax_tile<true, HAS_DS, PVH, DT>(sacc, pb, ph, c0, c1, dsl, P.sml2, kt0,
+                                                            lim, m_run, l_run);
             else
-                alpha = softmax_tile<false, HAS_DS>(sacc, pb, c0, c1, dsl, P.sml2, kt0, lim,
-                                                    m_run, l_run);
+                alpha = softmax_tile<false, HAS_DS, PVH, DT>(sacc, pb, ph, c0, c1, dsl, P.sml2,
+                                                             kt0, lim, m_run, l_run);
             // acc (the tiles before t, at the previous max) is rescaled in
             // the next MFMA phase, before the P.V of tile t
             alpha_prev = alpha;
@@ -556,7 +647,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     }
     if (w.nt_w > 0 && w.nt_w == w.nt_wg) {
         rescale<D>(acc, alpha_prev);
-        pv_tile<D>(vst0 + ((w.nt_wg - 1) & 1) * T::VBYTES, pb, acc);
+        pv(w.nt_wg - 1);
     }
     if (grp == 0) bar();   // balance group 1's leading barrier
 
@@ -573,13 +664,15 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     if (w.q0 < nq) {
         const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         const int64_t vsb = ((int64_t)si.sid * P.hkv + w.hkv) * D;
-        // all scale (and mean) loads go out before the first use
+        // all scale (and mean) loads go out before the first use; the
+        // 16-bit operands carry no scale
         float4 sv[D / 32][4], mv[D / 32][4];
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4)
-                sv[c][r4] = *reinterpret_cast<const float4*>(vsc + vsb + 32 * c + 8 * r4 + 4 * h);
+                sv[c][r4] = PVH ? make_float4(1.f, 1.f, 1.f, 1.f)
+                                : *reinterpret_cast<const float4*>(vsc + vsb + 32 * c + 8 * r4 + 4 * h);
         const bool add_mu = mu_v && l_tot > 0.0f;
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
@@ -607,7 +700,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
             }
         if (lse && h == 0 && my_q < nq)
             lse[si.lse0 + (int64_t)w.head * P.lse_hstride + my_q] =
-                l_tot > 0.0f ? (m_run + __log2f(l_tot) - LOG2_448) * LN2 : -INFINITY;
+                l_tot > 0.0f ? (m_run + __log2f(l_tot) - (PVH ? 0.0f : LOG2_448)) * LN2 : -INFINITY;
         // whole rows: D/8 granules of 16 bytes per row, 32 rows
         uint16_t* obase = o + si.o_el + (int64_t)w.head * P.os.h;
         constexpr int GPRW = D / 8;
@@ -686,26 +779,28 @@ int wg_count_host(const KParams& P, int waves) {
     return tot;
 }
 
-template <int D, bool HAS_DS>
+template <int D, bool HAS_DS, bool PVH>
 constexpr int lds_bytes() {
-    return 2 * Tile<D>::KBYTES + 2 * Tile<D>::VBYTES + (HAS_DS ? 3 * Tile<D>::DSBYTES : 0);
+    return 2 * Tile<D, PVH>::KBYTES + 2 * Tile<D, PVH>::VBYTES +
+           (HAS_DS ? 3 * Tile<D, PVH>::DSBYTES : 0);
 }
 
-template <int D, int DT, bool HAS_DS>
+template <int D, int DT, bool HAS_DS, bool PVH>
 hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const int8_t* kc,
                   const float* ksc, const uint8_t* vc, const float* vsc, const float* ds,
                   const float* mu_v, void* o, float* lse, hipStream_t st) {
     static bool attr_set = false;   // benign race: the call is idempotent
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D, DT, HAS_DS>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           lds_bytes<D, HAS_DS>());
+        hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D, DT, HAS_DS, PVH>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds_bytes<D, HAS_DS, PVH>());
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int nblocks = wg_count_host(P, FWD_WAVES);
     if (nblocks <= 0) return hipSuccess;
-    k_attn<D, DT, HAS_DS><<<nblocks, FWD_NT, lds_bytes<D, HAS_DS>(), st>>>(
+    k_attn<D, DT, HAS_DS, PVH><<<nblocks, FWD_NT, lds_bytes<D, HAS_DS, PVH>(), st>>>(
         P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, static_cast<uint16_t*>(o), lse);
     return hipGetLastError();
 }
@@ -715,9 +810,14 @@ hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const in
 hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const float* qsc,
                        const int8_t* kc, const float* ksc, const uint8_t* vc, const float* vsc,
                        const float* ds, const float* mu_v, void* o, float* lse, hipStream_t st) {
-#define SAGE_A(D, DT)                                                                 \
-    return ds ? attn_d<D, DT, true>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st) \
-              : attn_d<D, DT, false>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st)
+#define SAGE_AH(D, DT, PVH)                                                                 \
+    return ds ? attn_d<D, DT, true, PVH>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st) \
+              : attn_d<D, DT, false, PVH>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st)
+#define SAGE_A(D, DT)                   \
+    do {                                \
+        if (P.pv_half) SAGE_AH(D, DT, true); \
+        SAGE_AH(D, DT, false);          \
+    } while (0)
     if (dtype == 0) {
         if (P.d == 64) { SAGE_A(64, 0); }
         if (P.d == 96) { SAGE_A(96, 0); }
@@ -728,6 +828,7 @@ hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const floa
         SAGE_A(128, 1);
     }
 #undef SAGE_A
+#undef SAGE_AH
 }
 
 hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,

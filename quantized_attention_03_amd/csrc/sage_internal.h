@@ -34,6 +34,7 @@ struct SeqTab {
 struct KParams {
     int32_t d, hq, hkv, group;          // group = hq / hkv
     int32_t causal;
+    int32_t pv_half;                    // P.V in the input's 16-bit type (else E4M3)
     float sm_scale;                     // natural-log units
     float sml2;                         // sm_scale * log2(e)
     Strides qs, ks, vs, os;
@@ -140,9 +141,10 @@ struct QuantArgs {
     const uint16_t *q, *k, *v;
     const float *mu_q, *mu_k, *mu_v, *v_amax;
     int8_t *q_codes, *k_codes;
-    uint8_t* v_codes;
+    uint8_t* v_codes;     // E4M3 codes, or 16-bit values when v_half
     float *q_scale, *k_scale, *delta_s;
     int32_t nq, nk, nv;   // workgroups: Q blocks, K blocks, V chunks
+    int32_t v_half;       // V operand kept 16-bit (no scale) instead of E4M3
 };
 // Chunks of 64 tokens one statistics workgroup covers (per sequence and head
 // the launch needs ceil(chunks / this) workgroups).

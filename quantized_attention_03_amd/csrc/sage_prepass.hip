@@ -409,6 +409,81 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
     }
 }
 
+// The 16-bit V operand of the INT8-QK / 16-bit-PV variant (install guide
+// "SageAttention量化加速框架", section 3.1: the qk_int8_pv_fp16 kernel): one
+// 64-token chunk of one head, v (or v - mu_v, rounded to nearest even into
+// the input's type) written channel-major like the E4M3 codes, 2 bytes per
+// element.  Without smoothing the values are the input bits.
+template <int DT>
+__device__ inline uint32_t to16(float f) {
+    if constexpr (DT == 0) {
+        return (uint32_t)__half_as_ushort(__float2half_rn(f));
+    } else {
+        uint32_t u = __float_as_uint(f);
+        u += 0x7fffu + ((u >> 16) & 1u);     // round to nearest even (inputs finite)
+        return u >> 16;
+    }
+}
+
+template <int D>
+constexpr int half_v_lds_bytes() { return D * (2 * QBLK + 8); }
+
+template <int DT, int D>
+__device__ inline void half_v_chunk(const KParams& P, const uint16_t* __restrict__ v,
+                                    const float* __restrict__ mu, uint16_t* __restrict__ out,
+                                    int blkid, uint8_t* tr) {
+    constexpr int GPR = D / 8;               // 8-channel granules of a token row
+    constexpr int TASKS = GPR * (QBLK / 4);  // (granule, group of 4 tokens) pairs
+    constexpr int TS = 2 * QBLK + 8;         // LDS bytes per channel row of the transpose
+
+    int local;
+    ChunkCount cnt{&P, false, P.hkv, 1};
+    const int s = find_seq(P, blkid, cnt, &local);
+    const SeqInfo si = seq_info(P, s);
+    const int n = si.nkv;
+    const int nch = si.npk / QBLK;
+    const int h = local / nch, chk = local % nch;
+    const int64_t el0 = si.v_el + (int64_t)h * P.vs.h;
+    const float* muh = mu ? mu + ((int64_t)si.sid * P.hkv + h) * D : nullptr;
+
+    // Each task reads 4 consecutive tokens of one granule and leaves, per
+    // channel, the 4 values as 8 bytes of the channel's LDS row.
+    for (int task = threadIdx.x; task < TASKS; task += WG) {
+        const int cg = 8 * (task % GPR), tq = task / GPR;
+        float m8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m8[e] = muh ? muh[cg + e] : 0.0f;
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = hi[e] = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = chk * QBLK + 4 * tq + u;
+            if (t >= n) continue;                  // tokens past the end: zero
+            float val[8];
+            load8<DT>(v + el0 + (int64_t)t * P.vs.n + cg, val);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t b = to16<DT>(muh ? val[e] - m8[e] : val[e]);
+                if (u < 2) lo[e] |= b << (16 * u);
+                else hi[e] |= b << (16 * (u - 2));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<uint2*>(tr + (cg + e) * TS + 8 * tq) = make_uint2(lo[e], hi[e]);
+    }
+    __syncthreads();
+    // store: channel c, 128 bytes = 8 x 16 B
+    const int64_t vrow = (si.rk * P.hkv + (int64_t)h * si.npk) * D;
+    for (int idx = threadIdx.x; idx < D * 8; idx += WG) {
+        const int c = idx / 8, part = idx % 8;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(tr + c * TS + part * 16);
+        *reinterpret_cast<uint4*>(out + vrow + (int64_t)c * si.npk + chk * QBLK + part * 8) =
+            make_uint4(src[0], src[1], src[2], src[3]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // All quantization of a problem in one launch: the Q blocks, then the K
 // blocks (with the score bias when Q is smoothed), then the V chunks.
@@ -416,7 +491,9 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
 template <int DT, int D, bool DELTA>
 __global__ __launch_bounds__(WG) void k_quant(KParams P, QuantArgs A) {
     constexpr int QK_LDS = (WG / 64 + (DELTA ? QBLK * D : 0)) * 4;
-    constexpr int LDS = QK_LDS > quant_v_lds_bytes<D>() ? QK_LDS : quant_v_lds_bytes<D>();
+    constexpr int VL = quant_v_lds_bytes<D>() > half_v_lds_bytes<D>() ? quant_v_lds_bytes<D>()
+                                                                      : half_v_lds_bytes<D>();
+    constexpr int LDS = QK_LDS > VL ? QK_LDS : VL;
     __shared__ __align__(16) uint8_t sm[LDS];
     int blk = blockIdx.x;
     if (blk < A.nq) {
@@ -431,7 +508,10 @@ __global__ __launch_bounds__(WG) void k_quant(KParams P, QuantArgs A) {
         return;
     }
     blk -= A.nk;
-    quant_v_chunk<DT, D>(P, A.v, A.mu_v, A.v_amax, A.v_codes, blk, sm);
+    if (A.v_half)
+        half_v_chunk<DT, D>(P, A.v, A.mu_v, reinterpret_cast<uint16_t*>(A.v_codes), blk, sm);
+    else
+        quant_v_chunk<DT, D>(P, A.v, A.mu_v, A.v_amax, A.v_codes, blk, sm);
 }
 
 // ---------------------------------------------------------------------------

@@ -33,18 +33,18 @@ def gpu_inputs(w: synth.Workload):
     return q, k, v, meta
 
 
-def run_quant(w, q, k, v, meta):
+def run_quant(w, q, k, v, meta, pv="fp8"):
     kw = dict(tensor_layout=w.layout, is_causal=w.causal, smooth_q=w.smooth_q,
-              smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale)
+              smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale, pv_mode=pv)
     if w.varlen:
         kw.update(cu_seqlens_q=meta["cu_seqlens_q"], cu_seqlens_kv=meta["cu_seqlens_kv"])
     return qa.sage_quant_qkv(q, k, v, **kw)
 
 
-def run_fwd(w, q, k, v, meta, return_lse=True):
+def run_fwd(w, q, k, v, meta, return_lse=True, pv="fp8"):
     kw = dict(tensor_layout=w.layout, is_causal=w.causal, smooth_q=w.smooth_q,
               smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale,
-              return_lse=return_lse)
+              return_lse=return_lse, pv_mode=pv)
     if w.varlen:
         return qa.sage_attn_fwd_varlen(q, k, v, meta["cu_seqlens_q"], meta["cu_seqlens_kv"], **kw)
     return qa.sage_attn_fwd(q, k, v, **kw)
@@ -54,8 +54,9 @@ def _pad(x, m):
     return (x + m - 1) // m * m
 
 
-def unpack_quant(w, bufs):
-    """GPU buffers -> oracle.Prepass-shaped lists (numpy), plus pad checks."""
+def unpack_quant(w, bufs, pv="fp8"):
+    """GPU buffers -> oracle.Prepass-shaped lists (numpy), plus pad checks.
+    With pv = "half" the V operand is 16-bit (uint16 patterns), unscaled."""
     seqs = w.seq_lens()
     hq, hkv, d = w.Hq, w.Hkv, w.d
     host = {k: v.cpu().numpy() for k, v in bufs.items() if not k.startswith("_")}
@@ -68,7 +69,8 @@ def unpack_quant(w, bufs):
         qs = host["q_scale"][rq * hq // QB:(rq * hq + hq * npq) // QB].reshape(hq, npq // QB)
         kc = host["k_codes"][rk * hkv * d:(rk * hkv + hkv * npk) * d].reshape(hkv, npk, d)
         ks = host["k_scale"][rk * hkv // QB:(rk * hkv + hkv * npk) // QB].reshape(hkv, npk // QB)
-        vc = host["v_codes"][rk * hkv * d:(rk * hkv + hkv * npk) * d].reshape(hkv, d, npk)
+        vall = host["v_codes"].view(np.uint16) if pv == "half" else host["v_codes"]
+        vc = vall[rk * hkv * d:(rk * hkv + hkv * npk) * d].reshape(hkv, d, npk)
         pads_ok &= not qc[:, nq:].any() and not kc[:, nkv:].any() and not vc[:, :, nkv:].any()
         pads_ok &= not ks[:, -(-nkv // QB):].any()
         R.qc.append(qc[:, :nq])
@@ -76,7 +78,7 @@ def unpack_quant(w, bufs):
         R.kc.append(kc[:, :nkv])
         R.ks.append(ks[:, :-(-nkv // QB)])
         R.vc.append(vc.transpose(0, 2, 1)[:, :nkv])
-        R.vs.append(host["v_scale"].reshape(-1, hkv, d)[s])
+        R.vs.append(None if pv == "half" else host["v_scale"].reshape(-1, hkv, d)[s])
         R.mu_q.append(host["mu_q"].reshape(-1, hq, d)[s] if w.smooth_q else None)
         R.mu_k.append(host["mu_k"].reshape(-1, hkv, d)[s] if w.smooth_k else None)
         R.mu_v.append(host["mu_v"].reshape(-1, hkv, d)[s] if w.smooth_v else None)

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = qa.lib()
-    assert L.sage_abi_version() == 1
+    assert L.sage_abi_version() == 2
     for code in range(14):
         assert L.sage_status_string(code)
     assert L.sage_status_string(999) == b"unknown status"
@@ -65,6 +65,7 @@ def _ws(d, cuq=None, cuk=None, n=0):
 def test_desc_init_defaults():
     d = _desc()
     assert (d.smooth_k, d.smooth_q, d.smooth_v, d.is_causal, d.sm_scale) == (1, 0, 0, 0, 0.0)
+    assert d.pv_mode == _abi.PV_FP8 and tuple(d.reserved) == (0, 0)
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -78,6 +79,8 @@ def test_desc_init_defaults():
     ("nq", -1, "SAGE_ERR_SHAPE"),
     ("batch", -3, "SAGE_ERR_SHAPE"),
     ("hq", 7, "SAGE_ERR_GQA"),
+    ("pv_mode", 2, "SAGE_ERR_FLAGS"),
+    ("pv_mode", -1, "SAGE_ERR_FLAGS"),
 ])
 def test_descriptor_errors(field, value, status):
     d = _desc(**{field: value})
@@ -160,6 +163,23 @@ def test_quant_buf_sizes_follow_documented_layout():
     assert qa.lib().sage_quant_buf_sizes(ctypes.byref(dv), cq, ck, 3, ctypes.byref(z)) == 0
     assert z.q_codes == hq * (64 + 64 + 0) * dd          # lengths 1, 64, 0
     assert z.k_codes == hkv * (256 + 128 + 0) * dd      # lengths 129, 1, 0
+
+
+def test_half_pv_sizes():
+    """16-bit P.V operands: V is 2 bytes per element, no V scale, and the
+    workspace (no V maxima) is not larger than the E4M3 one."""
+    B, hkv, dd = 2, 2, 128
+    npk = _pad(300, 128)
+    for sv in (0, 1):
+        f8 = qa.quant_buf_sizes(_desc(smooth_v=sv))
+        h = qa.quant_buf_sizes(_desc(smooth_v=sv, pv_mode=_abi.PV_HALF))
+        assert h["v_codes"] == 2 * f8["v_codes"] == 2 * B * hkv * npk * dd
+        assert h["v_scale"] == 0 and f8["v_scale"] == B * hkv * dd * 4
+        assert {k: v for k, v in h.items() if k not in ("v_codes", "v_scale")} == \
+            {k: v for k, v in f8.items() if k not in ("v_codes", "v_scale")}
+        st, wf8 = _ws(_desc(smooth_v=sv))
+        st2, wh = _ws(_desc(smooth_v=sv, pv_mode=_abi.PV_HALF))
+        assert st == st2 == 0 and wh <= wf8 + B * hkv * npk * dd
 
 
 def test_empty_problem_is_a_no_op():
