@@ -13,6 +13,9 @@ Prints ONE JSON line.  Besides the standard fields it carries
                  dense INT8/FP8 MFMA peak of MI355X (5.0 POPS);
   cpu_baseline : the CPU oracle (same recipe, plain C) timed on a bounded
                  sample of the same workload on the host cores.
+--pv half times the 16-bit P.V variant instead (P and V in the input's type
+on the 16-bit MFMA); its roofline peak is that of the op mix, half INT8 at
+5.0 POPS and half fp16/bf16 at 2.5 PFLOP/s, i.e. 3.33 POPS.
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TOPS = 5000.0           # MI355X dense INT8 / FP8 MFMA peak (T-ops/s)
+PEAK_16 = 2500.0             # ... dense fp16 / bf16 MFMA peak
 WORKLOAD = "causal_gqa"
 
 
@@ -36,6 +40,8 @@ def _parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--pv", choices=("fp8", "half"), default="fp8",
+                    help="P.V operands: E4M3 (default) or the input's 16-bit type")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows per query head")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -84,7 +90,7 @@ def copy_calibration(mib: int):
           flush=True)
 
 
-def cpu_baseline(w, q, k, v, rows_per_head: int):
+def cpu_baseline(w, q, k, v, rows_per_head: int, pv: str = "fp8"):
     """Time the oracle's same-recipe forward on evenly spaced query rows of
     every head (the pre-pass is run first and not timed)."""
     import numpy as np
@@ -95,7 +101,7 @@ def cpu_baseline(w, q, k, v, rows_per_head: int):
     def u16(t):
         return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
-    prob = orc.problem_from_workload(w)
+    prob = orc.problem_from_workload(w, pv)
     pre = orc.prepass(prob, u16(q), u16(k), u16(v))
     threads = os.cpu_count() or 1
     rows, pairs = [], 0
@@ -135,7 +141,8 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v, meta = synth.make_inputs(w, device=dev)
     kw = dict(tensor_layout=w.layout, is_causal=w.causal, smooth_q=w.smooth_q,
-              smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale)
+              smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale,
+              pv_mode=args.pv)
     o = torch.empty_like(q)
     cu = {}
     if w.varlen:
@@ -189,6 +196,11 @@ def main():
     exact = w.exact_ops()
     value = formula / (ms * 1e-3) / 1e12
     achieved = exact / (kern_ms * 1e-3) / 1e12
+    half = args.pv == "half"
+    # half the ops are INT8 Q.K^T, half P.V in the operand type
+    peak = PEAK_TOPS if not half else 1.0 / (0.5 / PEAK_TOPS + 0.5 / PEAK_16)
+    io = "fp16 io" if w.dtype == "f16" else "bf16 io"
+    pvt = ("f16" if w.dtype == "f16" else "bf16") if half else "fp8"
     line = {
         "metric": "attention TOPS at d=128, N=8K/32K; % of dense INT8/FP8 MFMA peak",
         "value": round(value, 2),
@@ -200,23 +212,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8-qk/fp8-pv (fp16 io)" if w.dtype == "f16" else "int8-qk/fp8-pv (bf16 io)",
+        "dtype": f"int8-qk/{pvt}-pv ({io})",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
                                f"Nq=Nkv={w.Nq} d={w.d} {w.dtype} {w.layout}"
-                               f"{' causal' if w.causal else ''}",
+                               f"{' causal' if w.causal else ''}"
+                               f"{', 16-bit P.V' if half else ''}",
                    "global_batch": w.B, "seq_len": w.Nq, "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TOPS, 4),
-                     "traffic": measured_traffic(w.name),
-                     "kernel": "k_attn (fused INT8-QK / softmax / FP8-PV)",
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None if half else measured_traffic(w.name),
+                     "kernel": f"k_attn (fused INT8-QK / softmax / {pvt.upper()}-PV)",
                      "kernel_ms": round(kern_ms, 4), "ops_per_launch": exact},
         "prepass_ms": round(pre_ms, 4),   # whole call minus the fused kernel
         "exact_pair_tops": round(exact / (ms * 1e-3) / 1e12, 2),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, args.pv)
     print(json.dumps(line), flush=True)
 
 

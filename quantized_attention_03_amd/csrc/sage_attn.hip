@@ -50,6 +50,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr float LOG2_448 = 8.807354922057604f;
@@ -166,7 +169,7 @@ __device__ inline void stage_v(uint8_t* vst, const DmaOffsets<D, NT, PVH>& off,
     using O = DmaOffsets<D, NT, PVH>;
     using T = Tile<D, PVH>;
     const int w = threadIdx.x >> 6;
-    const uint8_t* vt = vbase + (int64_t)t * KVT * T::VES;
+    const uint8_t* vt = vbase + t * (KVT * T::VES);
 #pragma unroll
     for (int i = 0; i < O::VCOPIES; ++i) {
         // D = 96: rows 96..127 of the stage are padding; their copies read
@@ -332,15 +335,12 @@ __device__ inline void pv_tile_h(const uint8_t* Vs, const v4i* ph, v16f* acc) {
 
 // Two FP32 values rounded to nearest even into the 16-bit type DT (0 fp16,
 // 1 bf16), packed low | high << 16.
+// (one v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 per pair)
 template <int DT>
 __device__ inline uint32_t pack16(float lo, float hi) {
-    if constexpr (DT == 0) {
-        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
-    } else {
-        return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
-    }
+    const v2f x = {lo, hi};
+    if constexpr (DT == 0) return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2h));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
 }
 
 __device__ inline float swap_max(float x) {
