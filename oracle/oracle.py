@@ -67,9 +67,9 @@ def lib():
         "orc_delta_s": (None, [P, P, i64, i32, P]),
         "orc_qk_int32": (None, [P, P, i64, i64, i32, P]),
         "orc_attn_recipe_rows": (None, [P, P, P, P, P, P, P, P, i64, i64, i32, f32,
-                                        i32, i32, i32, P, i64, P, P]),
+                                        i32, i32, i32, i64, P, i64, P, P]),
         "orc_attn_recipe_half_rows": (None, [P, P, P, P, P, i32, P, P, i64, i64, i32, f32,
-                                             i32, i32, i32, P, i64, P, P]),
+                                             i32, i32, i32, i64, P, i64, P, P]),
         "orc_attn_exact_rows": (None, [P, P, P, i64, i64, i32, f64, i32, P, i64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -172,7 +172,7 @@ def qk_int32(qc, kc) -> np.ndarray:
     return s
 
 
-def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, rows):
+def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, rows, split=0):
     qc, kc, vc = _c(qc, np.int8), _c(kc, np.int8), _c(vc, np.uint8)
     nq, d = qc.shape
     nkv = kc.shape[0]
@@ -183,11 +183,13 @@ def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, ro
         _p(qc), _p(_c(qs, np.float32)), _p(kc), _p(_c(ks, np.float32)), _p(vc),
         _p(_c(vs, np.float32)), _p(None if ds is None else _c(ds, np.float32)),
         _p(None if mu_v is None else _c(mu_v, np.float32)), nq, nkv, d,
-        float(sm_scale), int(causal), int(bkv), BLK, _p(rows), rows.size, _p(out), _p(lse))
+        float(sm_scale), int(causal), int(bkv), BLK, int(split), _p(rows), rows.size, _p(out),
+        _p(lse))
     return out, lse
 
 
-def attn_recipe_half_rows(qc, qs, kc, ks, vh, dtype, ds, mu_v, sm_scale, causal, bkv, rows):
+def attn_recipe_half_rows(qc, qs, kc, ks, vh, dtype, ds, mu_v, sm_scale, causal, bkv, rows,
+                          split=0):
     """The 16-bit P.V variant: vh [nkv, d] fp16/bf16 bit patterns of the V
     operand; p^ is p rounded to the same type."""
     qc, kc, vh = _c(qc, np.int8), _c(kc, np.int8), _c(vh, np.uint16)
@@ -200,7 +202,8 @@ def attn_recipe_half_rows(qc, qs, kc, ks, vh, dtype, ds, mu_v, sm_scale, causal,
         _p(qc), _p(_c(qs, np.float32)), _p(kc), _p(_c(ks, np.float32)), _p(vh),
         1 if dtype == "bf16" else 0, _p(None if ds is None else _c(ds, np.float32)),
         _p(None if mu_v is None else _c(mu_v, np.float32)), nq, nkv, d,
-        float(sm_scale), int(causal), int(bkv), BLK, _p(rows), rows.size, _p(out), _p(lse))
+        float(sm_scale), int(causal), int(bkv), BLK, int(split), _p(rows), rows.size, _p(out),
+        _p(lse))
     return out, lse
 
 
@@ -234,15 +237,16 @@ class Problem:
     smooth_v: bool = False
     sm_scale: float | None = None
     pv_mode: str = "fp8"        # "fp8" (SageAttention2) | "half" (16-bit P.V)
+    kv_split: int = 0           # keys per split of the key range (0: one split)
 
     @property
     def scale(self) -> float:
         return self.sm_scale if self.sm_scale else 1.0 / math.sqrt(self.d)
 
 
-def problem_from_workload(w, pv_mode: str = "fp8") -> Problem:
+def problem_from_workload(w, pv_mode: str = "fp8", kv_split: int = 0) -> Problem:
     return Problem(w.dtype, w.layout, w.Hq, w.Hkv, w.d, w.seq_lens(), w.varlen, w.causal,
-                   w.smooth_q, w.smooth_k, w.smooth_v, w.sm_scale, pv_mode)
+                   w.smooth_q, w.smooth_k, w.smooth_v, w.sm_scale, pv_mode, kv_split)
 
 
 def split_heads(prob: Problem, x, which: str):
@@ -358,10 +362,10 @@ def forward_rows(prob: Problem, pre: Prepass, rows=None, bkv: int = 128,
         if prob.pv_mode == "half":
             return attn_recipe_half_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk],
                                          pre.ks[s][hk], pre.vc[s][hk], prob.dtype, ds, mu_v,
-                                         prob.scale, prob.causal, bkv, r)
+                                         prob.scale, prob.causal, bkv, r, prob.kv_split)
         return attn_recipe_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk], pre.ks[s][hk],
                                 pre.vc[s][hk], pre.vs[s][hk], ds, mu_v,
-                                prob.scale, prob.causal, bkv, r)
+                                prob.scale, prob.causal, bkv, r, prob.kv_split)
 
     with ThreadPoolExecutor(max_workers=threads or os.cpu_count()) as ex:
         res = list(ex.map(one, units))

@@ -289,13 +289,19 @@ static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
  *   delta_s     : FP32 [nkv] Q-smoothing compensation, or NULL
  *   mu_v        : FP32 [d] V mean to add back at the output, or NULL
  *   bkv         : key-tile width of the online softmax (p^ depends on it)
+ *   split       : keys per split (a multiple of bkv), or 0 for one split
  *   rows[nrows] : query rows to compute; out [nrows][d] FP32, lse [nrows]
- * Steps: s = fl32(S)*(sq*sk*sm_scale) (+ ds_j*sm_scale); for each key tile in
- * order: m' = max(m, max s), alpha = e^(m-m'), p = e^(s-m') (FP32),
+ * Steps: s = fl32(S)*(sq*sk*sm_scale) (+ ds_j*sm_scale); the keys are cut into
+ * splits of `split` keys, and in each split, for each key tile in order:
+ * m' = max(m, max s), alpha = e^(m-m'), p = e^(s-m') (FP32),
  * l = alpha*l + sum p (from the FP32 p), p^ = the P.V operand made from p,
- * acc = alpha*acc + sum p^ * v; finally o = acc*out_scale/l (+ mu_v).
- * A row that sees no key gives o = 0 and lse = -inf.  LSE is the
- * natural log of sum_j e^(s_j) over the scores as the recipe forms them. */
+ * acc = alpha*acc + sum p^ * v, starting from m = -inf, l = 0, acc = 0.
+ * The splits are then merged as partial softmax results (the log-sum-exp
+ * merge of flash-decoding): M = max m_s, w_s = e^(m_s - M), L = sum w_s l_s,
+ * A = sum w_s acc_s (in split order); o = A*out_scale/L (+ mu_v).  One split
+ * is the plain online softmax.  A row that sees no key gives o = 0 and
+ * lse = -inf.  LSE = M + ln L, the natural log of sum_j e^(s_j) over the
+ * scores as the recipe forms them. */
 enum { P_FP8 = 0, P_F16 = 1, P_BF16 = 2 };
 
 static float p_operand(float p, int p_mode) {
@@ -310,58 +316,87 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
                         const float* k_scale, const float* vdec, const float* out_scale,
                         int p_mode, const float* delta_s, const float* mu_v, int64_t nq,
                         int64_t nkv, int d, float sm_scale, int causal, int bkv, int blk,
-                        const int64_t* rows, int64_t nrows, float* out, float* lse) {
+                        int64_t split, const int64_t* rows, int64_t nrows, float* out,
+                        float* lse) {
+    const int64_t span = split > 0 ? split : (nkv > 0 ? nkv : 1);
+    const int64_t nsplit = nkv > 0 ? (nkv + span - 1) / span : 1;
     float* s = (float*)malloc(sizeof(float) * (size_t)(bkv > 0 ? bkv : 1));
+    float* accs = (float*)malloc(sizeof(float) * (size_t)d * (size_t)nsplit);
+    float* ms = (float*)malloc(sizeof(float) * (size_t)nsplit);
+    float* ls = (float*)malloc(sizeof(float) * (size_t)nsplit);
     float* acc = (float*)malloc(sizeof(float) * (size_t)d);
     for (int64_t r = 0; r < nrows; ++r) {
         int64_t i = rows[r];
         int64_t jmax = last_visible(i, nq, nkv, causal);
         float sq = q_scale[i / blk];
-        float m = -INFINITY, l = 0.0f;
+        for (int64_t sp = 0; sp < nsplit; ++sp) {
+            float* a = accs + sp * d;
+            float m = -INFINITY, l = 0.0f;
+            for (int c = 0; c < d; ++c) a[c] = 0.0f;
+            int64_t k_end = (sp + 1) * span - 1 < jmax ? (sp + 1) * span - 1 : jmax;
+            for (int64_t t0 = sp * span; t0 <= k_end; t0 += bkv) {
+                int64_t t1 = t0 + bkv - 1 < k_end ? t0 + bkv - 1 : k_end;
+                int64_t nt = t1 - t0 + 1;
+                float mt = -INFINITY;
+                for (int64_t j = t0; j <= t1; ++j) {
+                    int32_t S = 0;
+                    for (int c = 0; c < d; ++c)
+                        S += (int32_t)qc[i * d + c] * (int32_t)kc[j * d + c];
+                    float comb = sq * k_scale[j / blk];
+                    comb = comb * sm_scale;
+                    float sv = (float)S * comb;
+                    if (delta_s) sv = sv + delta_s[j] * sm_scale;
+                    s[j - t0] = sv;
+                    if (sv > mt) mt = sv;
+                }
+                float mn = m > mt ? m : mt;
+                float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)(m - mn));
+                float psum = 0.0f;
+                for (int c = 0; c < d; ++c) a[c] = alpha * a[c];
+                for (int64_t jj = 0; jj < nt; ++jj) {
+                    float p = (float)exp((double)(s[jj] - mn));
+                    psum = psum + p;
+                    float ph = p_operand(p, p_mode);
+                    if (ph == 0.0f) continue;     /* a zero product leaves acc as is */
+                    const float* vrow = vdec + (t0 + jj) * d;
+                    for (int c = 0; c < d; ++c) a[c] = a[c] + ph * vrow[c];
+                }
+                l = alpha * l + psum;
+                m = mn;
+            }
+            ms[sp] = m;
+            ls[sp] = l;
+        }
+        /* merge the splits */
+        float M = -INFINITY, L = 0.0f;
+        for (int64_t sp = 0; sp < nsplit; ++sp)
+            if (ms[sp] > M) M = ms[sp];
         for (int c = 0; c < d; ++c) acc[c] = 0.0f;
-        for (int64_t t0 = 0; t0 <= jmax; t0 += bkv) {
-            int64_t t1 = t0 + bkv - 1 < jmax ? t0 + bkv - 1 : jmax;
-            int64_t nt = t1 - t0 + 1;
-            float mt = -INFINITY;
-            for (int64_t j = t0; j <= t1; ++j) {
-                int32_t S = 0;
-                for (int c = 0; c < d; ++c) S += (int32_t)qc[i * d + c] * (int32_t)kc[j * d + c];
-                float comb = sq * k_scale[j / blk];
-                comb = comb * sm_scale;
-                float sv = (float)S * comb;
-                if (delta_s) sv = sv + delta_s[j] * sm_scale;
-                s[j - t0] = sv;
-                if (sv > mt) mt = sv;
+        if (M != -INFINITY) {
+            for (int64_t sp = 0; sp < nsplit; ++sp) {
+                if (ms[sp] == -INFINITY) continue;   /* a split without visible keys */
+                float w = (float)exp((double)(ms[sp] - M));
+                L = L + w * ls[sp];
+                for (int c = 0; c < d; ++c) acc[c] = acc[c] + w * accs[sp * d + c];
             }
-            float mn = m > mt ? m : mt;
-            float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)(m - mn));
-            float psum = 0.0f;
-            for (int c = 0; c < d; ++c) acc[c] = alpha * acc[c];
-            for (int64_t jj = 0; jj < nt; ++jj) {
-                float p = (float)exp((double)(s[jj] - mn));
-                psum = psum + p;
-                float ph = p_operand(p, p_mode);
-                if (ph == 0.0f) continue;     /* a zero product leaves acc as is */
-                const float* vrow = vdec + (t0 + jj) * d;
-                for (int c = 0; c < d; ++c) acc[c] = acc[c] + ph * vrow[c];
-            }
-            l = alpha * l + psum;
-            m = mn;
         }
         float* o = out + r * d;
-        if (jmax < 0 || l == 0.0f) {
+        if (jmax < 0 || L == 0.0f) {
             for (int c = 0; c < d; ++c) o[c] = 0.0f;
             if (lse) lse[r] = -INFINITY;
             continue;
         }
         for (int c = 0; c < d; ++c) {
-            float val = (out_scale ? acc[c] * out_scale[c] : acc[c]) / l;
+            float val = (out_scale ? acc[c] * out_scale[c] : acc[c]) / L;
             if (mu_v) val = val + mu_v[c];
             o[c] = val;
         }
-        if (lse) lse[r] = m + logf(l);
+        if (lse) lse[r] = M + logf(L);
     }
     free(s);
+    free(accs);
+    free(ms);
+    free(ls);
     free(acc);
 }
 
@@ -374,7 +409,7 @@ ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
                                      const uint8_t* vc, const float* v_scale,
                                      const float* delta_s, const float* mu_v,
                                      int64_t nq, int64_t nkv, int d, float sm_scale,
-                                     int causal, int bkv, int blk,
+                                     int causal, int bkv, int blk, int64_t split,
                                      const int64_t* rows, int64_t nrows,
                                      float* out, float* lse) {
     /* decode every V code once; dec(v^) is exact in FP32 */
@@ -383,7 +418,7 @@ ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
     for (int64_t j = 0; j < nkv * d; ++j) vdec[j] = orc_e4m3_decode(vc[j]);
     for (int c = 0; c < d; ++c) fac[c] = v_scale[c] / 448.0f;
     recipe_rows(qc, q_scale, kc, k_scale, vdec, fac, P_FP8, delta_s, mu_v, nq, nkv, d, sm_scale,
-                causal, bkv, blk, rows, nrows, out, lse);
+                causal, bkv, blk, split, rows, nrows, out, lse);
     free(vdec);
     free(fac);
 }
@@ -400,14 +435,14 @@ ORC_EXPORT void orc_attn_recipe_half_rows(const int8_t* qc, const float* q_scale
                                           const uint16_t* vh, int bf16,
                                           const float* delta_s, const float* mu_v,
                                           int64_t nq, int64_t nkv, int d, float sm_scale,
-                                          int causal, int bkv, int blk,
+                                          int causal, int bkv, int blk, int64_t split,
                                           const int64_t* rows, int64_t nrows,
                                           float* out, float* lse) {
     float* vdec = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1) * (size_t)d);
     for (int64_t j = 0; j < nkv * d; ++j)
         vdec[j] = bf16 ? orc_bf16_decode(vh[j]) : orc_f16_decode(vh[j]);
     recipe_rows(qc, q_scale, kc, k_scale, vdec, NULL, bf16 ? P_BF16 : P_F16, delta_s, mu_v, nq,
-                nkv, d, sm_scale, causal, bkv, blk, rows, nrows, out, lse);
+                nkv, d, sm_scale, causal, bkv, blk, split, rows, nrows, out, lse);
     free(vdec);
 }
 

@@ -12,7 +12,12 @@
   weights give the plain mean of V, one tile equals the textbook softmax with
   p rounded by numpy's float16 / torch's bfloat16 conversion (library
   routines), its V operand is the input (or v - mu_v rounded by numpy), and it
-  is closer to exact attention than the FP8 recipe.
+  is closer to exact attention than the FP8 recipe;
+* the key range cut into splits and merged (flash-decoding): equal scores
+  give the plain mean of V, the LSE does not depend on the split (l is summed
+  from the FP32 p), the output moves only by the P rounding, and the merge
+  weights follow the splits' maxima (an unweighted merge misses exact
+  attention).
 """
 import math
 
@@ -343,3 +348,71 @@ def test_half_closer_to_exact_than_fp8(orc, d):
         errs[mode] = float(np.abs(out[0] - ex[0]).max())
         assert _cos(out[0], ex[0]) >= (0.9999 if mode == "half" else 0.999)
     assert errs["half"] < 0.5 * errs["fp8"]
+
+
+# ------------------------------------------- split key range (merge) ---
+
+@pytest.mark.parametrize("mode", ["fp8", "half"])
+def test_split_uniform_weights(orc, mode):
+    """Equal scores: every split's p is 1, every merge weight is 1, and o is
+    the plain mean of the (dequantized) V rows."""
+    rng = np.random.default_rng(31)
+    d, n = 64, 700
+    v = _f16(rng.normal(0, 1, (1, 1, n, d)))
+    k = _f16(np.broadcast_to(rng.normal(0, 1, (1, 1, 1, d)), (1, 1, n, d)))
+    q = _f16(rng.normal(0, 1, (1, 1, 3, d)))
+    prob = orc.Problem("f16", "HND", 1, 1, d, [(3, n)], pv_mode=mode, kv_split=256)
+    pre = orc.prepass(prob, q, k, v)
+    out, _ = orc.forward_rows(prob, pre)
+    if mode == "fp8":
+        vq = orc.e4m3_decode(pre.vc[0][0]).astype(np.float64) * pre.vs[0][0]
+    else:
+        vq = orc.decode16(pre.vc[0][0], "f16").astype(np.float64)
+    assert np.max(np.abs(out[0][0] - vq.mean(0))) < 1e-5
+
+
+@pytest.mark.parametrize("mode", ["fp8", "half"])
+@pytest.mark.parametrize("causal,nq,nkv", [(False, 5, 1000), (True, 40, 777), (True, 1, 513)])
+def test_split_lse_is_split_invariant(orc, mode, causal, nq, nkv):
+    """l is summed from the FP32 p, so the merged LSE is the same quantity for
+    any split (up to FP32 rounding), while p^ (hence o) only moves by its own
+    rounding."""
+    rng = np.random.default_rng(32 + nq)
+    d = 128
+    q = _f16(rng.normal(0, 1, (1, 2, nq, d)))
+    k = _f16(rng.normal(0, 1, (1, 1, nkv, d)) + rng.normal(0, 3, (1, 1, 1, d)))
+    v = _f16(rng.normal(0, 1, (1, 1, nkv, d)))
+    base = orc.Problem("f16", "HND", 2, 1, d, [(nq, nkv)], causal=causal, pv_mode=mode)
+    pre = orc.prepass(base, q, k, v)
+    o0, l0 = orc.forward_rows(base, pre)
+    for split in (128, 256, 512):
+        sp = orc.Problem("f16", "HND", 2, 1, d, [(nq, nkv)], causal=causal, pv_mode=mode,
+                         kv_split=split)
+        o1, l1 = orc.forward_rows(sp, pre)
+        fin = np.isfinite(l0[0])
+        assert np.array_equal(fin, np.isfinite(l1[0]))
+        assert np.max(np.abs(l1[0][fin] - l0[0][fin])) < 1e-5 * max(1.0, np.abs(l0[0][fin]).max())
+        bound = 0.05 if mode == "fp8" else 2e-3
+        assert np.max(np.abs(o1[0] - o0[0])) < bound and _cos(o1[0], o0[0]) > 0.9995
+
+
+def test_split_merge_weights_follow_the_maxima(orc):
+    """Split 0 holds keys aligned with the query (large scores), split 1 small
+    ones: the merge must weight the splits by e^(m_s - M).  Equal weights would
+    put half the mass on split 1 and miss exact attention by far."""
+    rng = np.random.default_rng(33)
+    d, n = 64, 512
+    q = rng.normal(0, 1, (1, 1, 2, d))
+    k = rng.normal(0, 0.2, (1, 1, n, d))
+    k[0, 0, :256] += 0.5 * q[0, 0, 0]              # split 0 scores high for row 0
+    v = rng.normal(0, 1, (1, 1, n, d))
+    v[0, 0, 256:] += 3.0                            # split 1's values stand apart
+    qh, kh, vh = _f16(q), _f16(k), _f16(v)
+    for mode in ("fp8", "half"):
+        prob = orc.Problem("f16", "HND", 1, 1, d, [(2, n)], smooth_k=False, sm_scale=1.0,
+                           pv_mode=mode, kv_split=256)
+        out, lse = orc.forward_rows(prob, orc.prepass(prob, qh, kh, vh))
+        ex, ex_lse = orc.exact_rows(prob, qh, kh, vh)
+        assert _cos(out[0][0], ex[0][0]) > 0.999
+        assert np.max(np.abs(out[0][0][0] - ex[0][0][0])) < 0.05
+        assert abs(lse[0][0][0] - ex_lse[0][0][0]) < 1e-3 * max(1.0, abs(ex_lse[0][0][0]))
