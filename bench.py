@@ -16,6 +16,11 @@ Prints ONE JSON line.  Besides the standard fields it carries
 --pv half times the 16-bit P.V variant instead (P and V in the input's type
 on the 16-bit MFMA); its roofline peak is that of the op mix, half INT8 at
 5.0 POPS and half fp16/bf16 at 2.5 PFLOP/s, i.e. 3.33 POPS.
+--kv-split N|auto splits the key range (flash-decoding).  A workload whose
+arithmetic intensity (ops per algorithmic byte of the fused kernel) is below
+the ridge of 5.0 POPS / 8 TB/s is reported against HBM instead: achieved =
+algorithmic bytes (Q, K, V codes and scales, O, split partials written and
+read back) per call / the kernel-only call's time, peak 8 TB/s.
 """
 from __future__ import annotations
 
@@ -31,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TOPS = 5000.0           # MI355X dense INT8 / FP8 MFMA peak (T-ops/s)
 PEAK_16 = 2500.0             # ... dense fp16 / bf16 MFMA peak
+PEAK_HBM = 8000.0            # MI355X HBM3E bandwidth (GB/s)
 WORKLOAD = "causal_gqa"
 
 
@@ -42,6 +48,8 @@ def _parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--pv", choices=("fp8", "half"), default="fp8",
                     help="P.V operands: E4M3 (default) or the input's 16-bit type")
+    ap.add_argument("--kv-split", default="0",
+                    help="keys per split of the key range (multiple of 128), 0 or auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows per query head")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -120,6 +128,21 @@ def cpu_baseline(w, q, k, v, rows_per_head: int, pv: str = "fp8"):
                       f"pairs, {dt:.1f} s wall), pre-pass excluded"}
 
 
+def kernel_bytes(w, pv: str, nsplit: int) -> float:
+    """Algorithmic HBM bytes of one fused-kernel call: the Q, K and V codes
+    and their scales read once, the output written once, and (split key
+    range) the partials written by the kernel and read back by the merge."""
+    ves = 2 if pv == "half" else 1
+    tot = 0.0
+    for nq, nkv in w.seq_lens():
+        tot += w.Hq * nq * w.d * (1 + 2) + w.Hq * math.ceil(nq / 64) * 4      # Q codes, O
+        tot += w.Hkv * nkv * w.d * (1 + ves) + w.Hkv * math.ceil(nkv / 64) * 4
+        tot += 0 if pv == "half" else w.Hkv * w.d * 4                         # V scales
+        if nsplit > 1:
+            tot += 2 * nsplit * w.Hq * nq * (w.d + 2) * 4                     # partials
+    return tot
+
+
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -140,9 +163,10 @@ def main():
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     q, k, v, meta = synth.make_inputs(w, device=dev)
+    kv_split = args.kv_split if args.kv_split == "auto" else int(args.kv_split)
     kw = dict(tensor_layout=w.layout, is_causal=w.causal, smooth_q=w.smooth_q,
               smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale,
-              pv_mode=args.pv)
+              pv_mode=args.pv, kv_split=kv_split)
     o = torch.empty_like(q)
     cu = {}
     if w.varlen:
@@ -199,6 +223,11 @@ def main():
     half = args.pv == "half"
     # half the ops are INT8 Q.K^T, half P.V in the operand type
     peak = PEAK_TOPS if not half else 1.0 / (0.5 / PEAK_TOPS + 0.5 / PEAK_16)
+    split = qa.kv_split_size(desc, cu.get("cu_seqlens_q"), cu.get("cu_seqlens_kv"))
+    max_nkv = max(nkv for _, nkv in w.seq_lens())
+    nsplit = math.ceil(max_nkv / split) if split else 1
+    kbytes = kernel_bytes(w, args.pv, nsplit)
+    hbm_bound = exact / kbytes < peak * 1e12 / (PEAK_HBM * 1e9)
     io = "fp16 io" if w.dtype == "f16" else "bf16 io"
     pvt = ("f16" if w.dtype == "f16" else "bf16") if half else "fp8"
     line = {
@@ -219,10 +248,16 @@ def main():
                                f"{' causal' if w.causal else ''}"
                                f"{', 16-bit P.V' if half else ''}",
                    "global_batch": w.B, "seq_len": w.Nq, "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None if half else measured_traffic(w.name),
-                     "kernel": f"k_attn (fused INT8-QK / softmax / {pvt.upper()}-PV)",
+        "roofline": ({"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+                     if not hbm_bound else
+                     {"bound": "hbm", "achieved": round(kbytes / (kern_ms * 1e-3) / 1e9, 1),
+                      "peak": PEAK_HBM, "unit": "GB/s",
+                      "frac": round(kbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM, 4),
+                      "bytes_per_launch": kbytes}) | {
+                     "traffic": None if half or split else measured_traffic(w.name),
+                     "kernel": f"k_attn (fused INT8-QK / softmax / {pvt.upper()}-PV)"
+                               + (f" + k_merge ({nsplit} splits of {split} keys)" if split else ""),
                      "kernel_ms": round(kern_ms, 4), "ops_per_launch": exact},
         "prepass_ms": round(pre_ms, 4),   # whole call minus the fused kernel
         "exact_pair_tops": round(exact / (ms * 1e-3) / 1e12, 2),

@@ -39,6 +39,14 @@
  *               nearest even into that type), no scale;
  *   p^        = e^(s - m) rounded to nearest even into the same type,
  *   o = sum p^ v / l (+ mu_v), accumulated in FP32 (the MFMA's accumulator).
+ *
+ * A split key range (kv_split != 0; flash-decoding, for few queries against
+ * long key ranges): the keys are cut into splits of kv_split keys, each split
+ * runs the online softmax above from scratch, and the partial results are
+ * merged by the log-sum-exp rule: M = max m_s, w_s = e^(m_s - M),
+ * o = sum w_s acc_s / sum w_s l_s (+ mu_v).  Since p^ is rounded relative to
+ * each split's own running maximum, the split is part of the recipe (the LSE
+ * does not depend on it).
  *   Causal masking is aligned bottom-right: row i sees keys j <= i + Nkv - Nq;
  *   a row that sees no key gives o = 0 and lse = -inf.
  *
@@ -99,6 +107,13 @@ typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1 } sage_dtype;
  * in the input's 16-bit type (the first SageAttention's variant). */
 typedef enum { SAGE_PV_FP8 = 0, SAGE_PV_HALF = 1 } sage_pv_mode;
 
+/* kv_split value that lets the library choose the split: none while the
+ * unsplit grid has at least 256 workgroups; otherwise splits of
+ * max(4, ceil(tiles / ceil(512 / workgroups))) key tiles, where tiles is the
+ * longest key range in SAGE_KV_TILE units (no split if that covers it).  The
+ * choice depends on the problem only; sage_kv_split_size reports it. */
+#define SAGE_KV_SPLIT_AUTO (-1)
+
 /* HND = [batch, heads, tokens, head_dim]; NHD = [batch, tokens, heads, head_dim].
  * Variable-length inputs are packed over the sequences: NHD = [tokens, heads,
  * head_dim], HND = [heads, tokens, head_dim]. */
@@ -125,7 +140,10 @@ typedef struct {
     int32_t smooth_v;        /* 0/1 (SA2-style V smoothing, mean added back)     */
     float sm_scale;          /* <= 0 selects 1/sqrt(head_dim)                     */
     int32_t pv_mode;         /* sage_pv_mode (default SAGE_PV_FP8)                */
-    int32_t reserved[2];     /* must be zero                                      */
+    int32_t kv_split;        /* keys per split of the key range: 0 none (default),
+                                a positive multiple of SAGE_KV_TILE, or
+                                SAGE_KV_SPLIT_AUTO                                */
+    int32_t reserved[1];     /* must be zero                                      */
 } sage_attn_desc;
 
 /* Fill `desc` for a dense, contiguous problem with the API defaults
@@ -180,8 +198,8 @@ SAGE_API sage_status sage_quant_buf_sizes(const sage_attn_desc* desc, const int3
                                  sage_quant_sizes* sizes);
 
 /* Device workspace bytes needed by sage_attn_fwd (varlen = 0) or
- * sage_attn_fwd_varlen (varlen = 1, cu_seqlens given) and by sage_quant_qkv
- * (which needs at most the same). */
+ * sage_attn_fwd_varlen (varlen = 1, cu_seqlens given); sage_quant_qkv and
+ * sage_attn_fwd_quantized need at most the same. */
 SAGE_API sage_status sage_workspace_size(const sage_attn_desc* desc, const int32_t* cu_seqlens_q,
                                 const int32_t* cu_seqlens_kv, int32_t nseq, size_t* bytes);
 
@@ -236,13 +254,27 @@ SAGE_API sage_status sage_attn_fwd_varlen(const sage_attn_desc* desc, const int3
  * cu_seqlens_q == NULL).  Lets a caller quantize K/V once and attend to them
  * many times, and isolates the O(N^2) part for timing (SA1 abstract,
  * llama.cpp discussion #9901: this is where attention spends its time).
- * o and lse as in sage_attn_fwd / sage_attn_fwd_varlen.  Needs no workspace.
+ * o and lse as in sage_attn_fwd / sage_attn_fwd_varlen.  The workspace holds
+ * the split partials and is only used with a split key range (it may then
+ * be any size from sage_workspace_size; otherwise NULL and 0 are accepted).
  */
 SAGE_API sage_status sage_attn_fwd_quantized(const sage_attn_desc* desc,
                                              const int32_t* cu_seqlens_q,
                                              const int32_t* cu_seqlens_kv, int32_t nseq,
                                              const sage_quant_bufs* bufs, void* o, float* lse,
+                                             void* workspace, size_t workspace_bytes,
                                              void* stream);
+
+/*
+ * sage_kv_split_size -- the keys per split the library uses for a problem
+ * (0: no split): the descriptor's kv_split, or the SAGE_KV_SPLIT_AUTO
+ * choice.  Same validation as the compute entry points.  Source: the
+ * llama.cpp discussion #9901 (SA1 abstract) puts attention's cost in long
+ * sequences; the split lets few queries use the whole GPU.
+ */
+SAGE_API sage_status sage_kv_split_size(const sage_attn_desc* desc, const int32_t* cu_seqlens_q,
+                                        const int32_t* cu_seqlens_kv, int32_t nseq,
+                                        int32_t* keys_per_split);
 
 /*
  * sage_debug_qk_int32 -- test hook: the exact int32 Q^.K^^T of the codes in

@@ -10,7 +10,9 @@ raises (there is no CPU or eager fallback).
 mirrors the `sageattn` call of the "sageattention" package page (Quickstart).
 Every entry point takes pv_mode="fp8" (E4M3 P and V, SageAttention2; the
 default) or pv_mode="half" (P and V in the input's 16-bit type, the first
-SageAttention's INT8-QK / 16-bit-PV kernel).
+SageAttention's INT8-QK / 16-bit-PV kernel), and kv_split: 0 (no split of
+the key range), a multiple of 128 keys, or "auto" (the library's rule; see
+kv_split_size).
 """
 from __future__ import annotations
 
@@ -23,7 +25,7 @@ from . import _abi
 from ._abi import BF16, F16, HND, NHD, KV_TILE, QK_BLOCK, SageError, lib
 
 __all__ = ["sageattn", "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_quant_qkv",
-           "sage_attn_fwd_quantized",
+           "sage_attn_fwd_quantized", "kv_split_size",
            "sage_debug_qk_int32", "workspace_size", "quant_buf_sizes", "make_desc",
            "SageError", "lib", "abi_version"]
 
@@ -45,7 +47,7 @@ def _strides(t: torch.Tensor, layout: str, varlen: bool):
 
 def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q=False,
               smooth_k=True, smooth_v=False, sm_scale=None, varlen=False,
-              pv_mode="fp8") -> _abi.Desc:
+              pv_mode="fp8", kv_split=0) -> _abi.Desc:
     """Descriptor for q/k/v torch tensors (dense [B,H,N,d] / [B,N,H,d], or packed
     varlen [T,H,d] / [H,T,d])."""
     if tensor_layout not in ("HND", "NHD"):
@@ -78,6 +80,7 @@ def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q
     d.smooth_v = int(bool(smooth_v))
     d.sm_scale = float(sm_scale) if sm_scale else 0.0
     d.pv_mode = _abi.PV_MODES[pv_mode]
+    d.kv_split = _abi.KV_SPLIT_AUTO if kv_split == "auto" else int(kv_split)
     return d
 
 
@@ -95,6 +98,16 @@ def _stream(t: torch.Tensor):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def kv_split_size(desc, cu_seqlens_q=None, cu_seqlens_kv=None) -> int:
+    """Keys per split the library uses for this problem (0: no split)."""
+    cq, n = _cu(cu_seqlens_q)
+    ck, _ = _cu(cu_seqlens_kv)
+    out = ctypes.c_int32(0)
+    _abi.check("sage_kv_split_size",
+               lib().sage_kv_split_size(ctypes.byref(desc), cq, ck, n, ctypes.byref(out)))
+    return out.value
 
 
 def workspace_size(desc, cu_seqlens_q=None, cu_seqlens_kv=None) -> int:
@@ -123,7 +136,7 @@ _BUF_DT = {"mu_q": torch.float32, "mu_k": torch.float32, "mu_v": torch.float32,
 
 def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
                    smooth_k=True, smooth_v=False, sm_scale=None, cu_seqlens_q=None,
-                   cu_seqlens_kv=None, bufs=None, pv_mode="fp8"):
+                   cu_seqlens_kv=None, bufs=None, pv_mode="fp8", kv_split=0):
     """Run the pre-pass alone; returns a dict of flat device tensors laid out as
     documented for sage_quant_bufs in include/sage.h.  Passing the dict of an
     earlier call on the same problem as `bufs` reuses its buffers and
@@ -131,7 +144,7 @@ def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=Fa
     varlen = cu_seqlens_q is not None
     desc = make_desc(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                     sm_scale=sm_scale, varlen=varlen, pv_mode=pv_mode)
+                     sm_scale=sm_scale, varlen=varlen, pv_mode=pv_mode, kv_split=kv_split)
     if bufs is None:
         sizes = quant_buf_sizes(desc, cu_seqlens_q, cu_seqlens_kv)
         bufs = {name: torch.zeros(max(1, nbytes // torch.empty((), dtype=_BUF_DT[name]).element_size()),
@@ -163,14 +176,18 @@ def quant_bufs_struct(bufs) -> _abi.QuantBufs:
 
 def sage_attn_fwd_quantized(bufs, out, *, cu_seqlens_q=None, cu_seqlens_kv=None, lse=None):
     """The fused kernel alone on buffers from sage_quant_qkv (same problem).
-    `out` has q's shape and dtype; lse (optional) is FP32 as in sage_attn_fwd."""
+    `out` has q's shape and dtype; lse (optional) is FP32 as in sage_attn_fwd.
+    A split key range keeps its partials in the workspace of the pre-pass
+    call (sized by sage_workspace_size, which covers both)."""
     desc = bufs["_desc"]
     cq, n = _cu(cu_seqlens_q)
     ck, _ = _cu(cu_seqlens_kv)
     qb = quant_bufs_struct(bufs)
+    ws = bufs["_workspace"]
     _abi.check("sage_attn_fwd_quantized",
                lib().sage_attn_fwd_quantized(ctypes.byref(desc), cq, ck, n, ctypes.byref(qb),
-                                             _ptr(out), _ptr(lse), _stream(out)))
+                                             _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                             _stream(out)))
     return out
 
 
@@ -196,12 +213,12 @@ def sage_debug_qk_int32(bufs, *, cu_seqlens_q=None, cu_seqlens_kv=None, device=N
 
 def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
                   smooth_k=True, smooth_v=False, sm_scale=None, return_lse=False,
-                  out=None, workspace=None, pv_mode="fp8"):
+                  out=None, workspace=None, pv_mode="fp8", kv_split=0):
     """Dense forward pass.  Returns o (and lse [B, hq, nq] FP32 if asked)."""
     o = torch.empty_like(q) if out is None else out
     desc = make_desc(q, k, v, o, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                     sm_scale=sm_scale, pv_mode=pv_mode)
+                     sm_scale=sm_scale, pv_mode=pv_mode, kv_split=kv_split)
     lse = None
     if return_lse:
         lse = torch.empty((desc.batch, desc.hq, desc.nq), dtype=torch.float32, device=q.device)
@@ -217,13 +234,13 @@ def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=Fal
 def sage_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, tensor_layout="NHD",
                          is_causal=False, smooth_q=False, smooth_k=True, smooth_v=False,
                          sm_scale=None, return_lse=False, out=None, workspace=None,
-                         pv_mode="fp8"):
+                         pv_mode="fp8", kv_split=0):
     """Packed variable-length forward pass (q [T,H,d] for NHD or [H,T,d] for
     HND; cu_seqlens are host int32 prefix offsets).  lse is [hq, T_q]."""
     o = torch.empty_like(q) if out is None else out
     desc = make_desc(q, k, v, o, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                     sm_scale=sm_scale, varlen=True, pv_mode=pv_mode)
+                     sm_scale=sm_scale, varlen=True, pv_mode=pv_mode, kv_split=kv_split)
     cq, n = _cu(cu_seqlens_q)
     ck, nk = _cu(cu_seqlens_kv)
     if nk != n:
@@ -243,8 +260,9 @@ def sage_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, tensor_layout=
 
 
 def sageattn(q, k, v, tensor_layout="HND", is_causal=False, smooth_k=True, sm_scale=None,
-             smooth_q=False, smooth_v=False, return_lse=False, pv_mode="fp8"):
+             smooth_q=False, smooth_v=False, return_lse=False, pv_mode="fp8", kv_split=0):
     """The package page's call: attention output of the quantized forward pass."""
     return sage_attn_fwd(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal,
                          smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                         sm_scale=sm_scale, return_lse=return_lse, pv_mode=pv_mode)
+                         sm_scale=sm_scale, return_lse=return_lse, pv_mode=pv_mode,
+                         kv_split=kv_split)

@@ -17,12 +17,13 @@ STATUS_NAMES = {
 F16, BF16 = 0, 1
 PV_FP8, PV_HALF = 0, 1
 PV_MODES = {"fp8": PV_FP8, "half": PV_HALF}
+KV_SPLIT_AUTO = -1
 HND, NHD = 0, 1
 QK_BLOCK, KV_TILE = 64, 128
 
 EXPORTS = ["sage_desc_init", "sage_quant_buf_sizes", "sage_workspace_size", "sage_quant_qkv",
            "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_attn_fwd_quantized",
-           "sage_debug_qk_int32",
+           "sage_debug_qk_int32", "sage_kv_split_size",
            "sage_status_string", "sage_abi_version"]
 
 
@@ -36,7 +37,7 @@ class Desc(ctypes.Structure):
         ("is_causal", ctypes.c_int32), ("smooth_q", ctypes.c_int32),
         ("smooth_k", ctypes.c_int32), ("smooth_v", ctypes.c_int32),
         ("sm_scale", ctypes.c_float), ("pv_mode", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("kv_split", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
     ]
 
 
@@ -79,7 +80,9 @@ def lib():
                                  ctypes.c_size_t, P]),
         "sage_attn_fwd": (I32, [D, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "sage_attn_fwd_varlen": (I32, [D, ip, ip, I32, P, P, P, P, P, P, ctypes.c_size_t, P]),
-        "sage_attn_fwd_quantized": (I32, [D, ip, ip, I32, ctypes.POINTER(QuantBufs), P, P, P]),
+        "sage_attn_fwd_quantized": (I32, [D, ip, ip, I32, ctypes.POINTER(QuantBufs), P, P, P,
+                                          ctypes.c_size_t, P]),
+        "sage_kv_split_size": (I32, [D, ip, ip, I32, ip]),
         "sage_debug_qk_int32": (I32, [D, ip, ip, I32, ctypes.POINTER(QuantBufs), P, P]),
         "sage_status_string": (ctypes.c_char_p, [I32]),
         "sage_abi_version": (I32, []),

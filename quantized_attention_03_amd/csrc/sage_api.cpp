@@ -31,6 +31,11 @@ struct Plan {
     float sm_scale = 0.0f;
     bool causal = false, smooth_q = false, smooth_k = false, smooth_v = false;
     bool pv_half = false;             // 16-bit P.V operands (SAGE_PV_HALF)
+    int32_t kv_split_req = 0;         // descriptor's kv_split (-1 auto, 0 none, keys)
+    int32_t kv_split = 0;             // effective keys per split (0: no split)
+    int32_t nsplit = 1;               // splits of the longest key range
+    int64_t rows_total = 0;           // lse rows: B*hq*nq, or hq*total_q (varlen)
+    int32_t max_nkv = 0;
 };
 
 // Byte offsets of everything placed in a workspace (quantized tensors first,
@@ -39,8 +44,16 @@ struct Plan {
 struct WsLayout {
     size_t mu_q, mu_k, mu_v, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, delta_s;
     size_t part_q, part_k, part_v, part_vmax, v_amax;
+    size_t split_o, split_ml;         // partials of a split key range
     size_t total;
 };
+
+size_t split_o_bytes(const Plan& p) {
+    return p.kv_split ? (size_t)p.nsplit * p.rows_total * p.d * 4 : 0;
+}
+size_t split_ml_bytes(const Plan& p) {
+    return p.kv_split ? (size_t)p.nsplit * p.rows_total * 8 : 0;
+}
 
 sage_quant_sizes quant_sizes(const Plan& p) {
     sage_quant_sizes z{};
@@ -85,11 +98,25 @@ WsLayout ws_layout(const Plan& p, bool quant_in_ws) {
     w.part_v = take(p.smooth_v ? (size_t)p.rows_k / QBLK * p.hkv * d * 4 : 0);
     w.part_vmax = take(p.pv_half ? 0 : (size_t)p.rows_k / QBLK * p.hkv * d * 4);
     w.v_amax = take(p.pv_half ? 0 : (size_t)p.S * p.hkv * d * 4);
+    w.split_o = take(split_o_bytes(p));
+    w.split_ml = take(split_ml_bytes(p));
     w.total = off + ALIGN;   // slack so that an unaligned base can be rounded up
     return w;
 }
 
+// Workspace of the fused kernel alone (sage_attn_fwd_quantized): only the
+// partials of a split key range.
+WsLayout ws_layout_fused(const Plan& p) {
+    WsLayout w{};
+    w.split_o = 0;
+    w.split_ml = al(split_o_bytes(p));
+    w.total = p.kv_split ? w.split_ml + al(split_ml_bytes(p)) + ALIGN : 0;
+    return w;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+void resolve_split(Plan* p);   // below, after make_params
 
 bool flag_ok(int32_t f) { return f == 0 || f == 1; }
 
@@ -103,7 +130,9 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
     if (D.layout != SAGE_HND && D.layout != SAGE_NHD) return SAGE_ERR_LAYOUT;
     if (!flag_ok(D.is_causal) || !flag_ok(D.smooth_q) || !flag_ok(D.smooth_k) ||
         !flag_ok(D.smooth_v) || (D.pv_mode != SAGE_PV_FP8 && D.pv_mode != SAGE_PV_HALF) ||
-        D.reserved[0] || D.reserved[1] || !std::isfinite(D.sm_scale))
+        !(D.kv_split == SAGE_KV_SPLIT_AUTO || D.kv_split == 0 ||
+          (D.kv_split > 0 && D.kv_split % SAGE_KV_TILE == 0 && D.kv_split <= (1 << 24))) ||
+        D.reserved[0] || !std::isfinite(D.sm_scale))
         return SAGE_ERR_FLAGS;
     if (D.head_dim != 64 && D.head_dim != 96 && D.head_dim != 128) return SAGE_ERR_HEAD_DIM;
     if (D.hq < 1 || D.hkv < 1 || D.hq > 65536 || D.hkv > 65536) return SAGE_ERR_SHAPE;
@@ -128,6 +157,7 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
     p.smooth_k = D.smooth_k;
     p.smooth_v = D.smooth_v;
     p.pv_half = D.pv_mode == SAGE_PV_HALF;
+    p.kv_split_req = D.kv_split;
     p.sm_scale = D.sm_scale > 0.0f ? D.sm_scale : 1.0f / std::sqrt((float)D.head_dim);
     if (varlen) {
         if (cuq[0] != 0 || cuk[0] != 0) return SAGE_ERR_SEQLENS;
@@ -155,7 +185,9 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
         p.rk.push_back(p.rows_k);
         p.rows_q += round_up(p.nq[s], QBLK);
         p.rows_k += round_up(p.nkv[s], KVT);
+        p.max_nkv = std::max(p.max_nkv, p.nkv[s]);
     }
+    p.rows_total = varlen ? (int64_t)p.hq * p.total_q : (int64_t)p.S * p.hq * D.nq;
     // strides: all-zero triple = contiguous in the layout
     const int64_t d = D.head_dim;
     auto fill = [&](const int64_t* in, int heads, int64_t n, Strides* o) {
@@ -177,6 +209,7 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
     fill(D.k_stride, D.hkv, varlen ? tot_k : D.nkv, &p.ks);
     fill(D.v_stride, D.hkv, varlen ? tot_k : D.nkv, &p.vs);
     fill(D.o_stride, D.hq, varlen ? p.total_q : D.nq, &p.os);
+    resolve_split(&p);
     *out = std::move(p);
     return SAGE_OK;
 }
@@ -214,6 +247,9 @@ std::vector<KParams> make_params(const Plan& p) {
     base.ks = p.ks;
     base.vs = p.vs;
     base.os = p.os;
+    base.kv_tiles = p.kv_split / KVT;
+    base.nsplit = p.kv_split ? p.nsplit : 1;
+    base.rows_total = p.rows_total;
     std::vector<KParams> out;
     if (!p.varlen) {
         if (p.S == 0) return out;
@@ -252,6 +288,33 @@ std::vector<KParams> make_params(const Plan& p) {
         out.push_back(k);
     }
     return out;
+}
+
+// The split of the key range.  An explicit kv_split is used as given (no
+// split when it covers the longest key range).  SAGE_KV_SPLIT_AUTO splits
+// only when the unsplit grid has fewer workgroups than MI355X has compute
+// units (256): it then aims at 512 workgroups, with at least 4 key tiles (512
+// keys) per split.  The rule depends on the problem only, never on the device
+// it runs on.
+void resolve_split(Plan* p) {
+    int32_t ks = 0;
+    const int32_t tiles_max = (p->max_nkv + KVT - 1) / KVT;
+    if (p->kv_split_req > 0) {
+        ks = p->kv_split_req;
+    } else if (p->kv_split_req == SAGE_KV_SPLIT_AUTO && tiles_max > 0) {
+        Plan tmp = *p;
+        tmp.kv_split = 0;
+        int64_t base = 0;
+        for (const KParams& P : make_params(tmp)) base += attn_base_wgs(P);
+        if (base > 0 && base < 256) {
+            const int64_t want = (512 + base - 1) / base;
+            const int32_t tps = std::max<int32_t>(4, (int32_t)((tiles_max + want - 1) / want));
+            ks = tps * KVT;
+        }
+    }
+    if (ks >= p->max_nkv) ks = 0;   // one split: the plain kernel
+    p->kv_split = ks;
+    p->nsplit = ks ? (p->max_nkv + ks - 1) / ks : 1;
 }
 
 // Blocks of a launch over (head, 64-token chunk) pairs for one table.
@@ -381,6 +444,37 @@ sage_quant_bufs bufs_in_ws(const Plan& p, uint8_t* ws, const WsLayout& w) {
     return b;
 }
 
+// The fused kernel over every parameter block, then (split key range) the
+// merge of the partials.
+sage_status run_attn(const Plan& p, std::vector<KParams> kp, int dtype, const sage_quant_bufs& b,
+                     const float* ds, const float* mu_v, void* o, float* lse, float* part_o,
+                     float* part_ml, hipStream_t st) {
+    for (KParams& P : kp) {
+        P.part_o = part_o;
+        P.part_ml = part_ml;
+        SAGE_TRY(launch_attn(P, dtype, b.q_codes, b.q_scale, b.k_codes, b.k_scale, b.v_codes,
+                             b.v_scale, ds, mu_v, o, lse, st));
+    }
+    if (p.kv_split && p.rows_total > 0) {
+        MergeArgs m{};
+        m.part_o = part_o;
+        m.part_ml = part_ml;
+        m.rows_total = p.rows_total;
+        m.nsplit = p.nsplit;
+        m.d = p.d;
+        m.hq = p.hq;
+        m.nq = p.varlen ? 0 : p.nq[0];
+        m.varlen = p.varlen;
+        m.total_q = p.total_q;
+        m.poff = p.pv_half ? 0.0f : (float)std::log2(448.0);
+        m.os = p.os;
+        m.o = o;
+        m.lse = lse;
+        SAGE_TRY(launch_merge(m, dtype, st));
+    }
+    return SAGE_OK;
+}
+
 sage_status forward(const sage_attn_desc* desc, const int32_t* cuq, const int32_t* cuk,
                     int32_t nseq, bool varlen, const void* q, const void* k, const void* v,
                     void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
@@ -401,10 +495,10 @@ sage_status forward(const sage_attn_desc* desc, const int32_t* cuq, const int32_
     const sage_quant_bufs b = bufs_in_ws(p, base, w);
     const std::vector<KParams> kp = make_params(p);
     if ((e = run_prepass(p, kp, desc->dtype, q, k, v, b, base, w, st)) != SAGE_OK) return e;
-    for (const KParams& P : kp)
-        SAGE_TRY(launch_attn(P, desc->dtype, b.q_codes, b.q_scale, b.k_codes, b.k_scale,
-                             b.v_codes, b.v_scale, b.delta_s, b.mu_v, o, lse, st));
-    return SAGE_OK;
+    return run_attn(p, kp, desc->dtype, b, p.smooth_q ? b.delta_s : nullptr,
+                    p.smooth_v ? b.mu_v : nullptr, o, lse,
+                    reinterpret_cast<float*>(base + w.split_o),
+                    reinterpret_cast<float*>(base + w.split_ml), st);
 }
 
 }  // namespace
@@ -492,7 +586,8 @@ sage_status sage_attn_fwd_varlen(const sage_attn_desc* desc, const int32_t* cuq,
 
 sage_status sage_attn_fwd_quantized(const sage_attn_desc* desc, const int32_t* cuq,
                                     const int32_t* cuk, int32_t nseq, const sage_quant_bufs* b,
-                                    void* o, float* lse, void* stream) {
+                                    void* o, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream) {
     Plan p;
     sage_status e = make_plan(desc, cuq, cuk, nseq, cuq != nullptr, &p);
     if (e != SAGE_OK) return e;
@@ -507,13 +602,26 @@ sage_status sage_attn_fwd_quantized(const sage_attn_desc* desc, const int32_t* c
     for (const void* ptr : ptrs)
         if (!aligned16(ptr)) return SAGE_ERR_ALIGN;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return SAGE_ERR_ALIGN;
+    const WsLayout w = ws_layout_fused(p);
+    if (!empty && w.total > 0 && !ws) return SAGE_ERR_NULL;
+    if (!empty && ws_bytes < w.total) return SAGE_ERR_WORKSPACE;
     if ((e = check_arch()) != SAGE_OK) return e;
     if (empty) return SAGE_OK;
-    for (const KParams& P : make_params(p))
-        SAGE_TRY(launch_attn(P, desc->dtype, b->q_codes, b->q_scale, b->k_codes, b->k_scale,
-                             b->v_codes, b->v_scale, p.smooth_q ? b->delta_s : nullptr,
-                             p.smooth_v ? b->mu_v : nullptr, o, lse,
-                             static_cast<hipStream_t>(stream)));
+    uint8_t* base = w.total ? align_up(ws) : nullptr;
+    return run_attn(p, make_params(p), desc->dtype, *b, p.smooth_q ? b->delta_s : nullptr,
+                    p.smooth_v ? b->mu_v : nullptr, o, lse,
+                    base ? reinterpret_cast<float*>(base + w.split_o) : nullptr,
+                    base ? reinterpret_cast<float*>(base + w.split_ml) : nullptr,
+                    static_cast<hipStream_t>(stream));
+}
+
+sage_status sage_kv_split_size(const sage_attn_desc* desc, const int32_t* cuq,
+                               const int32_t* cuk, int32_t nseq, int32_t* keys_per_split) {
+    if (!keys_per_split) return SAGE_ERR_NULL;
+    Plan p;
+    const sage_status e = make_plan(desc, cuq, cuk, nseq, cuq != nullptr, &p);
+    if (e != SAGE_OK) return e;
+    *keys_per_split = p.kv_split;
     return SAGE_OK;
 }
 
@@ -530,7 +638,9 @@ sage_status sage_debug_qk_int32(const sage_attn_desc* desc, const int32_t* cuq,
     if ((e = check_arch()) != SAGE_OK) return e;
     std::vector<int64_t> gbase(p.S + 1, 0);
     for (int s = 0; s < p.S; ++s) gbase[s + 1] = gbase[s] + (int64_t)p.hq * p.nq[s] * p.nkv[s];
-    for (const KParams& P : make_params(p)) {
+    for (KParams P : make_params(p)) {
+        P.kv_tiles = 0;           // the dump covers every key of every row
+        P.nsplit = 1;
         DumpBase db{};
         if (!P.tab.uniform)
             for (int j = 0; j < P.tab.n; ++j) db.base[j] = gbase[P.tab.sid[j]];

@@ -188,7 +188,10 @@ struct Work {
     int s;                    // index of the sequence in the launch's table
     int hkv, head, q0;        // q0 = first query row of this wave
     int head0, hpw;           // first query head of the workgroup, heads per workgroup
-    int nt_wg, nt_w;          // key tiles needed by the workgroup / by this wave
+    int t0;                   // first key tile of the workgroup's split (0 unsplit)
+    int nt_wg, nt_w;          // end (exclusive) of the key tiles of the workgroup /
+                              // of this wave; tiles t0 .. end-1 are processed
+    int split;                // split index of the key range (0 unsplit)
 };
 
 template <int WAVES>
@@ -206,12 +209,16 @@ __device__ inline Work decode_work(const KParams& P) {
     const int nhg = P.group / hpw;
     int local;
     auto per = [&](int s) {
-        return wg_count<WAVES>(P, P.tab.uniform ? P.tab.nq[0] : P.tab.nq[s]);
+        return wg_count<WAVES>(P, P.tab.uniform ? P.tab.nq[0] : P.tab.nq[s]) * P.nsplit;
     };
     const int s = find_seq(P, blockIdx.x, per, &local);
     w.s = s;
     w.si = seq_info(P, s);
     const int nq = w.si.nq, nkv = w.si.nkv;
+    // a split key range: the split index is the slowest
+    const int base = wg_count<WAVES>(P, nq);
+    w.split = local / base;
+    local %= base;
     // kv head fastest (consecutive workgroups land on different XCDs), then the
     // head group, then query tiles from the heaviest (last) to the lightest
     w.hkv = local % P.hkv;
@@ -236,6 +243,13 @@ __device__ inline Work decode_work(const KParams& P) {
         w.nt_w = end_w > 0 ? (end_w + KVT - 1) / KVT : 0;
     } else {
         w.nt_w = 0;
+    }
+    w.t0 = 0;
+    if (P.kv_tiles > 0) {
+        w.t0 = w.split * P.kv_tiles;
+        const int t1 = w.t0 + P.kv_tiles;
+        w.nt_wg = min(w.nt_wg, t1);
+        w.nt_w = min(w.nt_w, t1);
     }
     return w;
 }
@@ -538,7 +552,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
 
     v4i qf[D / 32];
     float sq = 0.0f;
-    if (w.nt_w > 0) {
+    if (w.nt_w > w.t0) {
         const int64_t qrow0 = si.rq * P.hq + (int64_t)w.head * si.npq;
         load_q<D>(qc + (qrow0 + my_q) * D, qf);
         sq = qsc[qrow0 / QBLK + w.q0 / QBLK];
@@ -563,9 +577,10 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     DmaOffsets<D, FWD_NT, PVH> off;
     off.init(si.npk);
 
-    // stage tile 0 (K and bias) with every wave, then offset group 1
-    if (w.nt_wg > 0)
-        stage_k<D, FWD_NT, HAS_DS, PVH>(kst0, dst0, off, kbase, dsb, si.npk, 0, w.hpw);
+    // stage the first tile (K and bias) with every wave, then offset group 1.
+    // Stage buffers are chosen by the tile's place r = t - t0 in the split.
+    if (w.nt_wg > w.t0)
+        stage_k<D, FWD_NT, HAS_DS, PVH>(kst0, dst0, off, kbase, dsb, si.npk, w.t0, w.hpw);
     bar();
     if (grp == 1) bar();
 
@@ -578,41 +593,42 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
 #pragma unroll
     for (int i = 0; i < (PVH ? 8 : 1); ++i) ph[i] = v4i{0, 0, 0, 0};
     // acc += V(t)^T . P^(t)^T in either operand type
-    auto pv = [&](int tt) {
-        const uint8_t* vs_ = vst0 + (tt & 1) * T::VBYTES;
+    auto pv = [&](int rr) {   // rr: the tile's place in the split
+        const uint8_t* vs_ = vst0 + (rr & 1) * T::VBYTES;
         if constexpr (PVH) pv_tile_h<D, DT>(vs_, ph, acc);
         else pv_tile<D>(vs_, pb, acc);
     };
     v16i sacc[4];
     float alpha_prev = 1.0f;   // rescale owed to acc before its next P.V
 
-    for (int t = 0; t < w.nt_wg; ++t) {
+    for (int t = w.t0; t < w.nt_wg; ++t) {
+        const int r = t - w.t0;
         // ---- MFMA phase ----
         __builtin_amdgcn_s_setprio(2);
         if (t + 1 < w.nt_wg)
-            stage_k<D, FWD_NT, HAS_DS, PVH>(kst0 + ((t + 1) & 1) * T::KBYTES,
-                                            dst0 + ((t + 1) % 3) * T::DSBYTES, off, kbase, dsb,
+            stage_k<D, FWD_NT, HAS_DS, PVH>(kst0 + ((r + 1) & 1) * T::KBYTES,
+                                            dst0 + ((r + 1) % 3) * T::DSBYTES, off, kbase, dsb,
                                             si.npk, t + 1, w.hpw);
-        stage_v<D, FWD_NT, PVH>(vst0 + (t & 1) * T::VBYTES, off, vbase, si.npk, t);
+        stage_v<D, FWD_NT, PVH>(vst0 + (r & 1) * T::VBYTES, off, vbase, si.npk, t);
         if (t < w.nt_w) {
             if constexpr (PVH) {
                 // P.V first: the 16-bit P^ then dies before S(t) is formed
-                if (t > 0) {
+                if (r > 0) {
                     rescale<D>(acc, alpha_prev);
-                    pv(t - 1);
+                    pv(r - 1);
                 }
-                qk_tile<D>(kst0 + (t & 1) * T::KBYTES, qf, sacc);
+                qk_tile<D>(kst0 + (r & 1) * T::KBYTES, qf, sacc);
             } else {
-                qk_tile<D>(kst0 + (t & 1) * T::KBYTES, qf, sacc);
-                if (t > 0) {
+                qk_tile<D>(kst0 + (r & 1) * T::KBYTES, qf, sacc);
+                if (r > 0) {
                     rescale<D>(acc, alpha_prev);
-                    pv(t - 1);
+                    pv(r - 1);
                 }
             }
-        } else if (t == w.nt_w && t > 0) {
+        } else if (t == w.nt_w && r > 0) {
             // this wave's rows are done: flush its last tile
             rescale<D>(acc, alpha_prev);
-            pv(t - 1);
+            pv(r - 1);
         }
         // the tile's score scales, loaded ahead of the softmax phase (the
         // empty asm keeps the compiler from sinking the loads past the barrier)
@@ -627,7 +643,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         // ---- softmax phase ----
         if (t < w.nt_w) {
             const int kt0 = t * KVT + 16 * h;     // key of sacc[b][r] = kt0 + 32b + r
-            const float* dsl = HAS_DS ? reinterpret_cast<const float*>(dst0 + (t % 3) * T::DSBYTES) +
+            const float* dsl = HAS_DS ? reinterpret_cast<const float*>(dst0 + (r % 3) * T::DSBYTES) +
                                             (w.head - w.head0) * KVT
                                       : nullptr;
             const bool need_mask =
@@ -645,9 +661,9 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         }
         bar();
     }
-    if (w.nt_w > 0 && w.nt_w == w.nt_wg) {
+    if (w.nt_w > w.t0 && w.nt_w == w.nt_wg) {
         rescale<D>(acc, alpha_prev);
-        pv(w.nt_wg - 1);
+        pv(w.nt_wg - 1 - w.t0);
     }
     if (grp == 0) bar();   // balance group 1's leading barrier
 
@@ -656,6 +672,35 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     // granules XOR-swizzled by row) and then written as whole rows, 16 bytes
     // per lane.
     const float l_tot = swap_sum(l_run);
+    if (P.kv_tiles > 0) {
+        // split key range: this split's partial of each row, unnormalised:
+        // acc*v_scale + mu_v*l (the mean then comes out of the merge's
+        // division by the total l), with m (log2 units) and l
+        if (my_q < nq) {
+            const int64_t row = si.lse0 + (int64_t)w.head * P.lse_hstride + my_q;
+            const int64_t pr = (int64_t)w.split * P.rows_total + row;
+            const int64_t vsb = ((int64_t)si.sid * P.hkv + w.hkv) * D;
+            const bool add_mu = mu_v && l_tot > 0.0f;
+            float* po = P.part_o + pr * D;
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int ch0 = 32 * c + 8 * r4 + 4 * h;
+                    const float4 s4 = PVH ? make_float4(1.f, 1.f, 1.f, 1.f)
+                                          : *reinterpret_cast<const float4*>(vsc + vsb + ch0);
+                    const float4 m4 = add_mu ? *reinterpret_cast<const float4*>(mu_v + vsb + ch0)
+                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+                    *reinterpret_cast<float4*>(po + ch0) =
+                        make_float4(fmaf(acc[c][4 * r4], s4.x, m4.x * l_tot),
+                                    fmaf(acc[c][4 * r4 + 1], s4.y, m4.y * l_tot),
+                                    fmaf(acc[c][4 * r4 + 2], s4.z, m4.z * l_tot),
+                                    fmaf(acc[c][4 * r4 + 3], s4.w, m4.w * l_tot));
+                }
+            if (h == 0) *reinterpret_cast<float2*>(P.part_ml + 2 * pr) = make_float2(m_run, l_tot);
+        }
+        return;
+    }
     constexpr int RS = D == 64 ? 128 : 256;    // LDS bytes per staged row
     constexpr int NGR = RS / 16;               // granules per staged row
     static_assert(FWD_WAVES * 32 * RS <= 2 * T::KBYTES + 2 * T::VBYTES, "staging fits the stages");
@@ -798,7 +843,7 @@ hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const in
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int nblocks = wg_count_host(P, FWD_WAVES);
+    const int nblocks = wg_count_host(P, FWD_WAVES) * P.nsplit;
     if (nblocks <= 0) return hipSuccess;
     k_attn<D, DT, HAS_DS, PVH><<<nblocks, FWD_NT, lds_bytes<D, HAS_DS, PVH>(), st>>>(
         P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, static_cast<uint16_t*>(o), lse);
@@ -841,6 +886,75 @@ hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, 
         k_qk_dump<96><<<nblocks, WG, Tile<96>::KBYTES, st>>>(P, qc, kc, s_out, db);
     else
         k_qk_dump<128><<<nblocks, WG, Tile<128>::KBYTES, st>>>(P, qc, kc, s_out, db);
+    return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Merge of a split key range (flash-decoding): per row, M = max m_s,
+// w_s = 2^(m_s - M), L = sum w_s l_s, o = sum w_s part_s / L, the partials
+// already holding acc*v_scale + mu_v*l.  One thread per 8 channels of a row.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
+    const int gpr = M.d / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / gpr;
+    if (row >= M.rows_total) return;
+    const int c0 = (int)(gid % gpr) * 8;
+    float mx = -INFINITY;
+    for (int sp = 0; sp < M.nsplit; ++sp)
+        mx = fmaxf(mx, M.part_ml[2 * ((int64_t)sp * M.rows_total + row)]);
+    float L = 0.0f, a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = 0.0f;
+    if (mx != -INFINITY) {
+        for (int sp = 0; sp < M.nsplit; ++sp) {
+            const int64_t pr = (int64_t)sp * M.rows_total + row;
+            const float2 ml = *reinterpret_cast<const float2*>(M.part_ml + 2 * pr);
+            if (ml.x == -INFINITY) continue;     // a split without visible keys
+            const float wgt = __builtin_amdgcn_exp2f(ml.x - mx);
+            L = fmaf(wgt, ml.y, L);
+            const float4 p0 = *reinterpret_cast<const float4*>(M.part_o + pr * M.d + c0);
+            const float4 p1 = *reinterpret_cast<const float4*>(M.part_o + pr * M.d + c0 + 4);
+            a[0] = fmaf(wgt, p0.x, a[0]);
+            a[1] = fmaf(wgt, p0.y, a[1]);
+            a[2] = fmaf(wgt, p0.z, a[2]);
+            a[3] = fmaf(wgt, p0.w, a[3]);
+            a[4] = fmaf(wgt, p1.x, a[4]);
+            a[5] = fmaf(wgt, p1.y, a[5]);
+            a[6] = fmaf(wgt, p1.z, a[6]);
+            a[7] = fmaf(wgt, p1.w, a[7]);
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    uint32_t bits[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bits[e] = f2h_bits<DT>(a[e] * inv);
+    int64_t off;
+    if (M.varlen) {
+        const int64_t h = row / M.total_q, tok = row % M.total_q;
+        off = tok * M.os.n + h * M.os.h;
+    } else {
+        const int64_t per_seq = (int64_t)M.hq * M.nq;
+        const int64_t sidx = row / per_seq, rem = row % per_seq;
+        off = sidx * M.os.b + (rem / M.nq) * M.os.h + (rem % M.nq) * M.os.n;
+    }
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(M.o) + off + c0) =
+        make_uint4(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16),
+                   bits[4] | (bits[5] << 16), bits[6] | (bits[7] << 16));
+    if (c0 == 0 && M.lse)
+        M.lse[row] = L > 0.0f ? (mx + __log2f(L) - M.poff) * LN2 : -INFINITY;
+}
+
+int attn_base_wgs(const KParams& P) { return wg_count_host(P, FWD_WAVES); }
+
+hipError_t launch_merge(const MergeArgs& M, int dtype, hipStream_t st) {
+    const int64_t threads = M.rows_total * (M.d / 8);
+    if (threads <= 0) return hipSuccess;
+    const int64_t nb = (threads + 255) / 256;
+    if (dtype == 0) k_merge<0><<<(unsigned)nb, 256, 0, st>>>(M);
+    else k_merge<1><<<(unsigned)nb, 256, 0, st>>>(M);
     return hipGetLastError();
 }
 

@@ -39,7 +39,29 @@ struct KParams {
     float sml2;                         // sm_scale * log2(e)
     Strides qs, ks, vs, os;
     int64_t lse_hstride;                // elements between heads of lse
+    // split key range (flash-decoding): kv_tiles key tiles per split (0: no
+    // split), nsplit splits per sequence in the grid; each workgroup writes
+    // its rows' partial (acc*v_scale + mu_v*l, m, l) at part_o / part_ml,
+    // split-major over rows_total rows (the lse row index)
+    int32_t kv_tiles, nsplit;
+    int64_t rows_total;
+    float* part_o;                      // [nsplit][rows_total][d]
+    float* part_ml;                     // [nsplit][rows_total][2]: m (log2 units), l
     SeqTab tab;
+};
+
+// The merge of the split partials into the output (and lse).
+struct MergeArgs {
+    const float* part_o;
+    const float* part_ml;
+    int64_t rows_total;
+    int32_t nsplit, d, hq, nq;          // nq: dense tokens per sequence
+    int32_t varlen;
+    int64_t total_q;                    // varlen: packed query tokens
+    float poff;                         // log2 of the P scale folded into l (448 or 1)
+    Strides os;
+    void* o;
+    float* lse;
 };
 
 struct SeqInfo {
@@ -156,6 +178,9 @@ hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const floa
                        const int8_t* kc, const float* ksc, const uint8_t* vc,
                        const float* vsc, const float* ds, const float* mu_v, void* o,
                        float* lse, hipStream_t st);
+// Workgroups of one fused-kernel launch before any key split.
+int attn_base_wgs(const KParams& P);
+hipError_t launch_merge(const MergeArgs& M, int dtype, hipStream_t st);
 struct DumpBase {
     int64_t base[MAXSEQ];               // first element of sequence s in the dump
 };

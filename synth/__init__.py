@@ -181,6 +181,9 @@ WORKLOADS = {
                            causal=True, seed=4, k_off_sigma=3.0,
                            seqlens_q=[a for a, _ in C5_LENS],
                            seqlens_kv=[b for _, b in C5_LENS]),
+    # one new query per sequence against a 32K-token context (decode)
+    "decode_gqa": Workload("decode_gqa", "f16", "HND", 8, 32, 8, 1, 32768, 128,
+                           causal=True, seed=5, k_off_sigma=3.0),
 }
 
 # tensor ids inside one seed

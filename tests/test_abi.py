@@ -24,7 +24,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     L = qa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -65,7 +65,7 @@ def _ws(d, cuq=None, cuk=None, n=0):
 def test_desc_init_defaults():
     d = _desc()
     assert (d.smooth_k, d.smooth_q, d.smooth_v, d.is_causal, d.sm_scale) == (1, 0, 0, 0, 0.0)
-    assert d.pv_mode == _abi.PV_FP8 and tuple(d.reserved) == (0, 0)
+    assert d.pv_mode == _abi.PV_FP8 and d.kv_split == 0 and tuple(d.reserved) == (0,)
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -81,6 +81,8 @@ def test_desc_init_defaults():
     ("hq", 7, "SAGE_ERR_GQA"),
     ("pv_mode", 2, "SAGE_ERR_FLAGS"),
     ("pv_mode", -1, "SAGE_ERR_FLAGS"),
+    ("kv_split", 100, "SAGE_ERR_FLAGS"),
+    ("kv_split", -2, "SAGE_ERR_FLAGS"),
 ])
 def test_descriptor_errors(field, value, status):
     d = _desc(**{field: value})
@@ -90,7 +92,7 @@ def test_descriptor_errors(field, value, status):
 
 def test_reserved_and_nan_scale_rejected():
     d = _desc()
-    d.reserved[1] = 5
+    d.reserved[0] = 5
     assert _abi.STATUS_NAMES[_fwd(d)] == "SAGE_ERR_FLAGS"
     d = _desc(sm_scale=float("nan"))
     assert _abi.STATUS_NAMES[_fwd(d)] == "SAGE_ERR_FLAGS"
@@ -180,6 +182,39 @@ def test_half_pv_sizes():
         st, wf8 = _ws(_desc(smooth_v=sv))
         st2, wh = _ws(_desc(smooth_v=sv, pv_mode=_abi.PV_HALF))
         assert st == st2 == 0 and wh <= wf8 + B * hkv * npk * dd
+
+
+def _split(d, cuq=None, cuk=None, n=0):
+    out = ctypes.c_int32(-7)
+    st = qa.lib().sage_kv_split_size(ctypes.byref(d), cuq, cuk, n, ctypes.byref(out))
+    return _abi.STATUS_NAMES[st], out.value
+
+
+def test_kv_split_rule():
+    """Explicit splits are used as given unless they cover the longest key
+    range; the automatic rule splits only grids below 256 workgroups."""
+    assert _split(_desc(nkv=1000, kv_split=256)) == ("SAGE_OK", 256)
+    assert _split(_desc(nkv=1000, kv_split=1024)) == ("SAGE_OK", 0)
+    assert _split(_desc(nkv=1000)) == ("SAGE_OK", 0)
+    # decode: B=2, hq=8 (group 4 -> one workgroup per kv head), nq=1:
+    # 2 * 2 workgroups, so ceil(512 / 4) = 128 splits wanted, at least 4
+    # tiles each: 32768 keys = 256 tiles -> 4 tiles = 512 keys
+    assert _split(_desc(nq=1, nkv=32768, kv_split=-1)) == ("SAGE_OK", 512)
+    # 16 tiles in all: max(4, ceil(16 / 128)) = 4 tiles
+    assert _split(_desc(nq=1, nkv=2048, kv_split=-1)) == ("SAGE_OK", 512)
+    # a prefill grid (well over 256 workgroups) is not split
+    assert _split(_desc(batch=4, hq=32, hkv=32, nq=4096, nkv=4096, kv_split=-1)) == ("SAGE_OK", 0)
+    # keys that fit one split: no split
+    assert _split(_desc(nq=1, nkv=300, kv_split=-1)) == ("SAGE_OK", 0)
+    assert _split(_desc(kv_split=96))[0] == "SAGE_ERR_FLAGS"
+
+
+def test_split_workspace_holds_the_partials():
+    base = _ws(_desc(nq=4, nkv=4096))
+    sp = _ws(_desc(nq=4, nkv=4096, kv_split=512))
+    rows, nsplit, d = 2 * 8 * 4, 8, 128              # B*hq*nq rows, 4096/512 splits
+    assert base[0] == sp[0] == 0
+    assert sp[1] - base[1] >= nsplit * rows * (d + 2) * 4
 
 
 def test_empty_problem_is_a_no_op():
