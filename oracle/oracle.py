@@ -172,7 +172,8 @@ def qk_int32(qc, kc) -> np.ndarray:
     return s
 
 
-def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, rows, split=0):
+def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, rows, split=0,
+                     blk=BLK):
     qc, kc, vc = _c(qc, np.int8), _c(kc, np.int8), _c(vc, np.uint8)
     nq, d = qc.shape
     nkv = kc.shape[0]
@@ -183,13 +184,13 @@ def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, ro
         _p(qc), _p(_c(qs, np.float32)), _p(kc), _p(_c(ks, np.float32)), _p(vc),
         _p(_c(vs, np.float32)), _p(None if ds is None else _c(ds, np.float32)),
         _p(None if mu_v is None else _c(mu_v, np.float32)), nq, nkv, d,
-        float(sm_scale), int(causal), int(bkv), BLK, int(split), _p(rows), rows.size, _p(out),
-        _p(lse))
+        float(sm_scale), int(causal), int(bkv), int(blk), int(split), _p(rows), rows.size,
+        _p(out), _p(lse))
     return out, lse
 
 
 def attn_recipe_half_rows(qc, qs, kc, ks, vh, dtype, ds, mu_v, sm_scale, causal, bkv, rows,
-                          split=0):
+                          split=0, blk=BLK):
     """The 16-bit P.V variant: vh [nkv, d] fp16/bf16 bit patterns of the V
     operand; p^ is p rounded to the same type."""
     qc, kc, vh = _c(qc, np.int8), _c(kc, np.int8), _c(vh, np.uint16)
@@ -202,8 +203,8 @@ def attn_recipe_half_rows(qc, qs, kc, ks, vh, dtype, ds, mu_v, sm_scale, causal,
         _p(qc), _p(_c(qs, np.float32)), _p(kc), _p(_c(ks, np.float32)), _p(vh),
         1 if dtype == "bf16" else 0, _p(None if ds is None else _c(ds, np.float32)),
         _p(None if mu_v is None else _c(mu_v, np.float32)), nq, nkv, d,
-        float(sm_scale), int(causal), int(bkv), BLK, int(split), _p(rows), rows.size, _p(out),
-        _p(lse))
+        float(sm_scale), int(causal), int(bkv), int(blk), int(split), _p(rows), rows.size,
+        _p(out), _p(lse))
     return out, lse
 
 
@@ -238,15 +239,17 @@ class Problem:
     sm_scale: float | None = None
     pv_mode: str = "fp8"        # "fp8" (SageAttention2) | "half" (16-bit P.V)
     kv_split: int = 0           # keys per split of the key range (0: one split)
+    qk_block: int = BLK         # tokens per Q/K quantization block (64, or 32)
 
     @property
     def scale(self) -> float:
         return self.sm_scale if self.sm_scale else 1.0 / math.sqrt(self.d)
 
 
-def problem_from_workload(w, pv_mode: str = "fp8", kv_split: int = 0) -> Problem:
+def problem_from_workload(w, pv_mode: str = "fp8", kv_split: int = 0,
+                          qk_block: int = BLK) -> Problem:
     return Problem(w.dtype, w.layout, w.Hq, w.Hkv, w.d, w.seq_lens(), w.varlen, w.causal,
-                   w.smooth_q, w.smooth_k, w.smooth_v, w.sm_scale, pv_mode, kv_split)
+                   w.smooth_q, w.smooth_k, w.smooth_v, w.sm_scale, pv_mode, kv_split, qk_block)
 
 
 def split_heads(prob: Problem, x, which: str):
@@ -285,9 +288,9 @@ class Prepass:
     mu_k: list = field(default_factory=list)     # [Hkv, d] FP32 or None
     mu_v: list = field(default_factory=list)     # [Hkv, d] FP32 or None
     qc: list = field(default_factory=list)       # [Hq, nq, d] int8
-    qs: list = field(default_factory=list)       # [Hq, ceil(nq/64)] FP32
+    qs: list = field(default_factory=list)       # [Hq, ceil(nq/qk_block)] FP32
     kc: list = field(default_factory=list)       # [Hkv, nkv, d] int8
-    ks: list = field(default_factory=list)       # [Hkv, ceil(nkv/64)] FP32
+    ks: list = field(default_factory=list)       # [Hkv, ceil(nkv/qk_block)] FP32
     vc: list = field(default_factory=list)       # [Hkv, nkv, d] e4m3 bytes, or
                                                  # 16-bit patterns (pv_mode "half")
     vs: list = field(default_factory=list)       # [Hkv, d] FP32 (None for "half")
@@ -307,7 +310,7 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
         mu_k = channel_mean(kf) if prob.smooth_k else None
         mu_v = channel_mean(vf) if prob.smooth_v else None
         k_s = smooth(kf, mu_k)
-        kc, ks = quant_int8_blocks(k_s)
+        kc, ks = quant_int8_blocks(k_s, prob.qk_block)
         if prob.pv_mode == "half":
             # the V operand stays 16-bit: v (or v - mu_v rounded to the type)
             vc, vs = encode16(smooth(vf, mu_v), prob.dtype), None
@@ -319,7 +322,7 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
         s, h = u
         qf = decode16(qh[s][h], prob.dtype)
         mu_q = channel_mean(qf) if prob.smooth_q else None
-        qc, qs = quant_int8_blocks(smooth(qf, mu_q))
+        qc, qs = quant_int8_blocks(smooth(qf, mu_q), prob.qk_block)
         ds = delta_s(mu_q, k_s) if prob.smooth_q else None
         return mu_q, qc, qs, ds
 
@@ -362,10 +365,11 @@ def forward_rows(prob: Problem, pre: Prepass, rows=None, bkv: int = 128,
         if prob.pv_mode == "half":
             return attn_recipe_half_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk],
                                          pre.ks[s][hk], pre.vc[s][hk], prob.dtype, ds, mu_v,
-                                         prob.scale, prob.causal, bkv, r, prob.kv_split)
+                                         prob.scale, prob.causal, bkv, r, prob.kv_split,
+                                         prob.qk_block)
         return attn_recipe_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk], pre.ks[s][hk],
                                 pre.vc[s][hk], pre.vs[s][hk], ds, mu_v,
-                                prob.scale, prob.causal, bkv, r, prob.kv_split)
+                                prob.scale, prob.causal, bkv, r, prob.kv_split, prob.qk_block)
 
     with ThreadPoolExecutor(max_workers=threads or os.cpu_count()) as ex:
         res = list(ex.map(one, units))

@@ -24,7 +24,7 @@ import torch
 from . import _abi
 from ._abi import BF16, F16, HND, NHD, KV_TILE, QK_BLOCK, SageError, lib
 
-__all__ = ["sageattn", "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_quant_qkv",
+__all__ = ["sageattn", "sdpa", "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_quant_qkv",
            "sage_attn_fwd_quantized", "kv_split_size",
            "sage_debug_qk_int32", "workspace_size", "quant_buf_sizes", "make_desc",
            "SageError", "lib", "abi_version"]
@@ -266,3 +266,27 @@ def sageattn(q, k, v, tensor_layout="HND", is_causal=False, smooth_k=True, sm_sc
                          smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
                          sm_scale=sm_scale, return_lse=return_lse, pv_mode=pv_mode,
                          kv_split=kv_split)
+
+
+def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
+         enable_gqa=False):
+    """Drop-in for torch.nn.functional.scaled_dot_product_attention (the
+    package page, "What it is and what it does": a drop-in replacement for
+    scaled_dot_product_attention).  Tensors are [B, H, N, d] (HND), fp16 or
+    bf16, d in {64, 96, 128}; GQA needs enable_gqa=True, as in torch.  What
+    the quantized method cannot honour raises ValueError before any GPU
+    call: an attention mask, dropout, and a causal mask when Nq != Nkv (torch
+    aligns it top-left; this library bottom-right)."""
+    if attn_mask is not None:
+        raise ValueError("sdpa: attn_mask is not supported (only is_causal)")
+    if dropout_p:
+        raise ValueError("sdpa: dropout is not supported (inference only)")
+    if query.dim() != 4 or key.dim() != 4 or value.dim() != 4:
+        raise ValueError("sdpa: expects [B, H, N, d] tensors")
+    if key.shape[1] != query.shape[1] and not enable_gqa:
+        raise ValueError("sdpa: query and key head counts differ; pass enable_gqa=True")
+    if is_causal and query.shape[2] != key.shape[2]:
+        raise ValueError("sdpa: is_causal with Nq != Nkv aligns top-left in torch; "
+                         "use sageattn (bottom-right) instead")
+    return sage_attn_fwd(query, key, value, tensor_layout="HND", is_causal=is_causal,
+                         sm_scale=scale)

@@ -416,3 +416,49 @@ def test_split_merge_weights_follow_the_maxima(orc):
         assert _cos(out[0][0], ex[0][0]) > 0.999
         assert np.max(np.abs(out[0][0][0] - ex[0][0][0])) < 0.05
         assert abs(lse[0][0][0] - ex_lse[0][0][0]) < 1e-3 * max(1.0, abs(ex_lse[0][0][0]))
+
+
+# -------------------------------------------- 32-token Q/K blocks ---
+
+@pytest.mark.parametrize("mode", ["fp8", "half"])
+def test_finer_qk_blocks_track_exact_attention_closer(orc, mode):
+    """32-token Q/K blocks: scores stay within the dequantization bound of their
+    own (finer) scales, so with a few loud tokens the recipe lands closer to
+    exact FP64 attention than with 64-token blocks."""
+    rng = np.random.default_rng(41)
+    d, nq, nkv = 128, 96, 320
+    q = rng.normal(0, 1, (1, 1, nq, d))
+    k = rng.normal(0, 1, (1, 1, nkv, d))
+    q[0, 0, 5::37] *= 10.0                           # loud query tokens
+    k[0, 0, 3::41] *= 10.0                           # loud keys
+    v = rng.normal(0, 1, (1, 1, nkv, d))
+    qh, kh, vh = _f16(q), _f16(k), _f16(v)
+    errs = {}
+    for bs in (64, 32):
+        prob = orc.Problem("f16", "HND", 1, 1, d, [(nq, nkv)], pv_mode=mode, qk_block=bs)
+        pre = orc.prepass(prob, qh, kh, vh)
+        assert pre.qs[0].shape == (1, -(-nq // bs)) and pre.ks[0].shape == (1, -(-nkv // bs))
+        out, _ = orc.forward_rows(prob, pre)
+        ex, _ = orc.exact_rows(prob, qh, kh, vh)
+        errs[bs] = float(np.sqrt(np.mean((out[0] - ex[0]) ** 2)))
+        assert _cos(out[0], ex[0]) > 0.98
+    assert errs[32] < 0.9 * errs[64]
+
+
+def test_finer_qk_blocks_score_bound(orc):
+    """The dequantized-score bound with 32-token scales (one scale per 32
+    query rows and per 32 keys)."""
+    rng = np.random.default_rng(42)
+    d, n = 64, 100
+    q = rng.normal(0, 1, (n, d)).astype(np.float32)
+    k = (rng.normal(0, 1, (n, d)) * np.repeat(rng.uniform(0.2, 5, (n, 1)), d, 1)).astype(np.float32)
+    qc, qsc = orc.quant_int8_blocks(q, 32)
+    kc, ksc = orc.quant_int8_blocks(k, 32)
+    S = orc.qk_int32(qc, kc).astype(np.float64)
+    sq = np.repeat(qsc, 32)[:n].astype(np.float64)
+    sk = np.repeat(ksc, 32)[:n].astype(np.float64)
+    s = S * sq[:, None] * sk[None, :]
+    t = q.astype(np.float64) @ k.T.astype(np.float64)
+    bound = (np.abs(q) @ np.ones((d, n))) * sk[None, :] / 2 \
+        + (np.ones((n, d)) @ np.abs(k).T) * sq[:, None] / 2 + d * sq[:, None] * sk[None, :] / 4
+    assert np.all(np.abs(s - t) <= bound * (1 + 1e-6))

@@ -44,16 +44,17 @@ def test_mean_close_to_fp64(orc):
     assert np.max(np.abs(mu - ref)) < 1e-4
 
 
-def test_int8_blocks_roundtrip_bound(orc):
+@pytest.mark.parametrize("bs", [64, 32])
+def test_int8_blocks_roundtrip_bound(orc, bs):
     rng = np.random.default_rng(2)
-    for n in (1, 63, 64, 65, 300):
+    for n in (1, 31, 32, 33, 63, 64, 65, 300):
         x = (rng.normal(0, 1, (n, 96)) * rng.uniform(0.1, 10)).astype(np.float32)
-        codes, scales = orc.quant_int8_blocks(x)
-        assert codes.dtype == np.int8 and scales.shape == (-(-n // 64),)
+        codes, scales = orc.quant_int8_blocks(x, bs)
+        assert codes.dtype == np.int8 and scales.shape == (-(-n // bs),)
         assert codes.min() >= -127 and codes.max() <= 127
         for b in range(scales.size):
-            blk = x[64 * b:64 * (b + 1)].astype(np.float64)
-            cb = codes[64 * b:64 * (b + 1)].astype(np.float64)
+            blk = x[bs * b:bs * (b + 1)].astype(np.float64)
+            cb = codes[bs * b:bs * (b + 1)].astype(np.float64)
             s = float(scales[b])
             a = np.abs(blk).max()
             assert s == np.float32(np.float32(a) / np.float32(127.0))
@@ -62,6 +63,21 @@ def test_int8_blocks_roundtrip_bound(orc):
             # the block's absmax element maps to +-127
             idx = np.unravel_index(np.abs(blk).argmax(), blk.shape)
             assert abs(cb[idx]) == 127 and np.sign(cb[idx]) == np.sign(blk[idx])
+
+
+def test_int8_finer_blocks_are_the_halves(orc):
+    """A 32-token block is quantized exactly as a 64-token block holding only
+    those rows: each half gets its own absmax and scale."""
+    rng = np.random.default_rng(4)
+    x = rng.normal(0, 1, (128, 64)).astype(np.float32)
+    x[40] *= 30.0                                   # one loud row in the second half
+    c32, s32 = orc.quant_int8_blocks(x, 32)
+    for b in range(4):
+        cb, sb = orc.quant_int8_blocks(x[32 * b:32 * (b + 1)], 64)
+        assert np.array_equal(c32[32 * b:32 * (b + 1)], cb) and s32[b] == sb[0]
+    c64, s64 = orc.quant_int8_blocks(x, 64)
+    # the loud row coarsens only its own 32-token block
+    assert s32[0] < s64[0] and s32[1] == s64[0]
 
 
 def test_int8_zero_block(orc):
