@@ -31,6 +31,12 @@
  *   online softmax over 128-key tiles with p^ = e4m3(448 * e^(s - m)),
  *   l summed from the FP32 p, o = sum p^ v^ * (v_scale/448) / l (+ mu_v).
  *
+ * Finer Q/K blocks (qk_block = 32): the same INT8 quantization per 32-token
+ * block, one wave's query rows and one 32-key MFMA block -- the gfx950 form
+ * of SageAttention2's finer, thread-level quantization of Q and K
+ * (SageAttention2 summary, "Main concepts"; package page: per-block
+ * quantization).
+ *
  * The 16-bit P.V variant (pv_mode = SAGE_PV_HALF), the first SageAttention's
  * INT8-QK / 16-bit-PV kernel (install guide "SageAttention量化加速框架",
  * section 3.1, the qk_int8_pv_fp16 benchmark; package page "What it is and
@@ -98,7 +104,7 @@ typedef enum {
     SAGE_ERR_SEQLENS = 10,   /* cu_seqlens not monotone / not starting at 0     */
     SAGE_ERR_ARCH = 11,      /* current device is not gfx950                    */
     SAGE_ERR_HIP = 12,       /* a HIP runtime call or kernel launch failed      */
-    SAGE_ERR_FLAGS = 13      /* a flag is not 0/1 or reserved fields are set    */
+    SAGE_ERR_FLAGS = 13      /* a flag, pv_mode, kv_split or qk_block is invalid */
 } sage_status;
 
 typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1 } sage_dtype;
@@ -143,7 +149,8 @@ typedef struct {
     int32_t kv_split;        /* keys per split of the key range: 0 none (default),
                                 a positive multiple of SAGE_KV_TILE, or
                                 SAGE_KV_SPLIT_AUTO                                */
-    int32_t reserved[1];     /* must be zero                                      */
+    int32_t qk_block;        /* tokens per Q/K quantization block: 0 or 64
+                                (default), or 32                                  */
 } sage_attn_desc;
 
 /* Fill `desc` for a dense, contiguous problem with the API defaults
@@ -161,9 +168,10 @@ SAGE_API void sage_desc_init(sage_attn_desc* desc, int32_t dtype, int32_t layout
  *   mu_v    [S][hkv][d] FP32, only if smooth_v
  *   q_codes int8: element (s,h,n,c) at ((rq_s*hq + h*npq_s + n)*d + c);
  *           rows n >= nq_s are zero
- *   q_scale FP32: (s,h,blk) at (rq_s*hq + h*npq_s)/64 + blk
+ *   q_scale FP32: (s,h,blk) at (rq_s*hq + h*npq_s)/QB + blk, QB = the
+ *           descriptor's qk_block (64 unless 32 is asked for)
  *   k_codes int8: (s,h,n,c) at ((rk_s*hkv + h*npk_s + n)*d + c), pad rows zero
- *   k_scale FP32: (s,h,blk) at (rk_s*hkv + h*npk_s)/64 + blk (pad blocks 0)
+ *   k_scale FP32: (s,h,blk) at (rk_s*hkv + h*npk_s)/QB + blk (pad blocks 0)
  *   v_codes OCP E4M3 bytes, channel-major: (s,h,n,c) at
  *           ((rk_s*hkv + h*npk_s)*d + c*npk_s + n), pad tokens zero;
  *           with SAGE_PV_HALF the same index counts 16-bit elements of the

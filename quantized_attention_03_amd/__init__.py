@@ -12,7 +12,8 @@ Every entry point takes pv_mode="fp8" (E4M3 P and V, SageAttention2; the
 default) or pv_mode="half" (P and V in the input's 16-bit type, the first
 SageAttention's INT8-QK / 16-bit-PV kernel), and kv_split: 0 (no split of
 the key range), a multiple of 128 keys, or "auto" (the library's rule; see
-kv_split_size).
+kv_split_size), and qk_block: 64 (default) or 32 tokens per Q/K quantization
+block.
 """
 from __future__ import annotations
 
@@ -47,7 +48,7 @@ def _strides(t: torch.Tensor, layout: str, varlen: bool):
 
 def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q=False,
               smooth_k=True, smooth_v=False, sm_scale=None, varlen=False,
-              pv_mode="fp8", kv_split=0) -> _abi.Desc:
+              pv_mode="fp8", kv_split=0, qk_block=64) -> _abi.Desc:
     """Descriptor for q/k/v torch tensors (dense [B,H,N,d] / [B,N,H,d], or packed
     varlen [T,H,d] / [H,T,d])."""
     if tensor_layout not in ("HND", "NHD"):
@@ -81,6 +82,7 @@ def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q
     d.sm_scale = float(sm_scale) if sm_scale else 0.0
     d.pv_mode = _abi.PV_MODES[pv_mode]
     d.kv_split = _abi.KV_SPLIT_AUTO if kv_split == "auto" else int(kv_split)
+    d.qk_block = int(qk_block)
     return d
 
 
@@ -136,7 +138,7 @@ _BUF_DT = {"mu_q": torch.float32, "mu_k": torch.float32, "mu_v": torch.float32,
 
 def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
                    smooth_k=True, smooth_v=False, sm_scale=None, cu_seqlens_q=None,
-                   cu_seqlens_kv=None, bufs=None, pv_mode="fp8", kv_split=0):
+                   cu_seqlens_kv=None, bufs=None, pv_mode="fp8", kv_split=0, qk_block=64):
     """Run the pre-pass alone; returns a dict of flat device tensors laid out as
     documented for sage_quant_bufs in include/sage.h.  Passing the dict of an
     earlier call on the same problem as `bufs` reuses its buffers and
@@ -144,7 +146,8 @@ def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=Fa
     varlen = cu_seqlens_q is not None
     desc = make_desc(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                     sm_scale=sm_scale, varlen=varlen, pv_mode=pv_mode, kv_split=kv_split)
+                     sm_scale=sm_scale, varlen=varlen, pv_mode=pv_mode, kv_split=kv_split,
+                     qk_block=qk_block)
     if bufs is None:
         sizes = quant_buf_sizes(desc, cu_seqlens_q, cu_seqlens_kv)
         bufs = {name: torch.zeros(max(1, nbytes // torch.empty((), dtype=_BUF_DT[name]).element_size()),
@@ -213,12 +216,13 @@ def sage_debug_qk_int32(bufs, *, cu_seqlens_q=None, cu_seqlens_kv=None, device=N
 
 def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
                   smooth_k=True, smooth_v=False, sm_scale=None, return_lse=False,
-                  out=None, workspace=None, pv_mode="fp8", kv_split=0):
+                  out=None, workspace=None, pv_mode="fp8", kv_split=0, qk_block=64):
     """Dense forward pass.  Returns o (and lse [B, hq, nq] FP32 if asked)."""
     o = torch.empty_like(q) if out is None else out
     desc = make_desc(q, k, v, o, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                     sm_scale=sm_scale, pv_mode=pv_mode, kv_split=kv_split)
+                     sm_scale=sm_scale, pv_mode=pv_mode, kv_split=kv_split,
+                     qk_block=qk_block)
     lse = None
     if return_lse:
         lse = torch.empty((desc.batch, desc.hq, desc.nq), dtype=torch.float32, device=q.device)
@@ -234,13 +238,14 @@ def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=Fal
 def sage_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, tensor_layout="NHD",
                          is_causal=False, smooth_q=False, smooth_k=True, smooth_v=False,
                          sm_scale=None, return_lse=False, out=None, workspace=None,
-                         pv_mode="fp8", kv_split=0):
+                         pv_mode="fp8", kv_split=0, qk_block=64):
     """Packed variable-length forward pass (q [T,H,d] for NHD or [H,T,d] for
     HND; cu_seqlens are host int32 prefix offsets).  lse is [hq, T_q]."""
     o = torch.empty_like(q) if out is None else out
     desc = make_desc(q, k, v, o, tensor_layout=tensor_layout, is_causal=is_causal,
                      smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
-                     sm_scale=sm_scale, varlen=True, pv_mode=pv_mode, kv_split=kv_split)
+                     sm_scale=sm_scale, varlen=True, pv_mode=pv_mode, kv_split=kv_split,
+                     qk_block=qk_block)
     cq, n = _cu(cu_seqlens_q)
     ck, nk = _cu(cu_seqlens_kv)
     if nk != n:
@@ -260,12 +265,13 @@ def sage_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, tensor_layout=
 
 
 def sageattn(q, k, v, tensor_layout="HND", is_causal=False, smooth_k=True, sm_scale=None,
-             smooth_q=False, smooth_v=False, return_lse=False, pv_mode="fp8", kv_split=0):
+             smooth_q=False, smooth_v=False, return_lse=False, pv_mode="fp8", kv_split=0,
+             qk_block=64):
     """The package page's call: attention output of the quantized forward pass."""
     return sage_attn_fwd(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal,
                          smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
                          sm_scale=sm_scale, return_lse=return_lse, pv_mode=pv_mode,
-                         kv_split=kv_split)
+                         kv_split=kv_split, qk_block=qk_block)
 
 
 def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,

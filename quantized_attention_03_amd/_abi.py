@@ -37,7 +37,7 @@ class Desc(ctypes.Structure):
         ("is_causal", ctypes.c_int32), ("smooth_q", ctypes.c_int32),
         ("smooth_k", ctypes.c_int32), ("smooth_v", ctypes.c_int32),
         ("sm_scale", ctypes.c_float), ("pv_mode", ctypes.c_int32),
-        ("kv_split", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
+        ("kv_split", ctypes.c_int32), ("qk_block", ctypes.c_int32),
     ]
 
 

@@ -36,6 +36,7 @@ struct Plan {
     int32_t nsplit = 1;               // splits of the longest key range
     int64_t rows_total = 0;           // lse rows: B*hq*nq, or hq*total_q (varlen)
     int32_t max_nkv = 0;
+    int32_t qb = QBLK;                // tokens per Q/K quantization block (64 or 32)
 };
 
 // Byte offsets of everything placed in a workspace (quantized tensors first,
@@ -62,9 +63,9 @@ sage_quant_sizes quant_sizes(const Plan& p) {
     z.mu_k = p.smooth_k ? S * p.hkv * d * 4 : 0;
     z.mu_v = p.smooth_v ? S * p.hkv * d * 4 : 0;
     z.q_codes = (size_t)p.rows_q * p.hq * d;
-    z.q_scale = (size_t)p.rows_q * p.hq / QBLK * 4;
+    z.q_scale = (size_t)p.rows_q * p.hq / p.qb * 4;
     z.k_codes = (size_t)p.rows_k * p.hkv * d;
-    z.k_scale = (size_t)p.rows_k * p.hkv / QBLK * 4;
+    z.k_scale = (size_t)p.rows_k * p.hkv / p.qb * 4;
     z.v_codes = (size_t)p.rows_k * p.hkv * d * (p.pv_half ? 2 : 1);
     z.v_scale = p.pv_half ? 0 : S * p.hkv * d * 4;
     z.delta_s = p.smooth_q ? (size_t)p.rows_k * p.hq * 4 : 0;
@@ -132,7 +133,8 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
         !flag_ok(D.smooth_v) || (D.pv_mode != SAGE_PV_FP8 && D.pv_mode != SAGE_PV_HALF) ||
         !(D.kv_split == SAGE_KV_SPLIT_AUTO || D.kv_split == 0 ||
           (D.kv_split > 0 && D.kv_split % SAGE_KV_TILE == 0 && D.kv_split <= (1 << 24))) ||
-        D.reserved[0] || !std::isfinite(D.sm_scale))
+        !(D.qk_block == 0 || D.qk_block == 64 || D.qk_block == 32) ||
+        !std::isfinite(D.sm_scale))
         return SAGE_ERR_FLAGS;
     if (D.head_dim != 64 && D.head_dim != 96 && D.head_dim != 128) return SAGE_ERR_HEAD_DIM;
     if (D.hq < 1 || D.hkv < 1 || D.hq > 65536 || D.hkv > 65536) return SAGE_ERR_SHAPE;
@@ -158,6 +160,7 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
     p.smooth_v = D.smooth_v;
     p.pv_half = D.pv_mode == SAGE_PV_HALF;
     p.kv_split_req = D.kv_split;
+    p.qb = D.qk_block == 32 ? 32 : QBLK;
     p.sm_scale = D.sm_scale > 0.0f ? D.sm_scale : 1.0f / std::sqrt((float)D.head_dim);
     if (varlen) {
         if (cuq[0] != 0 || cuk[0] != 0) return SAGE_ERR_SEQLENS;
@@ -241,6 +244,7 @@ std::vector<KParams> make_params(const Plan& p) {
     base.group = p.group;
     base.causal = p.causal;
     base.pv_half = p.pv_half;
+    base.qb = p.qb;
     base.sm_scale = p.sm_scale;
     base.sml2 = (float)((double)p.sm_scale * 1.4426950408889634);
     base.qs = p.qs;
@@ -665,7 +669,7 @@ const char* sage_status_string(sage_status s) {
         case SAGE_ERR_SEQLENS: return "invalid cu_seqlens";
         case SAGE_ERR_ARCH: return "device is not gfx950";
         case SAGE_ERR_HIP: return "HIP runtime error";
-        case SAGE_ERR_FLAGS: return "invalid flag, pv_mode or reserved field";
+        case SAGE_ERR_FLAGS: return "invalid flag, pv_mode, kv_split or qk_block";
     }
     return "unknown status";
 }

@@ -382,6 +382,14 @@ __device__ inline int max32(const v16i& a, const v16i& b) {
     return max(max(max(l2[0], l2[1]), l2[2]), max(l2[3], l1[10]));
 }
 
+// Max of the 16 integers of one accumulator block (v_max3_i32 tree).
+__device__ inline int max16(const v16i& a) {
+    int l1[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) l1[i] = max(max(a[3 * i], a[3 * i + 1]), a[3 * i + 2]);
+    return max(max(max(l1[0], l1[1]), l1[2]), max(max(l1[3], l1[4]), a[15]));
+}
+
 // Online softmax of one tile: updates the running max and sum, writes P^ in
 // the B layout of the 32x32x64 FP8 MFMA (half kh covers the lane's keys of
 // blocks 2kh and 2kh+1, bytes 0..15 and 16..31) -- or, with 16-bit operands
@@ -389,12 +397,18 @@ __device__ inline int max32(const v16i& a, const v16i& b) {
 // pv_tile_h reads them -- and returns alpha, the factor that moves earlier
 // contributions to the new max.  Keys past `lim` are masked when MASK.
 // The FP8 P^ carries the static scale 448 (folded into the exponent); the
-// 16-bit p does not.
-template <bool MASK, bool HAS_DS, bool PVH = false, int DT = 0>
-__device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, float c1,
-                                     const float* dsl, float sml2, int kt0, int lim, float& m_run,
-                                     float& l_run) {
+// 16-bit p does not.  Score scales: with 64-token K blocks c0 serves the
+// tile's first 64 keys and c1 the rest; with 32-token blocks (QB = 32)
+// c0..c3 serve the four 32-key blocks.
+template <bool MASK, bool HAS_DS, bool PVH = false, int DT = 0, int QB = QBLK>
+__device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, float c1, float c2,
+                                     float c3, const float* dsl, float sml2, int kt0, int lim,
+                                     float& m_run, float& l_run) {
     constexpr float POFF = PVH ? 0.0f : LOG2_448;
+    auto cof = [&](int b) {
+        if constexpr (QB == 32) return b == 0 ? c0 : (b == 1 ? c1 : (b == 2 ? c2 : c3));
+        else return b < 2 ? c0 : c1;
+    };
     const int h = (threadIdx.x & 63) >> 5;
     float p[4][16];
     float m_new;
@@ -408,18 +422,33 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
                 for (int r = 0; r < 16; ++r)
                     sacc[b][r] = kt0 + 32 * b + r > lim ? NEG_INF_BITS : sacc[b][r];
         }
-        // three-input max trees (v_max3_i32), one per 64-key half
-        const int mx0 = max32(sacc[0], sacc[1]), mx1 = max32(sacc[2], sacc[3]);
-        const float f0 = mx0 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx0) - SBIAS_F) * c0;
-        const float f1 = mx1 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx1) - SBIAS_F) * c1;
-        m_new = fmaxf(m_run, swap_max(fmaxf(f0, f1)));
+        // three-input max trees (v_max3_i32), one per block of keys that
+        // shares a scale (the integer order is the score order only there)
+        float fm;
+        if constexpr (QB == 32) {
+            fm = -INFINITY;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int mx = max16(sacc[b]);
+                fm = fmaxf(fm, mx == NEG_INF_BITS ? -INFINITY
+                                                  : (__int_as_float(mx) - SBIAS_F) * cof(b));
+            }
+        } else {
+            const int mx0 = max32(sacc[0], sacc[1]), mx1 = max32(sacc[2], sacc[3]);
+            const float f0 =
+                mx0 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx0) - SBIAS_F) * c0;
+            const float f1 =
+                mx1 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx1) - SBIAS_F) * c1;
+            fm = fmaxf(f0, f1);
+        }
+        m_new = fmaxf(m_run, swap_max(fm));
         const float nm = POFF - (m_new == -INFINITY ? 0.0f : m_new);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 p[b][r] = __builtin_amdgcn_exp2f(
-                    fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, b < 2 ? c0 : c1, nm));
+                    fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, cof(b), nm));
     } else {
         // here c0, c1 leave out sm_scale*log2(e): y = S*sq*sk + dS is formed
         // first (its maximum taken), and the base-2 factor is applied inside
@@ -427,7 +456,7 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
         float mt = -INFINITY;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const float c = b < 2 ? c0 : c1;
+            const float c = cof(b);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float y = fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, c, dsl[32 * b + 16 * h + r]);
@@ -523,7 +552,7 @@ __device__ inline uint32_t f2h_bits(float f) {
 //   every wave waits for its copies before each barrier.
 //   bias(t): three buffers, as it is read up to epoch 2t+2.
 // ---------------------------------------------------------------------------
-template <int D, int DT, bool HAS_DS, bool PVH>
+template <int D, int DT, bool HAS_DS, bool PVH, int QB>
 __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __restrict__ qc,
                                                  const float* __restrict__ qsc,
                                                  const int8_t* __restrict__ kc,
@@ -547,7 +576,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     const int64_t krow0 = (si.rk * P.hkv + (int64_t)w.hkv * si.npk);
     const int8_t* kbase = kc + krow0 * D;
     const uint8_t* vbase = vc + krow0 * D * T::VES;
-    const float* kscb = ksc + krow0 / QBLK;
+    const float* kscb = ksc + krow0 / QB;
     const float* dsb = HAS_DS ? ds + si.rk * P.hq + (int64_t)w.head0 * si.npk : nullptr;
 
     v4i qf[D / 32];
@@ -555,7 +584,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     if (w.nt_w > w.t0) {
         const int64_t qrow0 = si.rq * P.hq + (int64_t)w.head * si.npq;
         load_q<D>(qc + (qrow0 + my_q) * D, qf);
-        sq = qsc[qrow0 / QBLK + w.q0 / QBLK];
+        sq = qsc[(qrow0 + w.q0) / QB];
     } else {
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) qf[c] = v4i{0, 0, 0, 0};
@@ -635,9 +664,15 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         // (a zero scale -- an all-zero block -- is raised to the smallest
         // normal float, which leaves every score unchanged after rounding and
         // keeps a masked key's -inf * c at -inf)
-        float c0 = fmaxf(HAS_DS ? sq * kscb[2 * t] : sq * kscb[2 * t] * P.sml2, FLT_MIN);
-        float c1 = fmaxf(HAS_DS ? sq * kscb[2 * t + 1] : sq * kscb[2 * t + 1] * P.sml2, FLT_MIN);
+        constexpr int NB = KVT / QB;             // key blocks of a tile (2 or 4)
+        auto cs = [&](int b) {
+            const float ks = kscb[NB * t + b];
+            return fmaxf(HAS_DS ? sq * ks : sq * ks * P.sml2, FLT_MIN);
+        };
+        float c0 = cs(0), c1 = cs(1);
+        float c2 = NB == 4 ? cs(NB == 4 ? 2 : 0) : 0.0f, c3 = NB == 4 ? cs(NB == 4 ? 3 : 0) : 0.0f;
         asm volatile("" : "+v"(c0), "+v"(c1));
+        if constexpr (NB == 4) asm volatile("" : "+v"(c2), "+v"(c3));
         __builtin_amdgcn_s_setprio(0);
         bar();
         // ---- softmax phase ----
@@ -650,11 +685,12 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                 (t + 1) * KVT > nkv || (P.causal && (t + 1) * KVT - 1 > wave_diag);
             float alpha;
             if (need_mask)
-                alpha = softmax_tile<true, HAS_DS, PVH, DT>(sacc, pb, ph, c0, c1, dsl, P.sml2, kt0,
-                                                            lim, m_run, l_run);
+                alpha = softmax_tile<true, HAS_DS, PVH, DT, QB>(sacc, pb, ph, c0, c1, c2, c3, dsl,
+                                                                P.sml2, kt0, lim, m_run, l_run);
             else
-                alpha = softmax_tile<false, HAS_DS, PVH, DT>(sacc, pb, ph, c0, c1, dsl, P.sml2,
-                                                             kt0, lim, m_run, l_run);
+                alpha = softmax_tile<false, HAS_DS, PVH, DT, QB>(sacc, pb, ph, c0, c1, c2, c3,
+                                                                 dsl, P.sml2, kt0, lim, m_run,
+                                                                 l_run);
             // acc (the tiles before t, at the previous max) is rescaled in
             // the next MFMA phase, before the P.V of tile t
             alpha_prev = alpha;
@@ -830,14 +866,14 @@ constexpr int lds_bytes() {
            (HAS_DS ? 3 * Tile<D, PVH>::DSBYTES : 0);
 }
 
-template <int D, int DT, bool HAS_DS, bool PVH>
+template <int D, int DT, bool HAS_DS, bool PVH, int QB>
 hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const int8_t* kc,
                   const float* ksc, const uint8_t* vc, const float* vsc, const float* ds,
                   const float* mu_v, void* o, float* lse, hipStream_t st) {
     static bool attr_set = false;   // benign race: the call is idempotent
     if (!attr_set) {
         hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D, DT, HAS_DS, PVH>),
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D, DT, HAS_DS, PVH, QB>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
                                 lds_bytes<D, HAS_DS, PVH>());
         if (e != hipSuccess) return e;
@@ -845,7 +881,7 @@ hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const in
     }
     const int nblocks = wg_count_host(P, FWD_WAVES) * P.nsplit;
     if (nblocks <= 0) return hipSuccess;
-    k_attn<D, DT, HAS_DS, PVH><<<nblocks, FWD_NT, lds_bytes<D, HAS_DS, PVH>(), st>>>(
+    k_attn<D, DT, HAS_DS, PVH, QB><<<nblocks, FWD_NT, lds_bytes<D, HAS_DS, PVH>(), st>>>(
         P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, static_cast<uint16_t*>(o), lse);
     return hipGetLastError();
 }
@@ -855,9 +891,14 @@ hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const in
 hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const float* qsc,
                        const int8_t* kc, const float* ksc, const uint8_t* vc, const float* vsc,
                        const float* ds, const float* mu_v, void* o, float* lse, hipStream_t st) {
-#define SAGE_AH(D, DT, PVH)                                                                 \
-    return ds ? attn_d<D, DT, true, PVH>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st) \
-              : attn_d<D, DT, false, PVH>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st)
+#define SAGE_AQ(D, DT, PVH, QB)                                                                  \
+    return ds ? attn_d<D, DT, true, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st) \
+              : attn_d<D, DT, false, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st)
+#define SAGE_AH(D, DT, PVH)                    \
+    do {                                       \
+        if (P.qb == 32) SAGE_AQ(D, DT, PVH, 32); \
+        SAGE_AQ(D, DT, PVH, QBLK);             \
+    } while (0)
 #define SAGE_A(D, DT)                   \
     do {                                \
         if (P.pv_half) SAGE_AH(D, DT, true); \
@@ -874,6 +915,7 @@ hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const floa
     }
 #undef SAGE_A
 #undef SAGE_AH
+#undef SAGE_AQ
 }
 
 hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,

@@ -35,6 +35,7 @@ struct KParams {
     int32_t d, hq, hkv, group;          // group = hq / hkv
     int32_t causal;
     int32_t pv_half;                    // P.V in the input's 16-bit type (else E4M3)
+    int32_t qb;                         // tokens per Q/K quantization block (64 or 32)
     float sm_scale;                     // natural-log units
     float sml2;                         // sm_scale * log2(e)
     Strides qs, ks, vs, os;

@@ -242,7 +242,9 @@ __global__ __launch_bounds__(WG) void k_finalize(KParams P, FinJobs J) {
 // staged in LDS and ds[h_q][j] = sum_c mu_q[h_q][c] * k_s[j][c] (ascending c,
 // FP32) is written for every query head of the group.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool DELTA>
+// QB: tokens per quantization block (64: the workgroup's whole chunk; 32:
+// each half of it gets its own absmax and scale).
+template <int DT, int D, bool DELTA, int QB = QBLK>
 __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restrict__ x,
                                       Strides xs, int is_q, int heads,
                                       const float* __restrict__ mu, int8_t* __restrict__ codes,
@@ -252,8 +254,9 @@ __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restri
     constexpr int GPR = D / 8;              // granules per token row
     constexpr int NG = QBLK * GPR;          // granules per block
     constexpr int PER = (NG + WG - 1) / WG; // granules per thread
-    float* red = smf;                       // WG / 64 floats
-    float* ks_lds = smf + WG / 64;          // QBLK * D floats (DELTA)
+    constexpr int NSUB = QBLK / QB;         // quantization blocks per chunk (1 or 2)
+    float* red = smf;                       // NSUB * WG / 64 floats
+    float* ks_lds = smf + 2 * (WG / 64);    // QBLK * D floats (DELTA)
 
     int local;
     ChunkCount cnt{&P, is_q != 0, heads, 1};
@@ -268,7 +271,9 @@ __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restri
     const float* muh = mu ? mu + ((int64_t)si.sid * heads + h) * D : nullptr;
 
     float val[PER][8];
-    float amax = 0.0f;
+    float amax[NSUB];
+#pragma unroll
+    for (int k = 0; k < NSUB; ++k) amax[k] = 0.0f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int gi = threadIdx.x + i * WG;
@@ -282,27 +287,38 @@ __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restri
 #pragma unroll
                 for (int e = 0; e < 8; ++e) val[i][e] = val[i][e] - muh[cg + e];
             }
+            float m = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(val[i][e]));
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(val[i][e]));
+            if constexpr (NSUB == 1) amax[0] = fmaxf(amax[0], m);
+            else if (r < QB) amax[0] = fmaxf(amax[0], m);
+            else amax[1] = fmaxf(amax[1], m);
         }
     }
-    amax = wave_max(amax);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    float a = red[0];
 #pragma unroll
-    for (int w = 1; w < WG / 64; ++w) a = fmaxf(a, red[w]);
-
-    const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+    for (int k = 0; k < NSUB; ++k) {
+        const float wm = wave_max(amax[k]);
+        if ((threadIdx.x & 63) == 0) red[k * (WG / 64) + (threadIdx.x >> 6)] = wm;
+    }
+    __syncthreads();
+    float a[NSUB], inv[NSUB];
+#pragma unroll
+    for (int k = 0; k < NSUB; ++k) {
+        a[k] = red[k * (WG / 64)];
+#pragma unroll
+        for (int w = 1; w < WG / 64; ++w) a[k] = fmaxf(a[k], red[k * (WG / 64) + w]);
+        inv[k] = a[k] > 0.0f ? 127.0f / a[k] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int gi = threadIdx.x + i * WG;
         if (gi >= NG) continue;
         const int r = gi / GPR, cg = (gi % GPR) * 8;
+        const float inv_r = (NSUB == 1 || r < QB) ? inv[0] : inv[NSUB - 1];
         uint32_t w0 = 0, w1 = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float q = rintf(val[i][e] * inv);
+            float q = rintf(val[i][e] * inv_r);
             q = fminf(fmaxf(q, -127.0f), 127.0f);
             const uint32_t b = (uint32_t)(int32_t)q & 0xffu;
             if (e < 4) w0 |= b << (8 * e); else w1 |= b << (8 * (e - 4));
@@ -313,7 +329,10 @@ __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restri
             for (int e = 0; e < 8; ++e) ks_lds[r * D + cg + e] = val[i][e];
         }
     }
-    if (threadIdx.x == 0) scales[row0 / QBLK + blk] = a > 0.0f ? a / 127.0f : 0.0f;
+    if (threadIdx.x < NSUB) {
+        const float av = threadIdx.x == 0 ? a[0] : a[NSUB - 1];
+        scales[row0 / QB + blk * NSUB + threadIdx.x] = av > 0.0f ? av / 127.0f : 0.0f;
+    }
 
     if constexpr (DELTA) {
         __syncthreads();
@@ -488,22 +507,22 @@ __device__ inline void half_v_chunk(const KParams& P, const uint16_t* __restrict
 // All quantization of a problem in one launch: the Q blocks, then the K
 // blocks (with the score bias when Q is smoothed), then the V chunks.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool DELTA>
+template <int DT, int D, bool DELTA, int QB>
 __global__ __launch_bounds__(WG) void k_quant(KParams P, QuantArgs A) {
-    constexpr int QK_LDS = (WG / 64 + (DELTA ? QBLK * D : 0)) * 4;
+    constexpr int QK_LDS = (2 * (WG / 64) + (DELTA ? QBLK * D : 0)) * 4;
     constexpr int VL = quant_v_lds_bytes<D>() > half_v_lds_bytes<D>() ? quant_v_lds_bytes<D>()
                                                                       : half_v_lds_bytes<D>();
     constexpr int LDS = QK_LDS > VL ? QK_LDS : VL;
     __shared__ __align__(16) uint8_t sm[LDS];
     int blk = blockIdx.x;
     if (blk < A.nq) {
-        quant_qk_block<DT, D, false>(P, A.q, P.qs, 1, P.hq, A.mu_q, A.q_codes, A.q_scale,
+        quant_qk_block<DT, D, false, QB>(P, A.q, P.qs, 1, P.hq, A.mu_q, A.q_codes, A.q_scale,
                                      nullptr, nullptr, blk, reinterpret_cast<float*>(sm));
         return;
     }
     blk -= A.nq;
     if (blk < A.nk) {
-        quant_qk_block<DT, D, DELTA>(P, A.k, P.ks, 0, P.hkv, A.mu_k, A.k_codes, A.k_scale,
+        quant_qk_block<DT, D, DELTA, QB>(P, A.k, P.ks, 0, P.hkv, A.mu_k, A.k_codes, A.k_scale,
                                      A.mu_q, A.delta_s, blk, reinterpret_cast<float*>(sm));
         return;
     }
@@ -541,8 +560,13 @@ hipError_t launch_finalize(const KParams& P, const FinJobs& J, hipStream_t st) {
 
 template <int DT, int D>
 static void quant_d(const KParams& P, const QuantArgs& A, int nb, hipStream_t st) {
-    if (A.delta_s) k_quant<DT, D, true><<<nb, WG, 0, st>>>(P, A);
-    else k_quant<DT, D, false><<<nb, WG, 0, st>>>(P, A);
+    if (P.qb == 32) {
+        if (A.delta_s) k_quant<DT, D, true, 32><<<nb, WG, 0, st>>>(P, A);
+        else k_quant<DT, D, false, 32><<<nb, WG, 0, st>>>(P, A);
+    } else {
+        if (A.delta_s) k_quant<DT, D, true, QBLK><<<nb, WG, 0, st>>>(P, A);
+        else k_quant<DT, D, false, QBLK><<<nb, WG, 0, st>>>(P, A);
+    }
 }
 
 hipError_t launch_quant(const KParams& P, int dtype, const QuantArgs& A, hipStream_t st) {

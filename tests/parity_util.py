@@ -33,18 +33,19 @@ def gpu_inputs(w: synth.Workload):
     return q, k, v, meta
 
 
-def run_quant(w, q, k, v, meta, pv="fp8"):
+def run_quant(w, q, k, v, meta, pv="fp8", qb=64):
     kw = dict(tensor_layout=w.layout, is_causal=w.causal, smooth_q=w.smooth_q,
-              smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale, pv_mode=pv)
+              smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale, pv_mode=pv,
+              qk_block=qb)
     if w.varlen:
         kw.update(cu_seqlens_q=meta["cu_seqlens_q"], cu_seqlens_kv=meta["cu_seqlens_kv"])
     return qa.sage_quant_qkv(q, k, v, **kw)
 
 
-def run_fwd(w, q, k, v, meta, return_lse=True, pv="fp8"):
+def run_fwd(w, q, k, v, meta, return_lse=True, pv="fp8", qb=64):
     kw = dict(tensor_layout=w.layout, is_causal=w.causal, smooth_q=w.smooth_q,
               smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale,
-              return_lse=return_lse, pv_mode=pv)
+              return_lse=return_lse, pv_mode=pv, qk_block=qb)
     if w.varlen:
         return qa.sage_attn_fwd_varlen(q, k, v, meta["cu_seqlens_q"], meta["cu_seqlens_kv"], **kw)
     return qa.sage_attn_fwd(q, k, v, **kw)
@@ -54,7 +55,7 @@ def _pad(x, m):
     return (x + m - 1) // m * m
 
 
-def unpack_quant(w, bufs, pv="fp8"):
+def unpack_quant(w, bufs, pv="fp8", qb=64):
     """GPU buffers -> oracle.Prepass-shaped lists (numpy), plus pad checks.
     With pv = "half" the V operand is 16-bit (uint16 patterns), unscaled."""
     seqs = w.seq_lens()
@@ -66,17 +67,17 @@ def unpack_quant(w, bufs, pv="fp8"):
     for s, (nq, nkv) in enumerate(seqs):
         npq, npk = _pad(nq, QB), _pad(nkv, KVT)
         qc = host["q_codes"][rq * hq * d:(rq * hq + hq * npq) * d].reshape(hq, npq, d)
-        qs = host["q_scale"][rq * hq // QB:(rq * hq + hq * npq) // QB].reshape(hq, npq // QB)
+        qs = host["q_scale"][rq * hq // qb:(rq * hq + hq * npq) // qb].reshape(hq, npq // qb)
         kc = host["k_codes"][rk * hkv * d:(rk * hkv + hkv * npk) * d].reshape(hkv, npk, d)
-        ks = host["k_scale"][rk * hkv // QB:(rk * hkv + hkv * npk) // QB].reshape(hkv, npk // QB)
+        ks = host["k_scale"][rk * hkv // qb:(rk * hkv + hkv * npk) // qb].reshape(hkv, npk // qb)
         vall = host["v_codes"].view(np.uint16) if pv == "half" else host["v_codes"]
         vc = vall[rk * hkv * d:(rk * hkv + hkv * npk) * d].reshape(hkv, d, npk)
         pads_ok &= not qc[:, nq:].any() and not kc[:, nkv:].any() and not vc[:, :, nkv:].any()
-        pads_ok &= not ks[:, -(-nkv // QB):].any()
+        pads_ok &= not ks[:, -(-nkv // qb):].any()
         R.qc.append(qc[:, :nq])
-        R.qs.append(qs[:, :-(-nq // QB)])
+        R.qs.append(qs[:, :-(-nq // qb)])
         R.kc.append(kc[:, :nkv])
-        R.ks.append(ks[:, :-(-nkv // QB)])
+        R.ks.append(ks[:, :-(-nkv // qb)])
         R.vc.append(vc.transpose(0, 2, 1)[:, :nkv])
         R.vs.append(None if pv == "half" else host["v_scale"].reshape(-1, hkv, d)[s])
         R.mu_q.append(host["mu_q"].reshape(-1, hq, d)[s] if w.smooth_q else None)

@@ -65,7 +65,7 @@ def _ws(d, cuq=None, cuk=None, n=0):
 def test_desc_init_defaults():
     d = _desc()
     assert (d.smooth_k, d.smooth_q, d.smooth_v, d.is_causal, d.sm_scale) == (1, 0, 0, 0, 0.0)
-    assert d.pv_mode == _abi.PV_FP8 and d.kv_split == 0 and tuple(d.reserved) == (0,)
+    assert d.pv_mode == _abi.PV_FP8 and d.kv_split == 0 and d.qk_block == 0
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -83,6 +83,8 @@ def test_desc_init_defaults():
     ("pv_mode", -1, "SAGE_ERR_FLAGS"),
     ("kv_split", 100, "SAGE_ERR_FLAGS"),
     ("kv_split", -2, "SAGE_ERR_FLAGS"),
+    ("qk_block", 16, "SAGE_ERR_FLAGS"),
+    ("qk_block", 128, "SAGE_ERR_FLAGS"),
 ])
 def test_descriptor_errors(field, value, status):
     d = _desc(**{field: value})
@@ -90,10 +92,7 @@ def test_descriptor_errors(field, value, status):
     assert _abi.STATUS_NAMES[_ws(d)[0]] == status
 
 
-def test_reserved_and_nan_scale_rejected():
-    d = _desc()
-    d.reserved[0] = 5
-    assert _abi.STATUS_NAMES[_fwd(d)] == "SAGE_ERR_FLAGS"
+def test_nan_scale_rejected():
     d = _desc(sm_scale=float("nan"))
     assert _abi.STATUS_NAMES[_fwd(d)] == "SAGE_ERR_FLAGS"
 
@@ -165,6 +164,18 @@ def test_quant_buf_sizes_follow_documented_layout():
     assert qa.lib().sage_quant_buf_sizes(ctypes.byref(dv), cq, ck, 3, ctypes.byref(z)) == 0
     assert z.q_codes == hq * (64 + 64 + 0) * dd          # lengths 1, 64, 0
     assert z.k_codes == hkv * (256 + 128 + 0) * dd      # lengths 129, 1, 0
+
+
+def test_finer_qk_block_sizes():
+    """32-token Q/K blocks: twice the Q and K scales, everything else equal
+    (codes keep their 64-token row padding)."""
+    a = qa.quant_buf_sizes(_desc(smooth_q=1))
+    b = qa.quant_buf_sizes(_desc(smooth_q=1, qk_block=32))
+    c = qa.quant_buf_sizes(_desc(smooth_q=1, qk_block=64))
+    assert a == c
+    assert b["q_scale"] == 2 * a["q_scale"] and b["k_scale"] == 2 * a["k_scale"]
+    assert {k: v for k, v in b.items() if k not in ("q_scale", "k_scale")} == \
+        {k: v for k, v in a.items() if k not in ("q_scale", "k_scale")}
 
 
 def test_half_pv_sizes():
