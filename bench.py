@@ -50,6 +50,8 @@ def _parse():
                     help="P.V operands: E4M3 (default) or the input's 16-bit type")
     ap.add_argument("--kv-split", default="0",
                     help="keys per split of the key range (multiple of 128), 0 or auto")
+    ap.add_argument("--qk-block", type=int, choices=(64, 32), default=64,
+                    help="tokens per Q/K quantization block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows per query head")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -98,7 +100,8 @@ def copy_calibration(mib: int):
           flush=True)
 
 
-def cpu_baseline(w, q, k, v, rows_per_head: int, pv: str = "fp8"):
+def cpu_baseline(w, q, k, v, rows_per_head: int, pv: str = "fp8", split: int = 0,
+                 qb: int = 64):
     """Time the oracle's same-recipe forward on evenly spaced query rows of
     every head (the pre-pass is run first and not timed)."""
     import numpy as np
@@ -109,7 +112,7 @@ def cpu_baseline(w, q, k, v, rows_per_head: int, pv: str = "fp8"):
     def u16(t):
         return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
-    prob = orc.problem_from_workload(w, pv)
+    prob = orc.problem_from_workload(w, pv, split, qb)
     pre = orc.prepass(prob, u16(q), u16(k), u16(v))
     threads = os.cpu_count() or 1
     rows, pairs = [], 0
@@ -166,7 +169,7 @@ def main():
     kv_split = args.kv_split if args.kv_split == "auto" else int(args.kv_split)
     kw = dict(tensor_layout=w.layout, is_causal=w.causal, smooth_q=w.smooth_q,
               smooth_k=w.smooth_k, smooth_v=w.smooth_v, sm_scale=w.sm_scale,
-              pv_mode=args.pv, kv_split=kv_split)
+              pv_mode=args.pv, kv_split=kv_split, qk_block=args.qk_block)
     o = torch.empty_like(q)
     cu = {}
     if w.varlen:
@@ -246,7 +249,8 @@ def main():
         "config": {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
                                f"Nq=Nkv={w.Nq} d={w.d} {w.dtype} {w.layout}"
                                f"{' causal' if w.causal else ''}"
-                               f"{', 16-bit P.V' if half else ''}",
+                               f"{', 16-bit P.V' if half else ''}"
+                               f"{', 32-token Q/K blocks' if args.qk_block == 32 else ''}",
                    "global_batch": w.B, "seq_len": w.Nq, "parallelism": "single-gpu"},
         "roofline": ({"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                       "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
@@ -255,7 +259,8 @@ def main():
                       "peak": PEAK_HBM, "unit": "GB/s",
                       "frac": round(kbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM, 4),
                       "bytes_per_launch": kbytes}) | {
-                     "traffic": None if half or split else measured_traffic(w.name),
+                     "traffic": None if half or split or args.qk_block != 64
+                     else measured_traffic(w.name),
                      "kernel": f"k_attn (fused INT8-QK / softmax / {pvt.upper()}-PV)"
                                + (f" + k_merge ({nsplit} splits of {split} keys)" if split else ""),
                      "kernel_ms": round(kern_ms, 4), "ops_per_launch": exact},
@@ -264,7 +269,8 @@ def main():
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, args.pv)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, args.pv, split,
+                                            args.qk_block)
     print(json.dumps(line), flush=True)
 
 
