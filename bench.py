@@ -60,7 +60,6 @@ def _parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_causal_gqa_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "quantized_attention_03_amd", "csrc", "sage_attn.hip")
 
 
@@ -70,13 +69,13 @@ def kernel_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the fused kernel from the committed counter
-    summary, or None when it is missing, is for another workload, or was
-    taken on a different kernel source."""
+def measured_traffic(workload: str, kernel: str = "k_attn"):
+    """HBM bytes per launch of the kernel from the committed counter summary
+    profiles/<kernel>_<workload>_traffic.txt, or None when it is missing or
+    was taken on a different kernel source."""
     try:
         fields = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")) as f:
             for ln in f:
                 if ":" in ln and not ln.startswith("#"):
                     k, v = ln.split(":", 1)
@@ -230,6 +229,9 @@ def main():
     max_nkv = max(nkv for _, nkv in w.seq_lens())
     nsplit = math.ceil(max_nkv / split) if split else 1
     kbytes = kernel_bytes(w, args.pv, nsplit)
+    # a split key range whose GQA group x queries fit one wave's 32 rows runs
+    # the one-wave decode kernel
+    dec = bool(split) and (w.Hq // w.Hkv) * max(1, max(nq for nq, _ in w.seq_lens())) <= 32
     hbm_bound = exact / kbytes < peak * 1e12 / (PEAK_HBM * 1e9)
     io = "fp16 io" if w.dtype == "f16" else "bf16 io"
     pvt = ("f16" if w.dtype == "f16" else "bf16") if half else "fp8"
@@ -259,9 +261,14 @@ def main():
                       "peak": PEAK_HBM, "unit": "GB/s",
                       "frac": round(kbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM, 4),
                       "bytes_per_launch": kbytes}) | {
-                     "traffic": None if half or split or args.qk_block != 64
-                     else measured_traffic(w.name),
-                     "kernel": f"k_attn (fused INT8-QK / softmax / {pvt.upper()}-PV)"
+                     "traffic": (measured_traffic(w.name, "k_decode")
+                                 if dec and not half and args.kv_split == "auto"
+                                 and args.qk_block == 64 else
+                                 None if half or split or args.qk_block != 64
+                                 else measured_traffic(w.name)),
+                     "kernel": (f"k_decode (one wave per kv head and split, INT8-QK / "
+                                f"softmax / {pvt.upper()}-PV)" if dec else
+                                f"k_attn (fused INT8-QK / softmax / {pvt.upper()}-PV)")
                                + (f" + k_merge ({nsplit} splits of {split} keys)" if split else ""),
                      "kernel_ms": round(kern_ms, 4), "ops_per_launch": exact},
         "prepass_ms": round(pre_ms, 4),   # whole call minus the fused kernel

@@ -113,11 +113,17 @@ typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1 } sage_dtype;
  * in the input's 16-bit type (the first SageAttention's variant). */
 typedef enum { SAGE_PV_FP8 = 0, SAGE_PV_HALF = 1 } sage_pv_mode;
 
-/* kv_split value that lets the library choose the split: none while the
- * unsplit grid has at least 256 workgroups; otherwise splits of
- * max(4, ceil(tiles / ceil(512 / workgroups))) key tiles, where tiles is the
- * longest key range in SAGE_KV_TILE units (no split if that covers it).  The
- * choice depends on the problem only; sage_kv_split_size reports it. */
+/* kv_split value that lets the library choose the split.  tiles is the
+ * longest key range in SAGE_KV_TILE units; a split has
+ * max(4, ceil(tiles / want)) tiles, and none is made if that covers them.
+ * - Decode shapes (hq / hkv times the longest query count at most 32): these
+ *   run one wave per (sequence, kv head, split), and want = max(2,
+ *   floor(256 * w / (sequences * hkv))), where w = 4 waves per compute unit
+ *   (fewer when a wave's LDS stages do not fit four times in 160 KB: 3 for
+ *   16-bit V at head_dim 128).
+ * - Other shapes: no split while the unsplit grid has at least 256
+ *   workgroups; otherwise want = ceil(512 / workgroups).
+ * The choice depends on the problem only; sage_kv_split_size reports it. */
 #define SAGE_KV_SPLIT_AUTO (-1)
 
 /* HND = [batch, heads, tokens, head_dim]; NHD = [batch, tokens, heads, head_dim].

@@ -295,23 +295,38 @@ std::vector<KParams> make_params(const Plan& p) {
 }
 
 // The split of the key range.  An explicit kv_split is used as given (no
-// split when it covers the longest key range).  SAGE_KV_SPLIT_AUTO splits
-// only when the unsplit grid has fewer workgroups than MI355X has compute
-// units (256): it then aims at 512 workgroups, with at least 4 key tiles (512
-// keys) per split.  The rule depends on the problem only, never on the device
-// it runs on.
+// split when it covers the longest key range).  SAGE_KV_SPLIT_AUTO:
+// * decode shapes (GQA group x queries of every sequence within one wave's
+//   DEC_ROWS rows) run one wave per (sequence, kv head, split); the rule aims
+//   at one round of the grid, 256 compute units x decode_waves_per_cu waves
+//   (4 for FP8 V, 3 for 16-bit V at d = 128), and at least two splits, with
+//   at least 4 key tiles (512 keys) per split;
+// * other shapes split only when the unsplit grid has fewer workgroups than
+//   MI355X has compute units (256); it then aims at 512 workgroups, with at
+//   least 4 key tiles per split.
+// The rule depends on the problem only, never on the device it runs on.
 void resolve_split(Plan* p) {
     int32_t ks = 0;
     const int32_t tiles_max = (p->max_nkv + KVT - 1) / KVT;
+    int32_t max_nq = 0;
+    for (int s = 0; s < p->S; ++s) max_nq = std::max(max_nq, p->nq[s]);
     if (p->kv_split_req > 0) {
         ks = p->kv_split_req;
     } else if (p->kv_split_req == SAGE_KV_SPLIT_AUTO && tiles_max > 0) {
-        Plan tmp = *p;
-        tmp.kv_split = 0;
-        int64_t base = 0;
-        for (const KParams& P : make_params(tmp)) base += attn_base_wgs(P);
-        if (base > 0 && base < 256) {
-            const int64_t want = (512 + base - 1) / base;
+        int64_t want = 0;
+        if ((int64_t)p->group * std::max(max_nq, 1) <= DEC_ROWS) {
+            const int64_t units = (int64_t)p->S * p->hkv;
+            const int64_t round =
+                (int64_t)NUM_CU * decode_waves_per_cu(p->d, p->pv_half, p->smooth_q, p->group);
+            want = std::max<int64_t>(2, round / units);
+        } else {
+            Plan tmp = *p;
+            tmp.kv_split = 0;
+            int64_t base = 0;
+            for (const KParams& P : make_params(tmp)) base += attn_base_wgs(P);
+            if (base > 0 && base < 256) want = (512 + base - 1) / base;
+        }
+        if (want > 0) {
             const int32_t tps = std::max<int32_t>(4, (int32_t)((tiles_max + want - 1) / want));
             ks = tps * KVT;
         }

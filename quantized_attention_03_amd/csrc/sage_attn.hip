@@ -37,6 +37,7 @@
 //    phase runs at raised priority.
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
+#include <algorithm>
 #include <cfloat>
 
 #include "sage_internal.h"
@@ -797,6 +798,245 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
 }
 
 // ---------------------------------------------------------------------------
+// Decode kernel (a split key range with few queries): one wave per
+// workgroup and one (sequence, kv head, split) per wave.  The query heads of
+// the GQA group and their queries are packed into the wave's 32 rows (row r:
+// head hkv*G + r / nq, query r % nq; the host only uses it when G*nq <= 32),
+// so every row of the MFMA tile is a real query.  The wave stages its own
+// tiles in LDS: K(t+1) streams in under softmax(t), V(t) under Q.K(t).  The
+// tiles, the online softmax and the split partials are those of k_attn, so
+// the result is the same recipe.
+// ---------------------------------------------------------------------------
+__device__ inline void wait_vm(int n) {
+    switch (n) {
+#define SAGE_W(k) \
+    case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+        SAGE_W(0) SAGE_W(1) SAGE_W(2) SAGE_W(3) SAGE_W(4) SAGE_W(5) SAGE_W(6) SAGE_W(7)
+        SAGE_W(8) SAGE_W(9) SAGE_W(10) SAGE_W(11) SAGE_W(12) SAGE_W(13) SAGE_W(14) SAGE_W(15)
+        SAGE_W(16) SAGE_W(17) SAGE_W(18) SAGE_W(19) SAGE_W(20) SAGE_W(21) SAGE_W(22) SAGE_W(23)
+        SAGE_W(24) SAGE_W(25) SAGE_W(26) SAGE_W(27) SAGE_W(28) SAGE_W(29) SAGE_W(30) SAGE_W(31)
+        SAGE_W(32) SAGE_W(33) SAGE_W(34) SAGE_W(35) SAGE_W(36) SAGE_W(37) SAGE_W(38) SAGE_W(39)
+        SAGE_W(40) SAGE_W(41) SAGE_W(42) SAGE_W(43) SAGE_W(44) SAGE_W(45) SAGE_W(46) SAGE_W(47)
+        SAGE_W(48)
+#undef SAGE_W
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+// Bytes of one score-bias stage of a decode wave: G heads of 128 floats,
+// copied two heads (1 KB) at a time.
+__host__ __device__ constexpr int dec_ds_stage(int G) { return (G + 1) / 2 * 1024; }
+
+// LDS bytes of one decode wave: K and V^T stages and two score-bias stages.
+template <int D, bool HAS_DS, bool PVH>
+__host__ __device__ constexpr int dec_lds_bytes(int G) {
+    return Tile<D, PVH>::KBYTES + Tile<D, PVH>::VBYTES + (HAS_DS ? 2 * dec_ds_stage(G) : 0);
+}
+
+// Per-lane source offsets of one wave's 1 KB copies of a K tile and a V^T
+// tile into the LDS images described by Tile (dense rows, swizzled slots).
+// A copy spans 8 or 16 key rows (4 or 8 V^T rows), so the pattern of the key
+// permutation and swizzle (32 key rows, 16 V^T rows) takes KPER (VPER)
+// copies; later copies repeat it shifted by whole periods.  D = 96 copies
+// only the 96 V^T rows that the P.V reads.
+template <int D, bool PVH>
+struct WaveDma {
+    using T = Tile<D, PVH>;
+    static constexpr int KCOPIES = T::KBYTES / 1024;
+    static constexpr int VCOPIES = D * T::VRB / 1024;
+    static constexpr int KPER = 32 * T::KRS / 1024;
+    static constexpr int VPER = 16 * T::VRB / 1024;
+    static_assert(KCOPIES % KPER == 0 && VCOPIES % VPER == 0, "copy periods");
+    int k[KPER], v[VPER];
+
+    __device__ inline void init(int npk) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < KPER; ++i) {
+            const int o = 1024 * i + 16 * lane;
+            const int row = o / T::KRS, slot = (o % T::KRS) / 16;
+            int lg = slot ^ swz<T::KRS>(row);
+            if (D == 96 && lg >= 6) lg &= 1;       // unused slots: any in-row granule
+            k[i] = key_of_row(row) * D + lg * 16;
+        }
+#pragma unroll
+        for (int i = 0; i < VPER; ++i) {
+            const int o = 1024 * i + 16 * lane;
+            const int ch = o / T::VRB, vslot = (o % T::VRB) / 16;
+            v[i] = ch * npk * T::VES + ((vslot ^ swz<T::VRB>(ch)) << 4);
+        }
+    }
+    __device__ inline void stage_k(uint8_t* kst, const int8_t* kbase, int t) const {
+        const int8_t* kt = kbase + (int64_t)t * KVT * D;
+#pragma unroll
+        for (int i = 0; i < KCOPIES; ++i)
+            dma16(kt + k[i % KPER] + (i / KPER) * 32 * D, kst + 1024 * i);
+    }
+    __device__ inline void stage_v(uint8_t* vst, const uint8_t* vbase, int npk, int t) const {
+        const uint8_t* vt = vbase + t * (KVT * T::VES);
+#pragma unroll
+        for (int i = 0; i < VCOPIES; ++i)
+            dma16(vt + v[i % VPER] + (int64_t)(i / VPER) * 16 * npk * T::VES, vst + 1024 * i);
+    }
+};
+
+template <int D, int DT, bool HAS_DS, bool PVH, int QB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode(KParams P, const int8_t* __restrict__ qc,
+                                               const float* __restrict__ qsc,
+                                               const int8_t* __restrict__ kc,
+                                               const float* __restrict__ ksc,
+                                               const uint8_t* __restrict__ vc,
+                                               const float* __restrict__ vsc,
+                                               const float* __restrict__ ds,
+                                               const float* __restrict__ mu_v) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    using T = Tile<D, PVH>;
+    using O = WaveDma<D, PVH>;
+    int local;
+    auto per = [&](int) { return P.hkv * P.nsplit; };
+    const int s = find_seq(P, blockIdx.x, per, &local);
+    const SeqInfo si = seq_info(P, s);
+    const int split = local / P.hkv, hkv = local % P.hkv;   // kv head fastest
+    const int nq = si.nq, nkv = si.nkv;
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, qi = lane & 31;
+    const int G = P.group;
+    const bool row_ok = qi < G * nq;
+    const int hl = row_ok ? qi / nq : 0, my_q = row_ok ? qi % nq : 0;
+    const int head = hkv * G + hl;
+    const int diag = my_q + nkv - nq;             // last visible key of the row (causal)
+    const int lim = P.causal ? min(diag, nkv - 1) : nkv - 1;
+    const int diag0 = nkv - nq;                   // ... of the group's first query
+    const int nt_all = (nkv + KVT - 1) / KVT;
+    const int t0 = split * P.kv_tiles;
+    const int t1 = min(nt_all, t0 + P.kv_tiles);
+
+    const int64_t krow0 = (si.rk * P.hkv + (int64_t)hkv * si.npk);
+    const int8_t* kbase = kc + krow0 * D;
+    const uint8_t* vbase = vc + krow0 * D * T::VES;
+    const float* kscb = ksc + krow0 / QB;
+    const float* dsb = HAS_DS ? ds + si.rk * P.hq + (int64_t)(hkv * G) * si.npk : nullptr;
+    uint8_t* kbuf = smem;
+    uint8_t* vbuf = smem + T::KBYTES;
+    uint8_t* dsbuf = vbuf + T::VBYTES;            // two score-bias stages
+    O off;
+    off.init(si.npk);
+    const int nds = HAS_DS ? (G + 1) / 2 : 0;     // score-bias copies per tile
+    auto stage_ds = [&](int t, int which) {
+        if constexpr (HAS_DS) {
+            for (int i = 0; i < nds; ++i) {
+                const int hs = min(2 * i + h, G - 1);
+                dma16(dsb + (int64_t)hs * si.npk + t * KVT + qi * 4,
+                      dsbuf + which * dec_ds_stage(G) + i * 1024);
+            }
+        }
+    };
+
+    v4i qf[D / 32];
+    float sq = 0.0f;
+    const int64_t qrow0 = si.rq * P.hq + (int64_t)head * si.npq;
+    if (row_ok && t0 < t1) {
+        load_q<D>(qc + (qrow0 + my_q) * D, qf);
+        sq = qsc[(qrow0 + my_q) / QB];
+    } else {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) qf[c] = v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) asm volatile("" ::"v"(qf[c]));
+    asm volatile("" : "+v"(sq));
+
+    v16f acc[D / 32];
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+    v8i pb[2];
+    v4i ph[PVH ? 8 : 1];
+    v16i sacc[4];
+
+    // vmcnt counts at most 63 operations.  When K, its bias and V of a tile
+    // would exceed that (16-bit V with the bias of many heads), the wave
+    // waits for K(t) and its bias before issuing V(t), and issues the bias
+    // of tile t+1 only once V(t) has landed: at most V + K in flight.
+    const bool early = O::KCOPIES + nds + O::VCOPIES > 60;
+    if (t0 < t1) {
+        off.stage_k(kbuf, kbase, t0);
+        stage_ds(t0, 0);
+    }
+    for (int t = t0; t < t1; ++t) {
+        const int r = t - t0;
+        // V(t) streams in under Q.K(t) and softmax(t)
+        if (early) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        off.stage_v(vbuf, vbase, si.npk, t);
+        wait_vm(O::VCOPIES);                      // K(t) and its bias have landed
+        qk_tile<D>(kbuf, qf, sacc);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // K(t) reads done
+        int nnext = 0;
+        const bool more = t + 1 < t1;
+        if (more) {                               // K(t+1) streams in under the rest
+            off.stage_k(kbuf, kbase, t + 1);
+            if (!early) stage_ds(t + 1, (r + 1) & 1);
+            nnext = O::KCOPIES + (early ? 0 : nds);
+        }
+        constexpr int NB = KVT / QB;
+        auto cs = [&](int b) {
+            const float ks = kscb[NB * t + b];
+            return fmaxf(HAS_DS ? sq * ks : sq * ks * P.sml2, FLT_MIN);
+        };
+        const float c0 = cs(0), c1 = cs(1);
+        const float c2 = NB == 4 ? cs(NB == 4 ? 2 : 0) : 0.0f;
+        const float c3 = NB == 4 ? cs(NB == 4 ? 3 : 0) : 0.0f;
+        const int kt0 = t * KVT + 16 * h;
+        const float* dsl = HAS_DS ? reinterpret_cast<const float*>(dsbuf + (r & 1) * dec_ds_stage(G)) +
+                                        hl * KVT
+                                  : nullptr;
+        const bool need_mask = (t + 1) * KVT > nkv || (P.causal && (t + 1) * KVT - 1 > diag0);
+        float alpha;
+        if (need_mask)
+            alpha = softmax_tile<true, HAS_DS, PVH, DT, QB>(sacc, pb, ph, c0, c1, c2, c3, dsl,
+                                                            P.sml2, kt0, lim, m_run, l_run);
+        else
+            alpha = softmax_tile<false, HAS_DS, PVH, DT, QB>(sacc, pb, ph, c0, c1, c2, c3, dsl,
+                                                             P.sml2, kt0, lim, m_run, l_run);
+        wait_vm(nnext);                           // V(t) has landed
+        if (early && more) stage_ds(t + 1, (r + 1) & 1);
+        rescale<D>(acc, alpha);
+        if constexpr (PVH) pv_tile_h<D, DT>(vbuf, ph, acc);
+        else pv_tile<D>(vbuf, pb, acc);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // V(t) reads done
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // this split's partial of each row (as in k_attn's split epilogue)
+    const float l_tot = swap_sum(l_run);
+    if (row_ok) {
+        const int64_t row = si.lse0 + (int64_t)head * P.lse_hstride + my_q;
+        const int64_t pr = (int64_t)split * P.rows_total + row;
+        const int64_t vsb = ((int64_t)si.sid * P.hkv + hkv) * D;
+        const bool add_mu = mu_v && l_tot > 0.0f;
+        float* po = P.part_o + pr * D;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int ch0 = 32 * c + 8 * r4 + 4 * h;
+                const float4 s4 = PVH ? make_float4(1.f, 1.f, 1.f, 1.f)
+                                      : *reinterpret_cast<const float4*>(vsc + vsb + ch0);
+                const float4 m4 = add_mu ? *reinterpret_cast<const float4*>(mu_v + vsb + ch0)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+                *reinterpret_cast<float4*>(po + ch0) =
+                    make_float4(fmaf(acc[c][4 * r4], s4.x, m4.x * l_tot),
+                                fmaf(acc[c][4 * r4 + 1], s4.y, m4.y * l_tot),
+                                fmaf(acc[c][4 * r4 + 2], s4.z, m4.z * l_tot),
+                                fmaf(acc[c][4 * r4 + 3], s4.w, m4.w * l_tot));
+            }
+        if (h == 0) *reinterpret_cast<float2*>(P.part_ml + 2 * pr) = make_float2(m_run, l_tot);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Q.K^T dump for tests: the same key-tile staging and qk_tile as the fused
 // kernel (4-wave workgroups); the int32 scores are written instead of used.
 // ---------------------------------------------------------------------------
@@ -886,14 +1126,60 @@ hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const in
     return hipGetLastError();
 }
 
+template <int D, int DT, bool HAS_DS, bool PVH, int QB>
+hipError_t decode_d(const KParams& P, const int8_t* qc, const float* qsc, const int8_t* kc,
+                    const float* ksc, const uint8_t* vc, const float* vsc, const float* ds,
+                    const float* mu_v, hipStream_t st) {
+    static bool attr_set = false;   // benign race: the call is idempotent
+    if (!attr_set) {
+        hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<D, DT, HAS_DS, PVH, QB>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                dec_lds_bytes<D, HAS_DS, PVH>(32));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int nblocks = P.tab.n * P.hkv * P.nsplit;
+    if (nblocks <= 0) return hipSuccess;
+    k_decode<D, DT, HAS_DS, PVH, QB><<<nblocks, 64, dec_lds_bytes<D, HAS_DS, PVH>(P.group), st>>>(
+        P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+int decode_waves_per_cu(int d, bool pv_half, bool has_ds, int group) {
+    int b;
+#define SAGE_DL(D)                                                                        \
+    b = pv_half ? (has_ds ? dec_lds_bytes<D, true, true>(group) : dec_lds_bytes<D, false, true>(group)) \
+                : (has_ds ? dec_lds_bytes<D, true, false>(group) : dec_lds_bytes<D, false, false>(group))
+    if (d == 64) SAGE_DL(64);
+    else if (d == 96) SAGE_DL(96);
+    else SAGE_DL(128);
+#undef SAGE_DL
+    return std::max(1, std::min(4, LDS_PER_CU / b));
+}
+
+bool use_decode_kernel(const KParams& P) {
+    if (P.kv_tiles <= 0) return false;
+    int mq = 0;
+    const int n = P.tab.uniform ? 1 : P.tab.n;
+    for (int s = 0; s < n; ++s) mq = std::max(mq, P.tab.nq[s]);
+    return P.group * std::max(mq, 1) <= DEC_ROWS;
+}
 
 hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const float* qsc,
                        const int8_t* kc, const float* ksc, const uint8_t* vc, const float* vsc,
                        const float* ds, const float* mu_v, void* o, float* lse, hipStream_t st) {
+    const bool dec = use_decode_kernel(P);
 #define SAGE_AQ(D, DT, PVH, QB)                                                                  \
-    return ds ? attn_d<D, DT, true, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st) \
-              : attn_d<D, DT, false, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st)
+    do {                                                                                         \
+        if (dec)                                                                                 \
+            return ds ? decode_d<D, DT, true, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, st) \
+                      : decode_d<D, DT, false, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, st); \
+        return ds ? attn_d<D, DT, true, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st) \
+                  : attn_d<D, DT, false, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st); \
+    } while (0)
 #define SAGE_AH(D, DT, PVH)                    \
     do {                                       \
         if (P.qb == 32) SAGE_AQ(D, DT, PVH, 32); \
@@ -935,44 +1221,72 @@ hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, 
 // ---------------------------------------------------------------------------
 // Merge of a split key range (flash-decoding): per row, M = max m_s,
 // w_s = 2^(m_s - M), L = sum w_s l_s, o = sum w_s part_s / L, the partials
-// already holding acc*v_scale + mu_v*l.  One thread per 8 channels of a row.
+// already holding acc*v_scale + mu_v*l.  One wave per row: lane j first takes
+// the (m, l) of splits j, j+64, ..., then the wave walks the splits in order
+// with each lane accumulating two channels (coalesced 8-byte reads of every
+// partial row).  Every split writes its partial (zeros and m = -inf when it
+// saw no key), so the loads need no guard.
 // ---------------------------------------------------------------------------
+__device__ inline float wave_max64(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ inline float wave_sum64(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
-    const int gpr = M.d / 8;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = gid / gpr;
-    if (row >= M.rows_total) return;
-    const int c0 = (int)(gid % gpr) * 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M.rows_total) return;             // the whole wave leaves
+    const int64_t rs = M.rows_total;
     float mx = -INFINITY;
-    for (int sp = 0; sp < M.nsplit; ++sp)
-        mx = fmaxf(mx, M.part_ml[2 * ((int64_t)sp * M.rows_total + row)]);
-    float L = 0.0f, a[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = 0.0f;
+    for (int s0 = 0; s0 < M.nsplit; s0 += 64)
+        if (s0 + lane < M.nsplit) mx = fmaxf(mx, M.part_ml[2 * ((s0 + lane) * rs + row)]);
+    mx = wave_max64(mx);
+    const int c0 = 2 * lane;
+    const bool act = c0 < M.d;
+    float lp = 0.0f, a0 = 0.0f, a1 = 0.0f;
     if (mx != -INFINITY) {
-        for (int sp = 0; sp < M.nsplit; ++sp) {
-            const int64_t pr = (int64_t)sp * M.rows_total + row;
-            const float2 ml = *reinterpret_cast<const float2*>(M.part_ml + 2 * pr);
-            if (ml.x == -INFINITY) continue;     // a split without visible keys
-            const float wgt = __builtin_amdgcn_exp2f(ml.x - mx);
-            L = fmaf(wgt, ml.y, L);
-            const float4 p0 = *reinterpret_cast<const float4*>(M.part_o + pr * M.d + c0);
-            const float4 p1 = *reinterpret_cast<const float4*>(M.part_o + pr * M.d + c0 + 4);
-            a[0] = fmaf(wgt, p0.x, a[0]);
-            a[1] = fmaf(wgt, p0.y, a[1]);
-            a[2] = fmaf(wgt, p0.z, a[2]);
-            a[3] = fmaf(wgt, p0.w, a[3]);
-            a[4] = fmaf(wgt, p1.x, a[4]);
-            a[5] = fmaf(wgt, p1.y, a[5]);
-            a[6] = fmaf(wgt, p1.z, a[6]);
-            a[7] = fmaf(wgt, p1.w, a[7]);
+        for (int s0 = 0; s0 < M.nsplit; s0 += 64) {
+            float wl = 0.0f;
+            if (s0 + lane < M.nsplit) {
+                const float2 ml = *reinterpret_cast<const float2*>(M.part_ml + 2 * ((s0 + lane) * rs + row));
+                wl = ml.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml.x - mx);
+                lp = fmaf(wl, ml.y, lp);
+            }
+            const int cnt = min(64, M.nsplit - s0);
+            const float* po = M.part_o + ((int64_t)s0 * rs + row) * M.d + c0;
+            const int64_t step = rs * M.d;
+            int j = 0;
+            for (; j + 4 <= cnt; j += 4) {
+                float2 p[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    p[u] = act ? *reinterpret_cast<const float2*>(po + (j + u) * step)
+                               : make_float2(0.f, 0.f);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float w = __shfl(wl, j + u);
+                    a0 = fmaf(w, p[u].x, a0);
+                    a1 = fmaf(w, p[u].y, a1);
+                }
+            }
+            for (; j < cnt; ++j) {
+                const float2 p = act ? *reinterpret_cast<const float2*>(po + j * step)
+                                     : make_float2(0.f, 0.f);
+                const float w = __shfl(wl, j);
+                a0 = fmaf(w, p.x, a0);
+                a1 = fmaf(w, p.y, a1);
+            }
         }
     }
+    const float L = wave_sum64(lp);
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    uint32_t bits[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bits[e] = f2h_bits<DT>(a[e] * inv);
     int64_t off;
     if (M.varlen) {
         const int64_t h = row / M.total_q, tok = row % M.total_q;
@@ -982,19 +1296,18 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
         const int64_t sidx = row / per_seq, rem = row % per_seq;
         off = sidx * M.os.b + (rem / M.nq) * M.os.h + (rem % M.nq) * M.os.n;
     }
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(M.o) + off + c0) =
-        make_uint4(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16),
-                   bits[4] | (bits[5] << 16), bits[6] | (bits[7] << 16));
-    if (c0 == 0 && M.lse)
+    if (act)
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(M.o) + off + c0) =
+            f2h_bits<DT>(a0 * inv) | (f2h_bits<DT>(a1 * inv) << 16);
+    if (lane == 0 && M.lse)
         M.lse[row] = L > 0.0f ? (mx + __log2f(L) - M.poff) * LN2 : -INFINITY;
 }
 
 int attn_base_wgs(const KParams& P) { return wg_count_host(P, FWD_WAVES); }
 
 hipError_t launch_merge(const MergeArgs& M, int dtype, hipStream_t st) {
-    const int64_t threads = M.rows_total * (M.d / 8);
-    if (threads <= 0) return hipSuccess;
-    const int64_t nb = (threads + 255) / 256;
+    if (M.rows_total <= 0) return hipSuccess;
+    const int64_t nb = (M.rows_total + 3) / 4;   // four rows (waves) per workgroup
     if (dtype == 0) k_merge<0><<<(unsigned)nb, 256, 0, st>>>(M);
     else k_merge<1><<<(unsigned)nb, 256, 0, st>>>(M);
     return hipGetLastError();

@@ -9,6 +9,9 @@ namespace sage {
 
 constexpr int QBLK = 64;      // Q/K quantization block (tokens)
 constexpr int KVT = 128;      // key tile of the fused kernel (tokens)
+constexpr int DEC_ROWS = 32;  // query rows of one wave of the decode kernel
+constexpr int LDS_PER_CU = 160 * 1024;   // LDS bytes of one MI355X compute unit
+constexpr int NUM_CU = 256;               // compute units of MI355X
 constexpr int MAXSEQ = 32;    // sequences described per launch
 constexpr int WG = 256;       // threads per workgroup of every kernel
 
@@ -181,6 +184,14 @@ hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const floa
                        float* lse, hipStream_t st);
 // Workgroups of one fused-kernel launch before any key split.
 int attn_base_wgs(const KParams& P);
+// Whether a split launch runs the one-wave decode kernel: every sequence's
+// GQA group times its queries fits the DEC_ROWS rows of one wave.
+bool use_decode_kernel(const KParams& P);
+// Waves of the decode kernel to place on one compute unit at once: at most
+// one per SIMD (a fifth wave per unit, which the LDS would hold with FP8 V at
+// d = 128, measured slower on the 32K-key decode workload), fewer when the
+// LDS stages of a wave do not fit four times.
+int decode_waves_per_cu(int d, bool pv_half, bool has_ds, int group);
 hipError_t launch_merge(const MergeArgs& M, int dtype, hipStream_t st);
 struct DumpBase {
     int64_t base[MAXSEQ];               // first element of sequence s in the dump

@@ -203,16 +203,30 @@ def _split(d, cuq=None, cuk=None, n=0):
 
 def test_kv_split_rule():
     """Explicit splits are used as given unless they cover the longest key
-    range; the automatic rule splits only grids below 256 workgroups."""
+    range.  The automatic rule: decode shapes (GQA group x queries <= 32)
+    aim at one round of one-wave units (256 compute units x 4 waves, or 3
+    for 16-bit V at d = 128, whose LDS stages fit only three times) and at
+    least two splits; other shapes split only grids below 256 workgroups,
+    aiming at 512; at least 4 key tiles per split either way."""
     assert _split(_desc(nkv=1000, kv_split=256)) == ("SAGE_OK", 256)
     assert _split(_desc(nkv=1000, kv_split=1024)) == ("SAGE_OK", 0)
     assert _split(_desc(nkv=1000)) == ("SAGE_OK", 0)
-    # decode: B=2, hq=8 (group 4 -> one workgroup per kv head), nq=1:
-    # 2 * 2 workgroups, so ceil(512 / 4) = 128 splits wanted, at least 4
-    # tiles each: 32768 keys = 256 tiles -> 4 tiles = 512 keys
+    # decode: B=2, hkv=2, group 4, nq=1 -> 4 units, 1024 / 4 = 256 splits
+    # wanted, at least 4 tiles each: 32768 keys = 256 tiles -> 512 keys
     assert _split(_desc(nq=1, nkv=32768, kv_split=-1)) == ("SAGE_OK", 512)
-    # 16 tiles in all: max(4, ceil(16 / 128)) = 4 tiles
+    # 16 tiles in all: max(4, ceil(16 / 256)) = 4 tiles
     assert _split(_desc(nq=1, nkv=2048, kv_split=-1)) == ("SAGE_OK", 512)
+    # the decode workload: 8 x 8 = 64 units -> 1024 / 64 = 16 splits of
+    # 256 / 16 = 16 tiles; with 16-bit V 768 / 64 = 12 -> ceil(256 / 12) = 22
+    assert _split(_desc(batch=8, hq=32, hkv=8, nq=1, nkv=32768, kv_split=-1)) == ("SAGE_OK", 2048)
+    assert _split(_desc(batch=8, hq=32, hkv=8, nq=1, nkv=32768, kv_split=-1, pv_mode=1)) == \
+        ("SAGE_OK", 2816)
+    # many units: still two splits (ceil(256 / 2) = 128 tiles)
+    assert _split(_desc(batch=512, hq=32, hkv=8, nq=1, nkv=32768, kv_split=-1)) == \
+        ("SAGE_OK", 16384)
+    # group 4 x 9 queries = 36 rows: the fused kernel's rule, 2 * 2 workgroups
+    # -> 128 splits wanted -> 4 tiles
+    assert _split(_desc(nq=9, nkv=32768, kv_split=-1)) == ("SAGE_OK", 512)
     # a prefill grid (well over 256 workgroups) is not split
     assert _split(_desc(batch=4, hq=32, hkv=32, nq=4096, nkv=4096, kv_split=-1)) == ("SAGE_OK", 0)
     # keys that fit one split: no split

@@ -2,9 +2,11 @@
 each split an online softmax of its own, merged by the log-sum-exp rule)
 through the C ABI, against the oracle's split recipe.
 
-* few queries against long key ranges (decode shapes), GQA, d 64/96/128,
-  causal and not, every smoothing flag, varlen with empty sequences, both P.V
-  modes, explicit and automatic splits;
+* few queries against long key ranges (decode shapes, where a GQA group's
+  heads and queries fill one wave's 32 rows), GQA, d 64/96/128, causal and
+  not, every smoothing flag, varlen with empty sequences, both P.V modes,
+  explicit and automatic splits, and shapes too large for one wave (the
+  fused kernel's split);
 * the LSE equals the unsplit oracle's (it does not depend on the split);
 * the kernel-only entry point reproduces the full call; runs are
   deterministic;
@@ -42,6 +44,21 @@ CASES = {
                        seqlens_kv=[700, 40, 1, 0]), 256, "fp8"),
     "split_wider_than_keys": (R(W["decode_gqa"], B=1, Hq=4, Hkv=4, Nq=4, Nkv=200, seed=27),
                               1024, "fp8"),
+    # the one-wave decode kernel at its limits: an odd GQA group with the
+    # score bias (Q smoothing), a full wave of 32 rows with the 16-bit P.V
+    # and the bias (the copies that exceed the wave's counter budget), d 96
+    # with 32 rows, d 64 in the 16-bit mode, and a shape one row too large
+    # for it (the fused kernel then takes the split)
+    "decode_g3_smooth_q": (R(W["video_dit"], B=1, Hq=6, Hkv=2, Nq=2, Nkv=900, d=128, seed=28,
+                             layout="HND"), 256, "fp8"),
+    "decode_rows32_half_ds": (R(W["video_dit"], B=1, Hq=32, Hkv=1, Nq=1, Nkv=700, d=128,
+                                seed=29, layout="HND"), 256, "half"),
+    "decode_rows32_d96": (R(W["decode_gqa"], B=1, Hq=16, Hkv=2, Nq=4, Nkv=1000, d=96, seed=30),
+                          384, "fp8"),
+    "decode_d64_half": (R(W["decode_gqa"], B=2, Hq=4, Hkv=2, Nq=1, Nkv=600, d=64, seed=31),
+                        128, "half"),
+    "rows33_fused_split": (R(W["decode_gqa"], B=1, Hq=3, Hkv=1, Nq=11, Nkv=700, seed=32),
+                           256, "fp8"),
 }
 
 
