@@ -381,6 +381,9 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
         const int kblocks = stat_blocks(P, false, p.hkv);
         const int qblocks = stat_blocks(P, true, p.hq);
         const int nseq = tab_seqs(P);
+        // finalize workgroups: one per sequence, head and FIN_CH channels
+        const int fin_wgs = nseq * p.hkv * (p.d / FIN_CH);
+        const int fin_wgs_q = nseq * p.hq * (p.d / FIN_CH);
         // 1. chunk statistics: the means that are needed, and the absolute
         //    maxima of V when V is not smoothed (else they need mu_v first)
         StatJobs sj{};
@@ -389,22 +392,22 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
         if (p.smooth_k) {
             sj.j[n] = StatJob{static_cast<const uint16_t*>(k), P.ks, nullptr, part_k, 1, p.hkv,
                               STAT_SUM, kblocks};
-            fj.j[n++] = FinJob{part_k, b.mu_k, nullptr, nullptr, 0, p.hkv, STAT_SUM, nseq * p.hkv};
+            fj.j[n++] = FinJob{part_k, b.mu_k, nullptr, nullptr, 0, p.hkv, STAT_SUM, fin_wgs};
         }
         if (p.smooth_q) {
             sj.j[n] = StatJob{static_cast<const uint16_t*>(q), P.qs, nullptr, part_q, 0, p.hq,
                               STAT_SUM, qblocks};
-            fj.j[n++] = FinJob{part_q, b.mu_q, nullptr, nullptr, 1, p.hq, STAT_SUM, nseq * p.hq};
+            fj.j[n++] = FinJob{part_q, b.mu_q, nullptr, nullptr, 1, p.hq, STAT_SUM, fin_wgs_q};
         }
         if (p.smooth_v) {
             sj.j[n] = StatJob{static_cast<const uint16_t*>(v), P.vs, nullptr, part_v, 2, p.hkv,
                               STAT_SUM, kblocks};
-            fj.j[n++] = FinJob{part_v, b.mu_v, nullptr, nullptr, 0, p.hkv, STAT_SUM, nseq * p.hkv};
+            fj.j[n++] = FinJob{part_v, b.mu_v, nullptr, nullptr, 0, p.hkv, STAT_SUM, fin_wgs};
         } else if (!p.pv_half) {
             sj.j[n] = StatJob{static_cast<const uint16_t*>(v), P.vs, nullptr, part_vmax, 2, p.hkv,
                               STAT_ABSMAX, kblocks};
             fj.j[n++] = FinJob{part_vmax, nullptr, v_amax, b.v_scale, 0, p.hkv, STAT_ABSMAX,
-                               nseq * p.hkv};
+                               fin_wgs};
         }
         SAGE_TRY(launch_stats(P, dtype, sj, st));
         SAGE_TRY(launch_finalize(P, fj, st));
@@ -415,7 +418,7 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
                               STAT_ABSMAX, kblocks};
             FinJobs fv{};
             fv.j[0] = FinJob{part_vmax, nullptr, v_amax, b.v_scale, 0, p.hkv, STAT_ABSMAX,
-                             nseq * p.hkv};
+                             fin_wgs};
             SAGE_TRY(launch_stats(P, dtype, sv, st));
             SAGE_TRY(launch_finalize(P, fv, st));
         }
@@ -436,7 +439,9 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
         qa.delta_s = p.smooth_q ? b.delta_s : nullptr;
         qa.nq = chunk_blocks(P, true, p.hq, true);
         qa.nk = chunk_blocks(P, false, p.hkv, true);
-        qa.nv = chunk_blocks(P, false, p.hkv, true);
+        // 16-bit V: 64-token chunks (128-byte rows already); E4M3 V: one
+        // 128-token key tile per workgroup
+        qa.nv = chunk_blocks(P, false, p.hkv, true) / (p.pv_half ? 1 : KVT / QBLK);
         qa.v_half = p.pv_half;
         SAGE_TRY(launch_quant(P, dtype, qa, st));
     }

@@ -12,6 +12,7 @@ constexpr int KVT = 128;      // key tile of the fused kernel (tokens)
 constexpr int DEC_ROWS = 32;  // query rows of one wave of the decode kernel
 constexpr int LDS_PER_CU = 160 * 1024;   // LDS bytes of one MI355X compute unit
 constexpr int NUM_CU = 256;               // compute units of MI355X
+constexpr int FIN_CH = 32;                // channels per statistics-finalize workgroup
 constexpr int MAXSEQ = 32;    // sequences described per launch
 constexpr int WG = 256;       // threads per workgroup of every kernel
 

@@ -176,38 +176,77 @@ __global__ __launch_bounds__(WG) void k_stats(KParams P, StatJobs J) {
 // ---------------------------------------------------------------------------
 // Finalize per (sequence, head, channel).  STAT_SUM: mu = (chunk sums added in
 // chunk order) / n.  STAT_ABSMAX: amax = max of the chunk maxima and
-// scale = amax / 448.  The workgroup first copies up to 64 chunks of partials
-// into LDS (all loads in flight at once); thread c then combines its
-// channel's values strictly in chunk order.
+// scale = amax / 448.  A workgroup owns FIN_CH channels of one (sequence,
+// head): it copies up to FIN_ROUND chunks of their partials into LDS with
+// every load in flight at once, transposed so that each channel's values are
+// contiguous, and thread c then combines channel c's values strictly in chunk
+// order, four per LDS read.  Narrow channel slices keep the rounds few (one
+// up to 28K tokens) and the workgroups many.
 // ---------------------------------------------------------------------------
-constexpr int FIN_CHUNKS = 64;
+constexpr int FIN_ROUND = 448;              // chunks per LDS round (57 KB)
 
 template <int MODE>
 __device__ inline void finalize_one(const KParams& P, const FinJob& J, int blk, float* lds) {
-    const int s = blk / J.heads, h = blk % J.heads;
-    const int c = threadIdx.x;
     const int d = P.d;
+    const int ns = d / FIN_CH;
+    const int sh = blk / ns, slice = blk % ns;
+    const int s = sh / J.heads, h = sh % J.heads;
+    const int c = threadIdx.x;
     const SeqInfo si = seq_info(P, s);
     const int n = J.is_q ? si.nq : si.nkv;
     const int nch = (n + QBLK - 1) / QBLK;
     const int64_t base = (J.is_q ? si.rq : si.rk) / QBLK * J.heads +
                          (int64_t)h * ((J.is_q ? si.npq : si.npk) / QBLK);
-    const float4* src = reinterpret_cast<const float4*>(J.partial + base * d);
+    const float* src = J.partial + base * d + slice * FIN_CH;
+    constexpr int G4 = FIN_CH / 4;          // float4 per chunk row of the slice
+    constexpr int PER = FIN_ROUND * G4 / WG;
     float acc = 0.0f;
-    for (int g0 = 0; g0 < nch; g0 += FIN_CHUNKS) {
-        const int cnt = min(FIN_CHUNKS, nch - g0);
+    for (int g0 = 0; g0 < nch; g0 += FIN_ROUND) {
+        const int cnt = min(FIN_ROUND, nch - g0);
+        float4 v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * WG;   // chunk idx / G4, float4 idx % G4
+            if (idx < cnt * G4)
+                v[i] = *reinterpret_cast<const float4*>(src + (int64_t)(g0 + idx / G4) * d +
+                                                        4 * (idx % G4));
+        }
+        __syncthreads();                    // the previous round's sums are done
+        // transposed image: channel row cc holds the round's chunks j at
+        // lds[cc * (FIN_ROUND + 4) + j]
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * WG;
+            if (idx < cnt * G4) {
+                const int j = idx / G4, c4 = 4 * (idx % G4);
+                lds[(c4 + 0) * (FIN_ROUND + 4) + j] = v[i].x;
+                lds[(c4 + 1) * (FIN_ROUND + 4) + j] = v[i].y;
+                lds[(c4 + 2) * (FIN_ROUND + 4) + j] = v[i].z;
+                lds[(c4 + 3) * (FIN_ROUND + 4) + j] = v[i].w;
+            }
+        }
         __syncthreads();
-        for (int i = threadIdx.x; i < cnt * d / 4; i += WG) reinterpret_cast<float4*>(lds)[i] = src[g0 * d / 4 + i];
-        __syncthreads();
-        if (c < d) {
-            for (int j = 0; j < cnt; ++j) {
-                if constexpr (MODE == STAT_SUM) acc = acc + lds[j * d + c];
-                else acc = fmaxf(acc, lds[j * d + c]);
+        if (c < FIN_CH) {
+            const float* row = lds + c * (FIN_ROUND + 4);
+            int j = 0;
+            for (; j + 16 <= cnt; j += 16) {
+                float4 t[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) t[u] = *reinterpret_cast<const float4*>(row + j + 4 * u);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if constexpr (MODE == STAT_SUM) acc = (((acc + t[u].x) + t[u].y) + t[u].z) + t[u].w;
+                    else acc = fmaxf(fmaxf(fmaxf(fmaxf(acc, t[u].x), t[u].y), t[u].z), t[u].w);
+                }
+            }
+            for (; j < cnt; ++j) {
+                if constexpr (MODE == STAT_SUM) acc = acc + row[j];
+                else acc = fmaxf(acc, row[j]);
             }
         }
     }
-    if (c >= d) return;
-    const int64_t o = ((int64_t)si.sid * J.heads + h) * d + c;
+    if (c >= FIN_CH) return;
+    const int64_t o = ((int64_t)si.sid * J.heads + h) * d + slice * FIN_CH + c;
     if constexpr (MODE == STAT_SUM) {
         J.out_mu[o] = n > 0 ? acc / (float)n : 0.0f;
     } else {
@@ -221,9 +260,10 @@ __device__ inline void finalize_job(const KParams& P, const FinJob& J, int blk, 
     else finalize_one<STAT_ABSMAX>(P, J, blk, lds);
 }
 
-// Up to three finalize jobs (one workgroup per sequence and head each).
+// Up to three finalize jobs (one workgroup per sequence, head and FIN_CH
+// channels each).
 __global__ __launch_bounds__(WG) void k_finalize(KParams P, FinJobs J) {
-    __shared__ __align__(16) float lds[FIN_CHUNKS * 128];
+    __shared__ __align__(16) float lds[(FIN_ROUND + 4) * FIN_CH];
     int blk = blockIdx.x;
     if (blk < J.j[0].nblocks) { finalize_job(P, J.j[0], blk, lds); return; }
     blk -= J.j[0].nblocks;
@@ -353,13 +393,26 @@ __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// E4M3 quantization of one 64-token chunk of V, written channel-major
-// (V^T, so that the P.V operand of the fused kernel reads contiguous keys).
-// Codes pass through LDS for the transpose; chunks past the sequence end and
-// tokens past it get zero codes.
+// E4M3 quantization of one 128-token chunk of V (one key tile), written
+// channel-major (V^T, so that the P.V operand of the fused kernel reads
+// contiguous keys).  Codes pass through LDS for the transpose, and each
+// channel's 128 codes leave as one whole 128-byte row segment (64-byte
+// segments write measurably slower).  Tokens past the sequence end get zero
+// codes.
 // ---------------------------------------------------------------------------
+constexpr int VQT = KVT;                     // tokens per E4M3 V chunk
+
 template <int D>
-constexpr int quant_v_lds_bytes() { return D * (QBLK + 4); }
+constexpr int quant_v_lds_bytes() { return D * (VQT + 4); }
+
+// Workgroups sequence s owns in the E4M3 V launch: heads x padded tiles.
+struct VTileCount {
+    const KParams* P;
+    __device__ int operator()(int s) const {
+        const int n = P->tab.uniform ? P->tab.nkv[0] : P->tab.nkv[s];
+        return P->hkv * (round_up(n, KVT) / VQT);
+    }
+};
 
 template <int DT, int D>
 __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restrict__ v,
@@ -367,22 +420,22 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
                                      const float* __restrict__ amax,
                                      uint8_t* __restrict__ codes, int blkid, uint8_t* tr) {
     constexpr int GPR = D / 8;               // 8-channel granules of a token row
-    constexpr int TASKS = GPR * (QBLK / 4);  // (granule, group of 4 tokens) pairs
-    constexpr int TS = QBLK + 4;             // LDS bytes per channel row of the transpose
+    constexpr int TASKS = GPR * (VQT / 4);   // (granule, group of 4 tokens) pairs
+    constexpr int TS = VQT + 4;              // LDS bytes per channel row of the transpose
 
     int local;
-    ChunkCount cnt{&P, false, P.hkv, 1};
+    VTileCount cnt{&P};
     const int s = find_seq(P, blkid, cnt, &local);
     const SeqInfo si = seq_info(P, s);
     const int n = si.nkv;
-    const int nch = si.npk / QBLK;
+    const int nch = si.npk / VQT;
     const int h = local / nch, chk = local % nch;
     const int64_t el0 = si.v_el + (int64_t)h * P.vs.h;
     const float* muh = mu ? mu + ((int64_t)si.sid * P.hkv + h) * D : nullptr;
     const float* amh = amax + ((int64_t)si.sid * P.hkv + h) * D;
 
-    // Each task reads 4 consecutive tokens of one granule (the 16 granules of
-    // a row are read by consecutive lanes) and leaves, per channel, the 4
+    // Each task reads 4 consecutive tokens of one granule (the granules of a
+    // row are read by consecutive lanes) and leaves, per channel, the 4
     // codes as one 32-bit word of the channel's LDS row.
     for (int task = threadIdx.x; task < TASKS; task += WG) {
         const int cg = 8 * (task % GPR), tq = task / GPR;
@@ -398,7 +451,7 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
         for (int e = 0; e < 8; ++e) word[e] = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int t = chk * QBLK + 4 * tq + u;
+            const int t = chk * VQT + 4 * tq + u;
             if (t >= n) continue;                  // tokens past the end: zero codes
             float val[8];
             load8<DT>(v + el0 + (int64_t)t * P.vs.n + cg, val);
@@ -418,12 +471,12 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
         for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(tr + (cg + e) * TS + 4 * tq) = word[e];
     }
     __syncthreads();
-    // store: channel c, 64 bytes = 4 x 16 B
+    // store: channel c, 128 bytes = 8 x 16 B
     const int64_t vrow = (si.rk * P.hkv + (int64_t)h * si.npk) * D;
-    for (int idx = threadIdx.x; idx < D * 4; idx += WG) {
-        const int c = idx / 4, part = idx % 4;
+    for (int idx = threadIdx.x; idx < D * (VQT / 16); idx += WG) {
+        const int c = idx / (VQT / 16), part = idx % (VQT / 16);
         const uint32_t* src = reinterpret_cast<const uint32_t*>(tr + c * TS + part * 16);
-        *reinterpret_cast<uint4*>(codes + vrow + (int64_t)c * si.npk + chk * QBLK + part * 16) =
+        *reinterpret_cast<uint4*>(codes + vrow + (int64_t)c * si.npk + chk * VQT + part * 16) =
             make_uint4(src[0], src[1], src[2], src[3]);
     }
 }
