@@ -59,6 +59,12 @@ CASES = {
                         128, "half"),
     "rows33_fused_split": (R(W["decode_gqa"], B=1, Hq=3, Hkv=1, Nq=11, Nkv=700, seed=32),
                            256, "fp8"),
+    # more than 64 splits: the merge walks its splits 64 per pass (71 here),
+    # after the one-wave kernel and after the fused kernel's split
+    "many_splits_decode": (R(W["decode_gqa"], B=1, Hq=4, Hkv=2, Nq=1, Nkv=9000, seed=33),
+                           128, "fp8"),
+    "many_splits_fused": (R(W["decode_gqa"], B=1, Hq=4, Hkv=1, Nq=9, Nkv=9000, seed=34),
+                          128, "fp8"),
 }
 
 
