@@ -10,7 +10,8 @@ through the C ABI, against the oracle's split recipe.
 * the LSE equals the unsplit oracle's (it does not depend on the split);
 * the kernel-only entry point reproduces the full call; runs are
   deterministic;
-* the decode workload at full size (8 x 32 heads, one query, 32K keys).
+* the decode workload at full size (8 x 32 heads, one query, 32K keys), both
+  P.V modes.
 """
 import numpy as np
 import pytest
@@ -163,16 +164,19 @@ def test_split_quantized_entry_and_determinism(case):
     assert torch.equal(l1.view(torch.int32), l3.view(torch.int32))
 
 
-def test_decode_full_size_split():
+@pytest.mark.parametrize("pv", ["fp8", "half"])
+def test_decode_full_size_split(pv):
+    """The decode workload at full size in the launch configuration bench.py
+    times (automatic split, one-wave decode kernel), both P.V modes."""
     w = W["decode_gqa"]
-    pu.say("[split full size decode_gqa] generating inputs")
+    pu.say(f"[split full size decode_gqa {pv}] generating inputs")
     q, k, v, meta = pu.gpu_inputs(w)
-    eff = _effective_split(w, q, k, v, meta, "auto", "fp8")
+    eff = _effective_split(w, q, k, v, meta, "auto", pv)
     assert eff > 0
-    prob = orc.problem_from_workload(w, "fp8", eff)
+    prob = orc.problem_from_workload(w, pv, eff)
     qh, kh, vh = pu.u16(q), pu.u16(k), pu.u16(v)
-    pu.say(f"[split full size decode_gqa] split {eff}")
-    o, lse = _run(w, q, k, v, meta, "auto", "fp8")
+    pu.say(f"[split full size decode_gqa {pv}] split {eff}")
+    o, lse = _run(w, q, k, v, meta, "auto", pv)
     torch.cuda.synchronize()
     got = pu.gpu_out_per_seq(w, o, meta)
     ref = orc.prepass(prob, qh, kh, vh)
