@@ -436,8 +436,26 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
 
     // Each task reads 4 consecutive tokens of one granule (the granules of a
     // row are read by consecutive lanes) and leaves, per channel, the 4
-    // codes as one 32-bit word of the channel's LDS row.
-    for (int task = threadIdx.x; task < TASKS; task += WG) {
+    // codes as one 32-bit word of the channel's LDS row.  All of a thread's
+    // row reads are issued before the first is converted.
+    constexpr int NT = (TASKS + WG - 1) / WG;     // tasks per thread
+    uint4 raw[NT][4];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int task = threadIdx.x + i * WG;
+        const int cg = 8 * (task % GPR), tq = task / GPR;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = chk * VQT + 4 * tq + u;
+            raw[i][u] = task < TASKS && t < n
+                            ? *reinterpret_cast<const uint4*>(v + el0 + (int64_t)t * P.vs.n + cg)
+                            : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int task = threadIdx.x + i * WG;
+        if (task >= TASKS) break;
         const int cg = 8 * (task % GPR), tq = task / GPR;
         float inv[8], m8[8];
 #pragma unroll
@@ -453,8 +471,13 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
         for (int u = 0; u < 4; ++u) {
             const int t = chk * VQT + 4 * tq + u;
             if (t >= n) continue;                  // tokens past the end: zero codes
+            const uint32_t w[4] = {raw[i][u].x, raw[i][u].y, raw[i][u].z, raw[i][u].w};
             float val[8];
-            load8<DT>(v + el0 + (int64_t)t * P.vs.n + cg, val);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                val[2 * k] = h2f<DT>((uint16_t)(w[k] & 0xffff));
+                val[2 * k + 1] = h2f<DT>((uint16_t)(w[k] >> 16));
+            }
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const float x0 = muh ? val[e] - m8[e] : val[e];
