@@ -807,6 +807,10 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
 // tiles, the online softmax and the split partials are those of k_attn, so
 // the result is the same recipe.
 // ---------------------------------------------------------------------------
+// Wait until at most n of this wave's vector memory operations (its
+// direct-to-LDS copies) are outstanding; they complete in issue order.  The
+// count is an immediate of s_waitcnt, hence one case per value (a decode
+// wave never has more than 48 copies in flight).
 __device__ inline void wait_vm(int n) {
     switch (n) {
 #define SAGE_W(k) \
