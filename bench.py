@@ -16,6 +16,8 @@ Prints ONE JSON line.  Besides the standard fields it carries
 --pv half times the 16-bit P.V variant instead (P and V in the input's type
 on the 16-bit MFMA); its roofline peak is that of the op mix, half INT8 at
 5.0 POPS and half fp16/bf16 at 2.5 PFLOP/s, i.e. 3.33 POPS.
+The W warm-up steps are untimed and continue until --min-warmup-s of wall
+time has passed (the clocks settle); the JSON line reports how many ran.
 --kv-split N|auto splits the key range (flash-decoding).  A workload whose
 arithmetic intensity (ops per algorithmic byte of the fused kernel) is below
 the ridge of 5.0 POPS / 8 TB/s is reported against HBM instead: achieved =
@@ -44,7 +46,10 @@ def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--min-warmup-s", type=float, default=0.3,
+                    help="keep warming up (untimed) until this much wall time has passed, "
+                         "so that the GPU clocks have settled")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--pv", choices=("fp8", "half"), default="fp8",
                     help="P.V operands: E4M3 (default) or the input's 16-bit type")
@@ -188,8 +193,16 @@ def main():
             qa.sage_attn_fwd(q, k, v, out=o, workspace=ws, **kw)
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
+    # W untimed steps, continued until the clocks have settled (min-warmup-s
+    # of wall time): with a short warm-up the timed loop still ran part of
+    # the time at lower clocks (7% slower at W = 10 on causal_gqa)
+    tw = time.perf_counter()
+    warm = 0
+    while warm < args.warmup or time.perf_counter() - tw < args.min_warmup_s:
         step()
+        warm += 1
+        if warm % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -200,6 +213,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
+    # the same steps timed one by one (median and minimum of the whole call)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) for a, b in evs)
 
     # the fused kernel alone, on buffers quantized once (one launch per call)
     bufs = qa.sage_quant_qkv(q, k, v, **kw, **cu)
@@ -242,7 +264,10 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm,
         "ms_per_step": round(ms, 4),
+        "ms_median": round(per_step[len(per_step) // 2], 4),
+        "ms_min": round(per_step[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
