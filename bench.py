@@ -153,7 +153,7 @@ def kernel_bytes(w, pv: str, nsplit: int) -> float:
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the forward pass shards over batch and heads with no exchange)",
               file=sys.stderr)
         sys.exit(2)
