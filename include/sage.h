@@ -64,6 +64,10 @@
  *    returns before it completes.  Inputs must stay alive and unmodified and
  *    the workspace must not be reused until that work has completed.  Calls
  *    on different streams with different workspaces may run concurrently.
+ *  - A call enqueues kernel launches only (no memset, copy, allocation or
+ *    synchronization), so it may be captured into a HIP graph once the same
+ *    kind of call has run eagerly (the first launch of a kernel sets its LDS
+ *    limit with hipFuncSetAttribute).
  *  - Argument checks run first, on the host, in a fixed order; the first
  *    failure is returned and nothing is launched or written.  Inputs must be
  *    finite (not checked).  No exception crosses this ABI.
