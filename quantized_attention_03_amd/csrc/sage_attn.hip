@@ -544,8 +544,8 @@ __device__ inline uint32_t f2h_bits(float f) {
 // Barrier epochs: group 0 runs [MFMA(t)] bar [softmax(t)] bar for t = 0, 1, ...;
 // group 1 runs the same after one extra leading barrier, so in every epoch one
 // group is in its MFMA phase and the other in its softmax phase.
-// MFMA(t) = S(t) = Q.K(t)^T plus acc += V(t-1)^T . P^(t-1)^T; softmax(t) then
-// rescales acc (which now holds tiles < t) and produces P^(t).
+// MFMA(t) = acc = alpha(t-1) * acc + V(t-1)^T . P^(t-1)^T, then S(t) = Q.K(t)^T;
+// softmax(t) produces P^(t) and the alpha(t) that acc owes before the next P.V.
 // LDS lifetimes (epochs 2t, 2t+1 read K(t) and V(t-1); softmax(t) of group 1
 // runs in epoch 2t+2 and reads the score bias of tile t):
 //   K(t+1), V(t): copied at the start of MFMA(t) by each group (epochs 2t,
@@ -641,20 +641,14 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                                             si.npk, t + 1, w.hpw);
         stage_v<D, FWD_NT, PVH>(vst0 + (r & 1) * T::VBYTES, off, vbase, si.npk, t);
         if (t < w.nt_w) {
-            if constexpr (PVH) {
-                // P.V first: the 16-bit P^ then dies before S(t) is formed
-                if (r > 0) {
-                    rescale<D>(acc, alpha_prev);
-                    pv(r - 1);
-                }
-                qk_tile<D>(kst0 + (r & 1) * T::KBYTES, qf, sacc);
-            } else {
-                qk_tile<D>(kst0 + (r & 1) * T::KBYTES, qf, sacc);
-                if (r > 0) {
-                    rescale<D>(acc, alpha_prev);
-                    pv(r - 1);
-                }
+            // P.V of the previous tile first: its P^ then dies before S(t)
+            // is formed (measured 0.2-0.8% faster than Q.K first with E4M3
+            // P^, and needed to fit the registers with 16-bit P^)
+            if (r > 0) {
+                rescale<D>(acc, alpha_prev);
+                pv(r - 1);
             }
+            qk_tile<D>(kst0 + (r & 1) * T::KBYTES, qf, sacc);
         } else if (t == w.nt_w && r > 0) {
             // this wave's rows are done: flush its last tile
             rescale<D>(acc, alpha_prev);
