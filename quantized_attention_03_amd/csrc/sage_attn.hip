@@ -401,7 +401,7 @@ __device__ inline int max16(const v16i& a) {
 // 16-bit p does not.  Score scales: with 64-token K blocks c0 serves the
 // tile's first 64 keys and c1 the rest; with 32-token blocks (QB = 32)
 // c0..c3 serve the four 32-key blocks.
-template <bool MASK, bool HAS_DS, bool PVH = false, int DT = 0, int QB = QBLK>
+template <bool MASK, bool HAS_DS, bool PVH = false, int DT = 0, int QB = QBLK, int NPS = 8>
 __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, float c1, float c2,
                                      float c3, const float* dsl, float sml2, int kt0, int lim,
                                      float& m_run, float& l_run) {
@@ -475,15 +475,26 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
     }
     const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    // row sum of the FP32 p in 8 interleaved partial sums
-    float ps[8];
+    // row sum of the FP32 p in NPS interleaved partial sums (16 shortens the
+    // dependency chains; measured faster at d = 64, where the softmax is the
+    // whole bound, and not at d = 128)
+    float ps[NPS];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) ps[k] = p[0][k];
+    for (int k = 0; k < NPS; ++k) ps[k] = p[0][k];
+    if constexpr (NPS == 16) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+        for (int b = 1; b < 4; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (b > 0 || r >= 8) ps[r % 8] += p[b][r];
+            for (int r = 0; r < 16; ++r) ps[r] += p[b][r];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ps[k] += ps[k + 8];
+    } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (b > 0 || r >= 8) ps[r % 8] += p[b][r];
+    }
     const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
     l_run = fmaf(alpha, l_run, psum);
     if constexpr (PVH) {
@@ -680,12 +691,11 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                 (t + 1) * KVT > nkv || (P.causal && (t + 1) * KVT - 1 > wave_diag);
             float alpha;
             if (need_mask)
-                alpha = softmax_tile<true, HAS_DS, PVH, DT, QB>(sacc, pb, ph, c0, c1, c2, c3, dsl,
-                                                                P.sml2, kt0, lim, m_run, l_run);
+                alpha = softmax_tile<true, HAS_DS, PVH, DT, QB, D == 64 ? 16 : 8>(
+                    sacc, pb, ph, c0, c1, c2, c3, dsl, P.sml2, kt0, lim, m_run, l_run);
             else
-                alpha = softmax_tile<false, HAS_DS, PVH, DT, QB>(sacc, pb, ph, c0, c1, c2, c3,
-                                                                 dsl, P.sml2, kt0, lim, m_run,
-                                                                 l_run);
+                alpha = softmax_tile<false, HAS_DS, PVH, DT, QB, D == 64 ? 16 : 8>(
+                    sacc, pb, ph, c0, c1, c2, c3, dsl, P.sml2, kt0, lim, m_run, l_run);
             // acc (the tiles before t, at the previous max) is rescaled in
             // the next MFMA phase, before the P.V of tile t
             alpha_prev = alpha;
