@@ -367,30 +367,6 @@ __device__ inline float swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Max of the 32 integers of two accumulator blocks, as a tree of 3-input
-// maxima (16 operations).
-__device__ inline int max32(const v16i& a, const v16i& b) {
-    int l1[12];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) l1[i] = max(max(a[3 * i], a[3 * i + 1]), a[3 * i + 2]);
-#pragma unroll
-    for (int i = 0; i < 5; ++i) l1[5 + i] = max(max(b[3 * i], b[3 * i + 1]), b[3 * i + 2]);
-    l1[10] = max(a[15], b[15]);
-    int l2[4];
-#pragma unroll
-    for (int i = 0; i < 3; ++i) l2[i] = max(max(l1[3 * i], l1[3 * i + 1]), l1[3 * i + 2]);
-    l2[3] = l1[9];
-    return max(max(max(l2[0], l2[1]), l2[2]), max(l2[3], l1[10]));
-}
-
-// Max of the 16 integers of one accumulator block (v_max3_i32 tree).
-__device__ inline int max16(const v16i& a) {
-    int l1[5];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) l1[i] = max(max(a[3 * i], a[3 * i + 1]), a[3 * i + 2]);
-    return max(max(max(l1[0], l1[1]), l1[2]), max(max(l1[3], l1[4]), a[15]));
-}
-
 // Online softmax of one tile: updates the running max and sum, writes P^ in
 // the B layout of the 32x32x64 FP8 MFMA (half kh covers the lane's keys of
 // blocks 2kh and 2kh+1, bytes 0..15 and 16..31) -- or, with 16-bit operands
@@ -423,33 +399,33 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
                 for (int r = 0; r < 16; ++r)
                     sacc[b][r] = kt0 + 32 * b + r > lim ? NEG_INF_BITS : sacc[b][r];
         }
-        // three-input max trees (v_max3_i32), one per block of keys that
-        // shares a scale (the integer order is the score order only there)
+        // the exact scores first (one subtraction each, independent of the
+        // row maximum), then three-input float max trees, one per block of
+        // keys that shares a scale, then the exponent's FMA
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[b][r] = __int_as_float(sacc[b][r]) - SBIAS_F;
+        auto fmax16 = [&](int b) {
+            float l1[5];
+#pragma unroll
+            for (int i = 0; i < 5; ++i) l1[i] = fmaxf(fmaxf(p[b][3 * i], p[b][3 * i + 1]), p[b][3 * i + 2]);
+            return fmaxf(fmaxf(fmaxf(l1[0], l1[1]), l1[2]), fmaxf(fmaxf(l1[3], l1[4]), p[b][15]));
+        };
         float fm;
         if constexpr (QB == 32) {
             fm = -INFINITY;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int mx = max16(sacc[b]);
-                fm = fmaxf(fm, mx == NEG_INF_BITS ? -INFINITY
-                                                  : (__int_as_float(mx) - SBIAS_F) * cof(b));
-            }
+            for (int b = 0; b < 4; ++b) fm = fmaxf(fm, fmax16(b) * cof(b));
         } else {
-            const int mx0 = max32(sacc[0], sacc[1]), mx1 = max32(sacc[2], sacc[3]);
-            const float f0 =
-                mx0 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx0) - SBIAS_F) * c0;
-            const float f1 =
-                mx1 == NEG_INF_BITS ? -INFINITY : (__int_as_float(mx1) - SBIAS_F) * c1;
-            fm = fmaxf(f0, f1);
+            fm = fmaxf(fmaxf(fmax16(0), fmax16(1)) * c0, fmaxf(fmax16(2), fmax16(3)) * c1);
         }
         m_new = fmaxf(m_run, swap_max(fm));
         const float nm = POFF - (m_new == -INFINITY ? 0.0f : m_new);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                p[b][r] = __builtin_amdgcn_exp2f(
-                    fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, cof(b), nm));
+            for (int r = 0; r < 16; ++r) p[b][r] = __builtin_amdgcn_exp2f(fmaf(p[b][r], cof(b), nm));
     } else {
         // here c0, c1 leave out sm_scale*log2(e): y = S*sq*sk + dS is formed
         // first (its maximum taken), and the base-2 factor is applied inside
