@@ -67,9 +67,9 @@ def lib():
         "orc_delta_s": (None, [P, P, i64, i32, P]),
         "orc_qk_int32": (None, [P, P, i64, i64, i32, P]),
         "orc_attn_recipe_rows": (None, [P, P, P, P, P, P, P, P, i64, i64, i32, f32,
-                                        i32, i32, i32, i64, P, i64, P, P]),
+                                        i32, i32, i32, i64, P, i64, P, P, P]),
         "orc_attn_recipe_half_rows": (None, [P, P, P, P, P, i32, P, P, i64, i64, i32, f32,
-                                             i32, i32, i32, i64, P, i64, P, P]),
+                                             i32, i32, i32, i64, P, i64, P, P, P]),
         "orc_attn_exact_rows": (None, [P, P, P, i64, i64, i32, f64, i32, P, i64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -173,24 +173,27 @@ def qk_int32(qc, kc) -> np.ndarray:
 
 
 def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, rows, split=0,
-                     blk=BLK):
+                     blk=BLK, tie=False):
+    """The INT8-QK / FP8-PV recipe for selected rows.  Returns (out, lse), and
+    with tie=True also the rounding-tie bound [nrows, d] (sage_oracle.c)."""
     qc, kc, vc = _c(qc, np.int8), _c(kc, np.int8), _c(vc, np.uint8)
     nq, d = qc.shape
     nkv = kc.shape[0]
     rows = _c(rows, np.int64)
     out = np.empty((rows.size, d), np.float32)
     lse = np.empty(rows.size, np.float32)
+    tb = np.empty((rows.size, d), np.float32) if tie else None
     lib().orc_attn_recipe_rows(
         _p(qc), _p(_c(qs, np.float32)), _p(kc), _p(_c(ks, np.float32)), _p(vc),
         _p(_c(vs, np.float32)), _p(None if ds is None else _c(ds, np.float32)),
         _p(None if mu_v is None else _c(mu_v, np.float32)), nq, nkv, d,
         float(sm_scale), int(causal), int(bkv), int(blk), int(split), _p(rows), rows.size,
-        _p(out), _p(lse))
-    return out, lse
+        _p(out), _p(lse), _p(tb))
+    return (out, lse, tb) if tie else (out, lse)
 
 
 def attn_recipe_half_rows(qc, qs, kc, ks, vh, dtype, ds, mu_v, sm_scale, causal, bkv, rows,
-                          split=0, blk=BLK):
+                          split=0, blk=BLK, tie=False):
     """The 16-bit P.V variant: vh [nkv, d] fp16/bf16 bit patterns of the V
     operand; p^ is p rounded to the same type."""
     qc, kc, vh = _c(qc, np.int8), _c(kc, np.int8), _c(vh, np.uint16)
@@ -199,13 +202,14 @@ def attn_recipe_half_rows(qc, qs, kc, ks, vh, dtype, ds, mu_v, sm_scale, causal,
     rows = _c(rows, np.int64)
     out = np.empty((rows.size, d), np.float32)
     lse = np.empty(rows.size, np.float32)
+    tb = np.empty((rows.size, d), np.float32) if tie else None
     lib().orc_attn_recipe_half_rows(
         _p(qc), _p(_c(qs, np.float32)), _p(kc), _p(_c(ks, np.float32)), _p(vh),
         1 if dtype == "bf16" else 0, _p(None if ds is None else _c(ds, np.float32)),
         _p(None if mu_v is None else _c(mu_v, np.float32)), nq, nkv, d,
         float(sm_scale), int(causal), int(bkv), int(blk), int(split), _p(rows), rows.size,
-        _p(out), _p(lse))
-    return out, lse
+        _p(out), _p(lse), _p(tb))
+    return (out, lse, tb) if tie else (out, lse)
 
 
 def attn_exact_rows(q, k, v, sm_scale, causal, rows):
@@ -348,10 +352,13 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
 
 
 def forward_rows(prob: Problem, pre: Prepass, rows=None, bkv: int = 128,
-                 threads: int | None = None):
+                 threads: int | None = None, tie: bool = False):
     """Same-recipe forward.  rows: None (all rows) or a list over sequences of
     int arrays of query rows.  Returns (out, lse): lists over sequences of
-    [Hq, nrows, d] FP32 and [Hq, nrows] FP32."""
+    [Hq, nrows, d] FP32 and [Hq, nrows] FP32; with tie=True also the
+    rounding-tie bound of each output element (same shape as out), the most
+    that re-rounding the P operands that sit at a rounding midpoint can move
+    it (sage_oracle.c, recipe_rows)."""
     G = prob.Hq // prob.Hkv
     units = [(s, h) for s in range(len(prob.seqs)) for h in range(prob.Hq)]
 
@@ -366,19 +373,22 @@ def forward_rows(prob: Problem, pre: Prepass, rows=None, bkv: int = 128,
             return attn_recipe_half_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk],
                                          pre.ks[s][hk], pre.vc[s][hk], prob.dtype, ds, mu_v,
                                          prob.scale, prob.causal, bkv, r, prob.kv_split,
-                                         prob.qk_block)
+                                         prob.qk_block, tie=tie)
         return attn_recipe_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk], pre.ks[s][hk],
                                 pre.vc[s][hk], pre.vs[s][hk], ds, mu_v,
-                                prob.scale, prob.causal, bkv, r, prob.kv_split, prob.qk_block)
+                                prob.scale, prob.causal, bkv, r, prob.kv_split, prob.qk_block,
+                                tie=tie)
 
     with ThreadPoolExecutor(max_workers=threads or os.cpu_count()) as ex:
         res = list(ex.map(one, units))
-    outs, lses = [], []
+    outs, lses, ties = [], [], []
     for s in range(len(prob.seqs)):
         part = res[s * prob.Hq:(s + 1) * prob.Hq]
         outs.append(np.stack([p[0] for p in part]))
         lses.append(np.stack([p[1] for p in part]))
-    return outs, lses
+        if tie:
+            ties.append(np.stack([p[2] for p in part]))
+    return (outs, lses, ties) if tie else (outs, lses)
 
 
 def exact_rows(prob: Problem, q, k, v, rows=None, threads: int | None = None):

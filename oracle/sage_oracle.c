@@ -291,6 +291,7 @@ static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
  *   bkv         : key-tile width of the online softmax (p^ depends on it)
  *   split       : keys per split (a multiple of bkv), or 0 for one split
  *   rows[nrows] : query rows to compute; out [nrows][d] FP32, lse [nrows]
+ *   tie         : [nrows][d] FP32 or NULL: the rounding-tie bound below
  * Steps: s = fl32(S)*(sq*sk*sm_scale) (+ ds_j*sm_scale); the keys are cut into
  * splits of `split` keys, and in each split, for each key tile in order:
  * m' = max(m, max s), alpha = e^(m-m'), p = e^(s-m') (FP32),
@@ -301,8 +302,55 @@ static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
  * A = sum w_s acc_s (in split order); o = A*out_scale/L (+ mu_v).  One split
  * is the plain online softmax.  A row that sees no key gives o = 0 and
  * lse = -inf.  LSE = M + ln L, the natural log of sum_j e^(s_j) over the
- * scores as the recipe forms them. */
+ * scores as the recipe forms them.
+ *
+ * Rounding-tie bound.  p^ is a code picked by rounding p (times 448 for E4M3)
+ * in FP32.  Any FP32 evaluation of the recipe (another order of the products
+ * in the exponent, log2 units, a hardware exp2) moves p by a few parts in
+ * 2^24 of the terms' magnitudes, so where p lies that close to a rounding
+ * midpoint of the operand format both neighbouring codes are correct results
+ * of the recipe.  For each such key (relative distance to the midpoint below
+ * tie_window) the bound adds one code step times |v| per channel, carried
+ * through the rescales and the split merge like acc, and scaled like the
+ * output (out_scale / L).  Everywhere else it is 0. */
 enum { P_FP8 = 0, P_F16 = 1, P_BF16 = 2 };
+
+/* Spacing of the operand format's representable values at x >= 0 (x in the
+ * format's own units: p*448 for E4M3, p for fp16/bf16). */
+static double operand_step(double x, int p_mode) {
+    int e;
+    if (x <= 0.0) x = 0.0;
+    frexp(x, &e);                       /* x in [2^(e-1), 2^e) */
+    e -= 1;
+    switch (p_mode) {
+    case P_FP8:  return e < -6 ? ldexp(1.0, -9) : ldexp(1.0, e - 3);
+    case P_F16:  return e < -14 ? ldexp(1.0, -24) : ldexp(1.0, e - 10);
+    default:     return e < -126 ? ldexp(1.0, -133) : ldexp(1.0, e - 7);
+    }
+}
+
+/* Relative window within which a rounding midpoint counts as a tie: twice the
+ * unit roundoff per rounding, six roundings per term, over the magnitudes of
+ * the exponent's terms (terms = |score product| + |Q-smoothing bias|, and the
+ * row maximum m; natural-log units), plus a constant for the exponential and
+ * the P scale. */
+static double tie_window(double terms, double m) {
+    return ldexp(1.0, -23) * (6.0 * (terms + fabs(m)) + 16.0);
+}
+
+/* One code step of p's operand if p lies within the window of a rounding
+ * midpoint, else 0 (in the operand's units, as p_operand returns it). */
+static float tie_step(float p, int p_mode, double window) {
+    double x = p_mode == P_FP8 ? (double)(p * 448.0f) : (double)p;
+    if (x <= 0.0) return 0.0f;
+    if (p_mode == P_FP8 && x >= 448.0) return 0.0f;        /* saturated top code */
+    /* the nearest midpoint within the window is the one of x's own binade:
+       the others lie at least a quarter step away */
+    double st = operand_step(x, p_mode);
+    double mid = floor(x / st) * st + 0.5 * st;
+    if (fabs(x - mid) > window * x) return 0.0f;
+    return (float)st;
+}
 
 static float p_operand(float p, int p_mode) {
     switch (p_mode) {
@@ -317,22 +365,26 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
                         int p_mode, const float* delta_s, const float* mu_v, int64_t nq,
                         int64_t nkv, int d, float sm_scale, int causal, int bkv, int blk,
                         int64_t split, const int64_t* rows, int64_t nrows, float* out,
-                        float* lse) {
+                        float* lse, float* tie) {
     const int64_t span = split > 0 ? split : (nkv > 0 ? nkv : 1);
     const int64_t nsplit = nkv > 0 ? (nkv + span - 1) / span : 1;
     float* s = (float*)malloc(sizeof(float) * (size_t)(bkv > 0 ? bkv : 1));
+    float* mag = (float*)malloc(sizeof(float) * (size_t)(bkv > 0 ? bkv : 1));
     float* accs = (float*)malloc(sizeof(float) * (size_t)d * (size_t)nsplit);
     float* ms = (float*)malloc(sizeof(float) * (size_t)nsplit);
     float* ls = (float*)malloc(sizeof(float) * (size_t)nsplit);
     float* acc = (float*)malloc(sizeof(float) * (size_t)d);
+    float* ties = (float*)malloc(sizeof(float) * (size_t)d * (size_t)nsplit);
+    float* tacc = (float*)malloc(sizeof(float) * (size_t)d);
     for (int64_t r = 0; r < nrows; ++r) {
         int64_t i = rows[r];
         int64_t jmax = last_visible(i, nq, nkv, causal);
         float sq = q_scale[i / blk];
         for (int64_t sp = 0; sp < nsplit; ++sp) {
             float* a = accs + sp * d;
+            float* ta = ties + sp * d;
             float m = -INFINITY, l = 0.0f;
-            for (int c = 0; c < d; ++c) a[c] = 0.0f;
+            for (int c = 0; c < d; ++c) a[c] = ta[c] = 0.0f;
             int64_t k_end = (sp + 1) * span - 1 < jmax ? (sp + 1) * span - 1 : jmax;
             for (int64_t t0 = sp * span; t0 <= k_end; t0 += bkv) {
                 int64_t t1 = t0 + bkv - 1 < k_end ? t0 + bkv - 1 : k_end;
@@ -345,6 +397,7 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
                     float comb = sq * k_scale[j / blk];
                     comb = comb * sm_scale;
                     float sv = (float)S * comb;
+                    if (tie) mag[j - t0] = fabsf(sv) + (delta_s ? fabsf(delta_s[j] * sm_scale) : 0.0f);
                     if (delta_s) sv = sv + delta_s[j] * sm_scale;
                     s[j - t0] = sv;
                     if (sv > mt) mt = sv;
@@ -353,9 +406,18 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
                 float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)(m - mn));
                 float psum = 0.0f;
                 for (int c = 0; c < d; ++c) a[c] = alpha * a[c];
+                if (tie)
+                    for (int c = 0; c < d; ++c) ta[c] = alpha * ta[c];
                 for (int64_t jj = 0; jj < nt; ++jj) {
                     float p = (float)exp((double)(s[jj] - mn));
                     psum = psum + p;
+                    if (tie) {
+                        float st = tie_step(p, p_mode, tie_window(mag[jj], mn));
+                        if (st > 0.0f) {
+                            const float* vrow = vdec + (t0 + jj) * d;
+                            for (int c = 0; c < d; ++c) ta[c] = ta[c] + st * fabsf(vrow[c]);
+                        }
+                    }
                     float ph = p_operand(p, p_mode);
                     if (ph == 0.0f) continue;     /* a zero product leaves acc as is */
                     const float* vrow = vdec + (t0 + jj) * d;
@@ -371,16 +433,22 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
         float M = -INFINITY, L = 0.0f;
         for (int64_t sp = 0; sp < nsplit; ++sp)
             if (ms[sp] > M) M = ms[sp];
-        for (int c = 0; c < d; ++c) acc[c] = 0.0f;
+        for (int c = 0; c < d; ++c) acc[c] = tacc[c] = 0.0f;
         if (M != -INFINITY) {
             for (int64_t sp = 0; sp < nsplit; ++sp) {
                 if (ms[sp] == -INFINITY) continue;   /* a split without visible keys */
                 float w = (float)exp((double)(ms[sp] - M));
                 L = L + w * ls[sp];
                 for (int c = 0; c < d; ++c) acc[c] = acc[c] + w * accs[sp * d + c];
+                if (tie)
+                    for (int c = 0; c < d; ++c) tacc[c] = tacc[c] + w * ties[sp * d + c];
             }
         }
         float* o = out + r * d;
+        if (tie)
+            for (int c = 0; c < d; ++c)
+                tie[r * d + c] = (jmax < 0 || L == 0.0f) ? 0.0f
+                    : tacc[c] * (out_scale ? fabsf(out_scale[c]) : 1.0f) / L;
         if (jmax < 0 || L == 0.0f) {
             for (int c = 0; c < d; ++c) o[c] = 0.0f;
             if (lse) lse[r] = -INFINITY;
@@ -394,10 +462,13 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
         if (lse) lse[r] = M + logf(L);
     }
     free(s);
+    free(mag);
     free(accs);
     free(ms);
     free(ls);
     free(acc);
+    free(ties);
+    free(tacc);
 }
 
 /* The INT8-QK / FP8-PV recipe ([BLOG] item 2, [SA2] item 3):
@@ -411,14 +482,14 @@ ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
                                      int64_t nq, int64_t nkv, int d, float sm_scale,
                                      int causal, int bkv, int blk, int64_t split,
                                      const int64_t* rows, int64_t nrows,
-                                     float* out, float* lse) {
+                                     float* out, float* lse, float* tie) {
     /* decode every V code once; dec(v^) is exact in FP32 */
     float* vdec = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1) * (size_t)d);
     float* fac = (float*)malloc(sizeof(float) * (size_t)d);
     for (int64_t j = 0; j < nkv * d; ++j) vdec[j] = orc_e4m3_decode(vc[j]);
     for (int c = 0; c < d; ++c) fac[c] = v_scale[c] / 448.0f;
     recipe_rows(qc, q_scale, kc, k_scale, vdec, fac, P_FP8, delta_s, mu_v, nq, nkv, d, sm_scale,
-                causal, bkv, blk, split, rows, nrows, out, lse);
+                causal, bkv, blk, split, rows, nrows, out, lse, tie);
     free(vdec);
     free(fac);
 }
@@ -437,12 +508,12 @@ ORC_EXPORT void orc_attn_recipe_half_rows(const int8_t* qc, const float* q_scale
                                           int64_t nq, int64_t nkv, int d, float sm_scale,
                                           int causal, int bkv, int blk, int64_t split,
                                           const int64_t* rows, int64_t nrows,
-                                          float* out, float* lse) {
+                                          float* out, float* lse, float* tie) {
     float* vdec = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1) * (size_t)d);
     for (int64_t j = 0; j < nkv * d; ++j)
         vdec[j] = bf16 ? orc_bf16_decode(vh[j]) : orc_f16_decode(vh[j]);
     recipe_rows(qc, q_scale, kc, k_scale, vdec, NULL, bf16 ? P_BF16 : P_F16, delta_s, mu_v, nq,
-                nkv, d, sm_scale, causal, bkv, blk, split, rows, nrows, out, lse);
+                nkv, d, sm_scale, causal, bkv, blk, split, rows, nrows, out, lse, tie);
     free(vdec);
 }
 

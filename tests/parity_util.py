@@ -126,13 +126,17 @@ def half_ulp(x, dtype: str):
     return np.exp2(e - mant) / 2
 
 
-def max_excess(g, r, dtype: str) -> float:
+def max_excess(g, r, dtype: str, tie=None) -> float:
     """max |g - r| beyond the final output rounding (g: decoded GPU output,
-    r: the oracle's FP32 result before that rounding)."""
+    r: the oracle's FP32 result before that rounding) and, with tie (the
+    oracle's rounding-tie bound, forward_rows(tie=True)), beyond what the
+    P-operand codes that sit at a rounding midpoint can move each element."""
     if np.size(g) == 0:
         return 0.0
-    d = np.abs(np.asarray(g, np.float64) - np.asarray(r, np.float64))
-    return float(np.max(np.maximum(d - half_ulp(r, dtype), 0.0)))
+    d = np.abs(np.asarray(g, np.float64) - np.asarray(r, np.float64)) - half_ulp(r, dtype)
+    if tie is not None:
+        d = d - np.asarray(tie, np.float64)
+    return float(np.max(np.maximum(d, 0.0)))
 
 
 def cos(a, b):

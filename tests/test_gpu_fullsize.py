@@ -43,11 +43,11 @@ def test_full_size(name):
     torch.cuda.synchronize()
     got = pu.gpu_out_per_seq(w, o, meta)
     rows = [pu.sample_rows(nq, ROWS, 100 + s) for s, (nq, _) in enumerate(w.seq_lens())]
-    rec, _ = orc.forward_rows(prob, ref, rows=rows, bkv=pu.KVT)
+    rec, _, tie = orc.forward_rows(prob, ref, rows=rows, bkv=pu.KVT, tie=True)
     ex, _ = orc.exact_rows(prob, qh, kh, vh, rows=rows)
     for s in range(len(rows)):
         g = got[s][:, rows[s]]
-        err = pu.max_excess(g, rec[s], w.dtype)
+        err = pu.max_excess(g, rec[s], w.dtype, tie[s])
         pu.say(f"  seq {s}: rows {len(rows[s])} max_excess {err:.4g} cos_recipe "
                f"{pu.cos(g, rec[s]):.6f} cos_fp64 {pu.cos(g, ex[s]):.6f}")
         assert np.all(np.isfinite(g))

@@ -8,8 +8,10 @@ It then checks, against the oracle on the same seeded inputs:
 
 * the pre-pass bit for bit (means, codes, scales; the score bias to FP32
   rounding);
-* the output within max-abs 2e-2 and cosine 0.999 of the same-recipe
-  oracle, and cosine 0.99 of exact FP64 attention;
+* the output within max-abs 2e-2 (beyond the oracle's rounding-tie bound:
+  P codes whose p sits at a rounding midpoint may round either way) and
+  cosine 0.999 of the same-recipe oracle, and cosine 0.99 of exact FP64
+  attention;
 * the LSE against the oracle's.
 """
 import numpy as np
@@ -94,7 +96,7 @@ def test_fuzz_case(i):
         o, lse = pu.qa.sage_attn_fwd(q, k, v, return_lse=True, **kw)
     torch.cuda.synchronize()
     got = pu.gpu_out_per_seq(w, o, meta)
-    rec, rec_lse = orc.forward_rows(prob, ref, bkv=pu.KVT)
+    rec, rec_lse, tie = orc.forward_rows(prob, ref, bkv=pu.KVT, tie=True)
     ex, _ = orc.exact_rows(prob, qh, kh, vh)
     lse_h = lse.cpu().numpy()
     for si, (nq, nkv) in enumerate(w.seq_lens()):
@@ -102,7 +104,7 @@ def test_fuzz_case(i):
         if g.size == 0:
             continue
         assert np.all(np.isfinite(g))
-        err = pu.max_excess(g, r, w.dtype)
+        err = pu.max_excess(g, r, w.dtype, tie[si])
         assert err <= 2e-2, (si, err)
         if np.abs(r).max() > 0:
             assert pu.cos(g, r) >= 0.999, (si, pu.cos(g, r))

@@ -54,12 +54,12 @@ def case(request):
     return name, w, q, k, v, meta, prob, ref
 
 
-def _check_forward(w, got, rec, rec_lse, ex, lse_h, meta, rows=None):
+def _check_forward(w, got, rec, rec_lse, ex, lse_h, meta, rows=None, tie=None):
     for si, (nq, nkv) in enumerate(w.seq_lens()):
         g = got[si] if rows is None else got[si][:, rows[si]]
         r, e = rec[si], ex[si]
         assert np.all(np.isfinite(g))
-        err = pu.max_excess(g, r, w.dtype)
+        err = pu.max_excess(g, r, w.dtype, None if tie is None else tie[si])
         assert err <= 2e-2, (si, err)
         assert pu.cos(g, r) >= 0.999, (si, pu.cos(g, r))
         assert pu.cos(g, e) >= 0.99, (si, pu.cos(g, e))
@@ -95,9 +95,9 @@ def test_half_forward_matches_oracle(case):
     o, lse = pu.run_fwd(w, q, k, v, meta, pv="half")
     torch.cuda.synchronize()
     got = pu.gpu_out_per_seq(w, o, meta)
-    rec, rec_lse = orc.forward_rows(prob, ref, bkv=pu.KVT)
+    rec, rec_lse, tie = orc.forward_rows(prob, ref, bkv=pu.KVT, tie=True)
     ex, _ = orc.exact_rows(prob, pu.u16(q), pu.u16(k), pu.u16(v))
-    _check_forward(w, got, rec, rec_lse, ex, lse.cpu().numpy(), meta)
+    _check_forward(w, got, rec, rec_lse, ex, lse.cpu().numpy(), meta, tie=tie)
 
 
 def test_half_quantized_entry_and_determinism(case):
@@ -154,6 +154,6 @@ def test_half_full_size(name):
     torch.cuda.synchronize()
     got = pu.gpu_out_per_seq(w, o, meta)
     rows = [pu.sample_rows(nq, 24, 200 + s) for s, (nq, _) in enumerate(w.seq_lens())]
-    rec, rec_lse = orc.forward_rows(prob, ref, rows=rows, bkv=pu.KVT)
+    rec, rec_lse, tie = orc.forward_rows(prob, ref, rows=rows, bkv=pu.KVT, tie=True)
     ex, _ = orc.exact_rows(prob, qh, kh, vh, rows=rows)
-    _check_forward(w, got, rec, rec_lse, ex, lse.cpu().numpy(), meta, rows=rows)
+    _check_forward(w, got, rec, rec_lse, ex, lse.cpu().numpy(), meta, rows=rows, tie=tie)
