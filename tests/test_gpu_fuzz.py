@@ -24,7 +24,7 @@ from tests import parity_util as pu
 
 pytestmark = pytest.mark.gpu
 
-NCASES = 48
+NCASES = 256
 
 
 def _draw(i: int):
