@@ -11,6 +11,7 @@ output element, what such re-roundings can move it.  The checks:
   picks the oracle's code except at a few keys; recomputing the output with
   those codes moves it by no more than the bound, and a row with one such key
   moves by the bound itself (one code step times |v| over L);
+* the same for the 16-bit P operand (fp16 and bf16 rounding of p);
 * the bound is zero on rows with no near-midpoint p, and such rows are few;
 * on the inputs where a GPU run differed from the oracle by one E4M3 step of
   a dominant key (p*448 = 200.000046 against the midpoint 200, between the
@@ -89,6 +90,53 @@ def test_bound_covers_other_evaluation_orders(orc):
                 np.testing.assert_allclose(np.abs(delta), b, rtol=1e-4, atol=1e-7)
     assert flips > 0 and single > 0          # the check saw re-rounded codes
     assert rows_with_bound < 0.1 * w.Hq * w.Nq
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bound_covers_other_orders_16bit_p(orc, dtype):
+    # the 16-bit P.V variant: p itself is rounded to the input's 16-bit type
+    # (numpy's float16 / torch's bfloat16 conversion here), with no P scale
+    import torch
+    w = synth.Workload(name="ties16", dtype=dtype, layout="HND", B=1, Hq=4, Hkv=4, Nq=2048,
+                       Nkv=128, d=64, smooth_k=True, seed=11, k_off_sigma=2.0,
+                       qv_mean_sigma=1.0)
+    prob = orc.problem_from_workload(w, "half", 0, 64)
+    q, k, v, _ = synth.make_inputs(w, device="cpu")
+    u = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    pre = orc.prepass(prob, u(q), u(k), u(v))
+    _, _, tie = orc.forward_rows(prob, pre, bkv=128, tie=True)
+
+    def r16(x):
+        if dtype == "f16":
+            return x.astype(np.float16).astype(np.float64)
+        return torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+
+    flips = 0
+    for h in range(w.Hq):
+        qc, qs, kc, ks = pre.qc[0][h], pre.qs[0][h], pre.kc[0][h], pre.ks[0][h]
+        vdec = orc.decode16(pre.vc[0][h], dtype).astype(np.float64)
+        ks_row = ks[np.arange(w.Nkv) // 64].astype(F32)
+        sq = qs[np.arange(w.Nq) // 64].astype(F32)
+        S = qc.astype(np.int64) @ kc.astype(np.int64).T
+        # the recipe's order
+        comb = (sq[:, None] * ks_row[None, :]).astype(F32) * F32(prob.scale)
+        s = (S.astype(F32) * comb.astype(F32)).astype(F32)
+        p = np.exp((s - s.max(axis=1, keepdims=True)).astype(F32).astype(np.float64)).astype(F32)
+        # log2 units and one fused multiply-add
+        c = ((sq[:, None] * ks_row[None, :]).astype(F32)
+             * F32(prob.scale * math.log2(math.e))).astype(F32)
+        y = (S.astype(F32) * c).astype(F32)
+        nm = (-y.max(axis=1, keepdims=True)).astype(F32)
+        x = (S.astype(np.float64) * c.astype(np.float64) + nm.astype(np.float64)).astype(F32)
+        pk = np.exp2(x.astype(np.float64)).astype(F32)
+        a, b = r16(p), r16(pk)
+        for i in np.nonzero((a != b).any(axis=1))[0]:
+            diff = np.nonzero(a[i] != b[i])[0]
+            flips += diff.size
+            L = float(p[i].astype(np.float64).sum())
+            delta = ((b[i, diff] - a[i, diff]) @ vdec[diff]) / L
+            assert np.all(np.abs(delta) <= tie[0][h, i] * (1 + 1e-4) + 1e-9), (h, i, diff)
+    assert flips > 0
 
 
 def test_bound_zero_without_midpoints(orc):
