@@ -38,6 +38,7 @@
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
 #include <algorithm>
+#include <atomic>
 #include <cfloat>
 
 #include "sage_internal.h"
@@ -387,6 +388,9 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
         else return b < 2 ? c0 : c1;
     };
     const int h = (threadIdx.x & 63) >> 5;
+    // key kt0 + 32b + r is masked when 32b + r > lim - kt0: one compare with
+    // a constant per key
+    const int th = lim - kt0;
     float p[4][16];
     float m_new;
     if constexpr (!HAS_DS) {
@@ -397,7 +401,7 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    sacc[b][r] = kt0 + 32 * b + r > lim ? NEG_INF_BITS : sacc[b][r];
+                    sacc[b][r] = 32 * b + r > th ? NEG_INF_BITS : sacc[b][r];
         }
         // the exact scores first (one subtraction each, independent of the
         // row maximum), then three-input float max trees, one per block of
@@ -437,7 +441,7 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float y = fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, c, dsl[32 * b + 16 * h + r]);
-                if (MASK) y = kt0 + 32 * b + r > lim ? -INFINITY : y;
+                if (MASK) y = 32 * b + r > th ? -INFINITY : y;
                 p[b][r] = y;
                 mt = fmaxf(mt, y);
             }
@@ -1090,19 +1094,30 @@ constexpr int lds_bytes() {
            (HAS_DS ? 3 * Tile<D, PVH>::DSBYTES : 0);
 }
 
+// Allow a kernel its dynamic LDS beyond the default, once per device (the
+// attribute belongs to the function on the current device).  `done` holds one
+// bit per device id below 64; devices above that set it on every call.  Two
+// threads racing on a device both set it, which is harmless.
+hipError_t lds_attr(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t{1} << dev) : 0;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    done.fetch_or(bit, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 template <int D, int DT, bool HAS_DS, bool PVH, int QB>
 hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const int8_t* kc,
                   const float* ksc, const uint8_t* vc, const float* vsc, const float* ds,
                   const float* mu_v, void* o, float* lse, hipStream_t st) {
-    static bool attr_set = false;   // benign race: the call is idempotent
-    if (!attr_set) {
-        hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D, DT, HAS_DS, PVH, QB>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds_bytes<D, HAS_DS, PVH>());
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_set{0};
+    hipError_t e = lds_attr(reinterpret_cast<const void*>(&k_attn<D, DT, HAS_DS, PVH, QB>),
+                            lds_bytes<D, HAS_DS, PVH>(), attr_set);
+    if (e != hipSuccess) return e;
     const int nblocks = wg_count_host(P, FWD_WAVES) * P.nsplit;
     if (nblocks <= 0) return hipSuccess;
     k_attn<D, DT, HAS_DS, PVH, QB><<<nblocks, FWD_NT, lds_bytes<D, HAS_DS, PVH>(), st>>>(
@@ -1114,15 +1129,10 @@ template <int D, int DT, bool HAS_DS, bool PVH, int QB>
 hipError_t decode_d(const KParams& P, const int8_t* qc, const float* qsc, const int8_t* kc,
                     const float* ksc, const uint8_t* vc, const float* vsc, const float* ds,
                     const float* mu_v, hipStream_t st) {
-    static bool attr_set = false;   // benign race: the call is idempotent
-    if (!attr_set) {
-        hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<D, DT, HAS_DS, PVH, QB>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                dec_lds_bytes<D, HAS_DS, PVH>(32));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_set{0};
+    hipError_t e = lds_attr(reinterpret_cast<const void*>(&k_decode<D, DT, HAS_DS, PVH, QB>),
+                            dec_lds_bytes<D, HAS_DS, PVH>(32), attr_set);
+    if (e != hipSuccess) return e;
     const int nblocks = P.tab.n * P.hkv * P.nsplit;
     if (nblocks <= 0) return hipSuccess;
     k_decode<D, DT, HAS_DS, PVH, QB><<<nblocks, 64, dec_lds_bytes<D, HAS_DS, PVH>(P.group), st>>>(
