@@ -305,9 +305,9 @@ static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
  * scores as the recipe forms them.
  *
  * Rounding-tie bound.  p^ is a code picked by rounding p (times 448 for E4M3)
- * in FP32.  Any FP32 evaluation of the recipe (another order of the products
- * in the exponent, log2 units, a hardware exp2) moves p by a few parts in
- * 2^24 of the terms' magnitudes, so where p lies that close to a rounding
+ * in FP32.  The plain FP32 evaluations of the exponent (another order of its
+ * products, log2 units, a hardware exp2 within an ulp) move p by a few parts
+ * in 2^24 of the terms' magnitudes, so where p lies that close to a rounding
  * midpoint of the operand format both neighbouring codes are correct results
  * of the recipe.  For each such key (relative distance to the midpoint below
  * tie_window) the bound adds one code step times |v| per channel, carried
