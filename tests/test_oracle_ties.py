@@ -13,9 +13,9 @@ output element, what such re-roundings can move it.  The checks:
   moves by the bound itself (one code step times |v| over L);
 * the same for the 16-bit P operand (fp16 and bf16 rounding of p);
 * the bound is zero on rows with no near-midpoint p, and such rows are few;
-* on the inputs where a GPU run differed from the oracle by one E4M3 step of
-  a dominant key (p*448 = 200.000046 against the midpoint 200, between the
-  codes 192 and 208), the bound covers the difference.
+* a row whose dominant key has p*448 just above an E4M3 midpoint (200,
+  between the codes 192 and 208): the other code would move the row by more
+  than the 2e-2 bar, and the bound covers it.
 """
 import math
 
@@ -149,9 +149,11 @@ def test_bound_zero_without_midpoints(orc):
     assert not tie[0].any()
 
 
-def test_bound_covers_observed_gpu_difference(orc):
+def test_bound_covers_a_dominant_key_at_a_midpoint(orc):
     # two varlen sequences (43 x 247 and 98 x 72 tokens), d = 128, fp16 NHD,
-    # K smoothing, Q/K blocks of 32 tokens, 128-key splits
+    # K smoothing, Q/K blocks of 32 tokens, 128-key splits: in the row of
+    # sequence 1, head 0, query 39, key 19 has p*448 a few parts in 2^24
+    # above the E4M3 midpoint 200 between the codes 192 and 208
     w = synth.Workload(name="tie201", dtype="f16", layout="NHD", B=2, Hq=2, Hkv=2, Nq=0,
                        Nkv=0, d=128, smooth_k=True, seed=251, k_off_sigma=2.0,
                        qv_mean_sigma=1.0, seqlens_q=[43, 98], seqlens_kv=[247, 72])
@@ -159,22 +161,19 @@ def test_bound_covers_observed_gpu_difference(orc):
     q, k, v, _ = synth.make_inputs(w, device="cpu")
     u = lambda t: t.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
     pre = orc.prepass(prob, u(q), u(k), u(v))
-    out, _, tie = orc.forward_rows(prob, pre, bkv=128, tie=True)
-    # the row of sequence 1, head 0, query 39: key 19 sits at a midpoint
+    _, _, tie = orc.forward_rows(prob, pre, bkv=128, tie=True)
     S = pre.qc[1][0][39:40].astype(np.int64) @ pre.kc[1][0].astype(np.int64).T
     ks_row = pre.ks[1][0][np.arange(72) // 32].astype(F32)
     co, p = _codes_oracle_order(orc, S, pre.qs[1][0][39 // 32:39 // 32 + 1].astype(F32),
                                 ks_row, prob.scale)
     co, p = co[0], p[0]
-    assert orc.e4m3_decode(co[19]) == 208.0
     x = float((p[19] * F32(448)).astype(F32))
-    assert abs(x - 200.0) < 1e-4
-    # the other code (192) moves channel 30 by 0.0216; the GPU output there
-    # was -1.7197266 against the oracle's -1.7413206
+    assert 0.0 < x - 200.0 < 1e-4            # just above the midpoint: rounds up
+    assert orc.e4m3_decode(co[19]) == 208.0
+    # the other code (192) moves the row by one code step times |v| over L,
+    # more than the 2e-2 bar on some channel; the bound covers every channel
     vdec = orc.e4m3_decode(pre.vc[1][0][19]).astype(np.float64)
     L = float(p.astype(np.float64).sum())
     delta = -16.0 * vdec * pre.vs[1][0].astype(np.float64) / 448.0 / L
-    assert abs(out[1][0, 39, 30] - -1.7413206) < 1e-6
-    assert abs(delta[30]) > 0.02
+    assert np.abs(delta).max() > 0.02
     assert np.all(np.abs(delta) <= tie[1][0, 39] * (1 + 1e-4))
-    assert abs((-1.7197266) - out[1][0, 39, 30]) <= tie[1][0, 39, 30] + 2e-2
