@@ -13,10 +13,12 @@
 //    workgroup take up to 4 query heads of one key/value head so that every
 //    K/V tile staged in LDS feeds all of them.
 //  * S^T = Kc . Qc^T on v_mfma_i32_32x32x32_i8 (A = key rows from LDS,
-//    B = the wave's Q codes held in VGPRs).  The row max is taken on the
-//    int32 scores (the scale is positive and uniform over a 64-key block);
-//    each score then costs one exact int -> float conversion and one FMA,
-//    x = S * (sq*sk*sm_scale*log2 e) - (m - log2 448), rounded once.
+//    B = the wave's Q codes held in VGPRs).  The accumulators start at the
+//    bits of 1.5*2^23, so each score S is recovered exactly as a float by one
+//    subtraction; the row max is a float max tree over the exact S of each
+//    block of keys that shares a scale, scaled once per block, and each score
+//    then costs one FMA, x = S * (sq*sk*sm_scale*log2 e) - (m - log2 448),
+//    rounded once.
 //  * Key rows are fed to the MFMA in a permuted order so that in the output
 //    layout each lane holds 16 consecutive keys of its own query row; lanes l
 //    and l+32 share a row, so the row max needs a single permlane32 swap.
@@ -30,11 +32,16 @@
 //    XOR-swizzled so the operand reads are bank-conflict free.
 //  * Ping-pong: a workgroup has 8 waves in two groups of 4; the two waves
 //    that share a SIMD belong to different groups.  Each group alternates an
-//    MFMA phase (Q.K(t)^T and the P.V of tile t-1) and a softmax phase (VALU
-//    and v_exp_f32), offset by one phase from the other group, with a
-//    workgroup barrier between phases.  So while one wave of a SIMD keeps
-//    the matrix unit busy the other issues the softmax VALU work; the MFMA
-//    phase runs at raised priority.
+//    MFMA phase and a softmax phase, offset by one phase from the other
+//    group, with a workgroup barrier between phases.  The softmax phase is
+//    the score half of tile t (exact S, row max, exponent FMA, v_exp_f32);
+//    the MFMA phase holds the P.V of tile t-1 with its operand half (FP8
+//    packing of p, the alpha rescale of O, the row sum of p) and then
+//    Q.K(t)^T.  A single wave issues VALU work only about every fifth
+//    cycle, about half of what the SIMD takes from two waves, so the work
+//    that does not depend on the new scores is moved to the wave whose
+//    matrix instructions are in flight; the MFMA phase runs at raised
+//    priority.
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
 #include <algorithm>
@@ -267,51 +274,74 @@ __device__ inline void load_q(const int8_t* qrow, v4i* qf) {
 }
 
 // S^T of one 128-key tile: sacc[b] covers keys 32b..32b+31; lane (row,
-// half) receives keys 32b + 16*half + r in register r (r = 0..15).  Chunk-
-// major order keeps consecutive MFMAs independent.
-template <int D>
-__device__ inline void qk_tile(const uint8_t* Ks, const v4i* qf, v16i* sacc) {
-    using T = Tile<D>;
-    const int lane = threadIdx.x & 63;
-    const int h = lane >> 5, i = lane & 31;
+// half) receives keys 32b + 16*half + r in register r (r = 0..15).  The
+// accumulators start at the bits of 1.5*2^23 (sbias_init), so that the int32
+// result read as a float is exactly 1.5*2^23 + S.  k_ops reads the A operands
+// of one 32-channel chunk (one 16-byte LDS read per 32-key block), qk_chunk
+// issues its four MFMAs; chunk-major order keeps consecutive MFMAs
+// independent.
+__device__ inline void sbias_init(v16i* sacc) {
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[b][r] = SBIAS_I;
+}
+
+template <int D>
+__device__ inline void k_ops(const uint8_t* Ks, int c, v4i* a) {
+    using T = Tile<D>;
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int row = 32 * b + i;
+        a[b] = *reinterpret_cast<const v4i*>(Ks + row * T::KRS +
+                                             (((2 * c + h) ^ swz<T::KRS>(row)) << 4));
+    }
+}
+
+__device__ inline void qk_chunk(const v4i* a, v4i q, v16i* sacc) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        sacc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[b], q, sacc[b], 0, 0, 0);
+}
+
+template <int D>
+__device__ inline void qk_tile(const uint8_t* Ks, const v4i* qf, v16i* sacc) {
+    sbias_init(sacc);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
         v4i a[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int row = 32 * b + i;
-            a[b] = *reinterpret_cast<const v4i*>(Ks + row * T::KRS +
-                                                 (((2 * c + h) ^ swz<T::KRS>(row)) << 4));
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            sacc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[b], qf[c], sacc[b], 0, 0, 0);
+        k_ops<D>(Ks, c, a);
+        qk_chunk(a, qf[c], sacc);
     }
 }
 
 // acc[c] += V^T(channels 32c..32c+31) . P^T for one 128-key tile held in a V
-// stage (two 64-key halves: P bytes pb[kh]).
+// stage (two 64-key halves: P bytes pb[kh]).  v_op reads the A operand of
+// half kh, chunk c: two 16-byte granules of the lane's channel row.
 template <int D>
-__device__ inline void pv_tile(const uint8_t* Vs, const v8i* pb, v16f* acc) {
+__device__ inline v8i v_op(const uint8_t* Vs, int kh, int c) {
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, qi = lane & 31;
+    const int ch = 32 * c + qi;
+    const uint8_t* vr = Vs + ch * KVT;
+    const int sw = swz<128>(ch);
+    const v4i lo = *reinterpret_cast<const v4i*>(vr + (((4 * kh + h) ^ sw) << 4));
+    const v4i hi = *reinterpret_cast<const v4i*>(vr + (((4 * kh + 2 + h) ^ sw) << 4));
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ inline v16f pv_mfma(v8i a, v8i p, v16f acc) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p, acc, 0, 0, 0, 0, 0, 0);
+}
+
+template <int D>
+__device__ inline void pv_tile(const uint8_t* Vs, const v8i* pb, v16f* acc) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-            const int ch = 32 * c + qi;
-            const uint8_t* vr = Vs + ch * KVT;
-            const int sw = swz<128>(ch);
-            const v4i lo = *reinterpret_cast<const v4i*>(vr + (((4 * kh + h) ^ sw) << 4));
-            const v4i hi = *reinterpret_cast<const v4i*>(vr + (((4 * kh + 2 + h) ^ sw) << 4));
-            const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb[kh], acc[c], 0, 0, 0, 0,
-                                                                      0, 0);
-        }
+        for (int c = 0; c < D / 32; ++c) acc[c] = pv_mfma(v_op<D>(Vs, kh, c), pb[kh], acc[c]);
 }
 
 // The 16-bit variant: acc[c] += V^T(channels 32c..32c+31) . P^T with the
@@ -368,20 +398,27 @@ __device__ inline float swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Online softmax of one tile: updates the running max and sum, writes P^ in
-// the B layout of the 32x32x64 FP8 MFMA (half kh covers the lane's keys of
-// blocks 2kh and 2kh+1, bytes 0..15 and 16..31) -- or, with 16-bit operands
-// (PVH), p itself rounded into the type DT, eight keys per ph entry as
-// pv_tile_h reads them -- and returns alpha, the factor that moves earlier
-// contributions to the new max.  Keys past `lim` are masked when MASK.
-// The FP8 P^ carries the static scale 448 (folded into the exponent); the
-// 16-bit p does not.  Score scales: with 64-token K blocks c0 serves the
-// tile's first 64 keys and c1 the rest; with 32-token blocks (QB = 32)
-// c0..c3 serve the four 32-key blocks.
-template <bool MASK, bool HAS_DS, bool PVH = false, int DT = 0, int QB = QBLK, int NPS = 8>
-__device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, float c1, float c2,
-                                     float c3, const float* dsl, float sml2, int kt0, int lim,
-                                     float& m_run, float& l_run) {
+// Online softmax of one tile, in two halves so that the fused kernel can run
+// them in different phases.
+//
+// The score half (score_exp) turns the tile's biased int32 scores into
+// p = 2^(s*log2 e - m) in FP32 (the FP8 operand's static scale 448 is folded
+// into the exponent; the 16-bit operand has none), updates the running max m
+// and returns alpha, the factor that moves earlier contributions to the new
+// max.  Keys past `lim` are masked when MASK.  Score scales: with 64-token K
+// blocks c0 serves the tile's first 64 keys and c1 the rest; with 32-token
+// blocks (QB = 32) c0..c3 serve the four 32-key blocks.
+//
+// The operand half adds the tile's FP32 p to the running sum,
+// l = alpha*l + sum p (row_sum), and writes P^ in the B layout of the
+// 32x32x64 FP8 MFMA (half kh covers the lane's keys of blocks 2kh and 2kh+1,
+// bytes 0..15 and 16..31) -- or, with 16-bit operands (PVH), p itself
+// rounded into the type DT, eight keys per ph entry as pv_tile_h reads them
+// (pack_p).
+template <bool MASK, bool HAS_DS, bool PVH = false, int QB = QBLK>
+__device__ inline float score_exp(v16i* sacc, float (&p)[4][16], float c0, float c1, float c2,
+                                  float c3, const float* dsl, float sml2, int kt0, int lim,
+                                  float& m_run) {
     constexpr float POFF = PVH ? 0.0f : LOG2_448;
     auto cof = [&](int b) {
         if constexpr (QB == 32) return b == 0 ? c0 : (b == 1 ? c1 : (b == 2 ? c2 : c3));
@@ -391,7 +428,6 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
     // key kt0 + 32b + r is masked when 32b + r > lim - kt0: one compare with
     // a constant per key
     const int th = lim - kt0;
-    float p[4][16];
     float m_new;
     if constexpr (!HAS_DS) {
         if constexpr (MASK) {
@@ -455,9 +491,14 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
     }
     const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    // row sum of the FP32 p in NPS interleaved partial sums (16 shortens the
-    // dependency chains; measured faster at d = 64, where the softmax is the
-    // whole bound, and not at d = 128)
+    return alpha;
+}
+
+// l = alpha*l + (sum of the tile's FP32 p), in NPS interleaved partial sums
+// (16 shortens the dependency chains; measured faster at d = 64, where the
+// softmax is the whole bound, and not at d = 128).
+template <int NPS = 8>
+__device__ inline void row_sum(const float (&p)[4][16], float alpha, float& l_run) {
     float ps[NPS];
 #pragma unroll
     for (int k = 0; k < NPS; ++k) ps[k] = p[0][k];
@@ -477,6 +518,11 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
     }
     const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
     l_run = fmaf(alpha, l_run, psum);
+}
+
+// The P operand of one tile from its FP32 p.
+template <bool PVH = false, int DT = 0>
+__device__ inline void pack_p(const float (&p)[4][16], v8i* pb, v4i* ph) {
     if constexpr (PVH) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -502,6 +548,18 @@ __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, flo
                 pb[kh][wd] = (int)u;
             }
     }
+}
+
+// The whole online softmax of one tile (both halves in one place).
+template <bool MASK, bool HAS_DS, bool PVH = false, int DT = 0, int QB = QBLK, int NPS = 8>
+__device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, float c1, float c2,
+                                     float c3, const float* dsl, float sml2, int kt0, int lim,
+                                     float& m_run, float& l_run) {
+    float p[4][16];
+    const float alpha = score_exp<MASK, HAS_DS, PVH, QB>(sacc, p, c0, c1, c2, c3, dsl, sml2, kt0,
+                                                         lim, m_run);
+    row_sum<NPS>(p, alpha, l_run);
+    pack_p<PVH, DT>(p, pb, ph);
     return alpha;
 }
 
@@ -514,6 +572,48 @@ __device__ inline void rescale(v16f* acc, float alpha) {
             for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
     }
 }
+
+// One MFMA phase of the FP8 path: acc = alpha*acc + V^T.P^T of the previous
+// tile (when pv), then S = Q.K^T of this tile into sacc.  The LDS operand reads
+// run ahead of the matrix instructions that consume them (two P.V
+// instructions, two Q.K chunks), so that their latency passes under earlier
+// matrix work instead of being waited for at every pair of reads; K chunk 0
+// is read first and arrives under the P.V.  With DEFER the previous tile's
+// P operand and row sum are formed here too, from its FP32 p in pd.
+template <int D, bool DEFER, int NPS>
+__device__ inline void mfma_phase(const uint8_t* Vs, const uint8_t* Ks, bool pv, v8i* pb,
+                                  const float (&pd)[4][16], v16i* sacc, v16f* acc, const v4i* qf,
+                                  float alpha, float& l_run) {
+    constexpr int NC = D / 32;
+    constexpr int NPV = 2 * NC;                // P.V instructions, kh-major
+    v4i ka[NC][4];
+    k_ops<D>(Ks, 0, ka[0]);
+    if (pv) {
+        v8i va[NPV];
+        va[0] = v_op<D>(Vs, 0, 0);
+        va[1] = v_op<D>(Vs, 1 / NC, 1 % NC);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DEFER) pack_p<false, 0>(pd, pb, nullptr);
+        rescale<D>(acc, alpha);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            if (i + 2 < NPV) va[i + 2] = v_op<D>(Vs, (i + 2) / NC, (i + 2) % NC);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[i % NC] = pv_mfma(va[i], pb[i / NC], acc[i % NC]);
+        }
+        if constexpr (DEFER) row_sum<NPS>(pd, alpha, l_run);
+    }
+    if constexpr (NC > 1) k_ops<D>(Ks, 1, ka[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    sbias_init(sacc);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (c + 2 < NC) k_ops<D>(Ks, c + 2, ka[c + 2]);
+        __builtin_amdgcn_sched_barrier(0);
+        qk_chunk(ka[c], qf[c], sacc);
+    }
+}
+
 
 template <int DT>
 __device__ inline uint32_t f2h_bits(float f) {
@@ -607,20 +707,27 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
 
     v8i pb[2];                  // P^ of the previous tile (E4M3)
     v4i ph[PVH ? 8 : 1];        // ... or its 16-bit p (PVH)
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int wd = 0; wd < 8; ++wd) pb[kh][wd] = 0;
-#pragma unroll
-    for (int i = 0; i < (PVH ? 8 : 1); ++i) ph[i] = v4i{0, 0, 0, 0};
-    // acc += V(t)^T . P^(t)^T in either operand type
-    auto pv = [&](int rr) {   // rr: the tile's place in the split
+    constexpr int NPS = D == 64 ? 16 : 8;
+    // Where a tile's row sum and P operand are formed.  At d = 64 the matrix
+    // phase is short and the softmax phase is the whole bound: they move to
+    // the next MFMA phase, under the P.V and Q.K matrix instructions.  At
+    // d = 96 and 128 the MFMA phase is as long as the softmax phase already,
+    // and they stay in the softmax phase.
+    constexpr bool DEFER = D == 64 && !PVH;
+    // software-pipelined LDS operand reads in the MFMA phase (FP8 path)
+    constexpr bool PIPE = true;
+    v16i sacc[4];               // a tile's biased int32 scores (Q.K^T)
+    float pd[4][16];            // with DEFER: the previous tile's FP32 p (else unused)
+    float alpha_prev = 1.0f;   // rescale owed to acc before its next P.V
+    // the P.V of the previous tile (its place rr in the split)
+    auto pv_prev = [&](int rr) {
+        if constexpr (DEFER) pack_p<PVH, DT>(pd, pb, ph);
+        rescale<D>(acc, alpha_prev);
         const uint8_t* vs_ = vst0 + (rr & 1) * T::VBYTES;
         if constexpr (PVH) pv_tile_h<D, DT>(vs_, ph, acc);
         else pv_tile<D>(vs_, pb, acc);
+        if constexpr (DEFER) row_sum<NPS>(pd, alpha_prev, l_run);
     };
-    v16i sacc[4];
-    float alpha_prev = 1.0f;   // rescale owed to acc before its next P.V
 
     for (int t = w.t0; t < w.nt_wg; ++t) {
         const int r = t - w.t0;
@@ -632,18 +739,19 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                                             si.npk, t + 1, w.hpw);
         stage_v<D, FWD_NT, PVH>(vst0 + (r & 1) * T::VBYTES, off, vbase, si.npk, t);
         if (t < w.nt_w) {
-            // P.V of the previous tile first: its P^ then dies before S(t)
-            // is formed (measured 0.2-0.8% faster than Q.K first with E4M3
-            // P^, and needed to fit the registers with 16-bit P^)
-            if (r > 0) {
-                rescale<D>(acc, alpha_prev);
-                pv(r - 1);
+            const uint8_t* ks_ = kst0 + (r & 1) * T::KBYTES;
+            if constexpr (PVH || !PIPE) {
+                // P.V of the previous tile first: its p then dies before S(t)
+                // is formed (needed to fit the registers with 16-bit P)
+                if (r > 0) pv_prev(r - 1);
+                qk_tile<D>(ks_, qf, sacc);
+            } else {
+                mfma_phase<D, DEFER, NPS>(vst0 + ((r - 1) & 1) * T::VBYTES, ks_, r > 0, pb, pd,
+                                          sacc, acc, qf, alpha_prev, l_run);
             }
-            qk_tile<D>(kst0 + (r & 1) * T::KBYTES, qf, sacc);
         } else if (t == w.nt_w && r > 0) {
             // this wave's rows are done: flush its last tile
-            rescale<D>(acc, alpha_prev);
-            pv(r - 1);
+            pv_prev(r - 1);
         }
         // the tile's score scales, loaded ahead of the softmax phase (the
         // empty asm keeps the compiler from sinking the loads past the barrier)
@@ -669,23 +777,27 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                                       : nullptr;
             const bool need_mask =
                 (t + 1) * KVT > nkv || (P.causal && (t + 1) * KVT - 1 > wave_diag);
-            float alpha;
-            if (need_mask)
-                alpha = softmax_tile<true, HAS_DS, PVH, DT, QB, D == 64 ? 16 : 8>(
-                    sacc, pb, ph, c0, c1, c2, c3, dsl, P.sml2, kt0, lim, m_run, l_run);
-            else
-                alpha = softmax_tile<false, HAS_DS, PVH, DT, QB, D == 64 ? 16 : 8>(
-                    sacc, pb, ph, c0, c1, c2, c3, dsl, P.sml2, kt0, lim, m_run, l_run);
-            // acc (the tiles before t, at the previous max) is rescaled in
-            // the next MFMA phase, before the P.V of tile t
-            alpha_prev = alpha;
+            // acc (the tiles before t, at the previous max) is rescaled by
+            // alpha in the next MFMA phase, before the P.V of tile t
+            if constexpr (DEFER) {
+                if (need_mask)
+                    alpha_prev = score_exp<true, HAS_DS, PVH, QB>(sacc, pd, c0, c1, c2, c3, dsl,
+                                                                  P.sml2, kt0, lim, m_run);
+                else
+                    alpha_prev = score_exp<false, HAS_DS, PVH, QB>(sacc, pd, c0, c1, c2, c3, dsl,
+                                                                   P.sml2, kt0, lim, m_run);
+            } else {
+                if (need_mask)
+                    alpha_prev = softmax_tile<true, HAS_DS, PVH, DT, QB, NPS>(
+                        sacc, pb, ph, c0, c1, c2, c3, dsl, P.sml2, kt0, lim, m_run, l_run);
+                else
+                    alpha_prev = softmax_tile<false, HAS_DS, PVH, DT, QB, NPS>(
+                        sacc, pb, ph, c0, c1, c2, c3, dsl, P.sml2, kt0, lim, m_run, l_run);
+            }
         }
         bar();
     }
-    if (w.nt_w > w.t0 && w.nt_w == w.nt_wg) {
-        rescale<D>(acc, alpha_prev);
-        pv(w.nt_wg - 1 - w.t0);
-    }
+    if (w.nt_w > w.t0 && w.nt_w == w.nt_wg) pv_prev(w.nt_wg - 1 - w.t0);
     if (grp == 0) bar();   // balance group 1's leading barrier
 
     // epilogue: lanes l and l+32 hold the same row's partial sums.  The
