@@ -305,6 +305,20 @@ SAGE_API sage_status sage_debug_qk_int32(const sage_attn_desc* desc, const int32
                                 const int32_t* cu_seqlens_kv, int32_t nseq,
                                 const sage_quant_bufs* bufs, int32_t* s_out, void* stream);
 
+/*
+ * sage_debug_e4m3_encode -- test hook: the OCP E4M3 codes of the FP32 values
+ * whose bit patterns are first, first+1, ..., first+count-1 (first + count <=
+ * 2^32), converted by the same device helper and in the same packing as every
+ * E4M3 code of the library (the V codes of the pre-pass and the P operand of
+ * the fused kernel), so that the conversion can be compared exhaustively with
+ * a reference encoder.  out: device, count bytes, 16-byte aligned.  Errors:
+ * SAGE_ERR_NULL (out NULL with count > 0), SAGE_ERR_ALIGN, SAGE_ERR_SHAPE
+ * (the range passes 2^32), SAGE_ERR_ARCH, SAGE_ERR_HIP.  Source: ComfyUI blog
+ * feature item 2 (P.V in FP8).
+ */
+SAGE_API sage_status sage_debug_e4m3_encode(uint32_t first, uint32_t count, uint8_t* out,
+                                            void* stream);
+
 /* Human-readable name of a status code (static storage). */
 SAGE_API const char* sage_status_string(sage_status status);
 

@@ -27,7 +27,7 @@ from ._abi import BF16, F16, HND, NHD, KV_TILE, QK_BLOCK, SageError, lib
 
 __all__ = ["sageattn", "sdpa", "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_quant_qkv",
            "sage_attn_fwd_quantized", "kv_split_size",
-           "sage_debug_qk_int32", "workspace_size", "quant_buf_sizes", "make_desc",
+           "sage_debug_qk_int32", "sage_debug_e4m3_encode", "workspace_size", "quant_buf_sizes", "make_desc",
            "SageError", "lib", "abi_version"]
 
 _DT = {torch.float16: F16, torch.bfloat16: BF16}
@@ -40,10 +40,50 @@ def abi_version() -> int:
 def _strides(t: torch.Tensor, layout: str, varlen: bool):
     if t.stride(-1) != 1:
         raise ValueError("the head_dim dimension must have stride 1")
+    for size, st in zip(t.shape, t.stride()):
+        if size > 1 and st == 0:
+            raise ValueError("a dimension of size > 1 has stride 0 (an expanded view): "
+                             "call .contiguous() first")
     s = t.stride()
     if varlen:
         return (0, s[1], s[0]) if layout == "NHD" else (0, s[0], s[1])
     return (s[0], s[2], s[1]) if layout == "NHD" else (s[0], s[1], s[2])
+
+
+def _check_shapes(q, k, v, o, layout, varlen):
+    """Refuse, before any GPU call, tensors whose shapes, devices or dtypes do
+    not describe one problem (the kernels would read or write out of bounds)."""
+    nd = 3 if varlen else 4
+    for name, t in (("q", q), ("k", k), ("v", v)) + ((("out", o),) if o is not None else ()):
+        if t.dim() != nd:
+            raise ValueError(f"{name} must have {nd} dimensions "
+                             f"({'packed [T,H,d] / [H,T,d]' if varlen else '[B,H,N,d] / [B,N,H,d]'}),"
+                             f" got {tuple(t.shape)}")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v must have k's shape {tuple(k.shape)}, got {tuple(v.shape)}")
+    if k.shape[-1] != q.shape[-1]:
+        raise ValueError(f"q and k head dims differ ({q.shape[-1]} vs {k.shape[-1]})")
+    if not varlen and k.shape[0] != q.shape[0]:
+        raise ValueError(f"q and k batch sizes differ ({q.shape[0]} vs {k.shape[0]})")
+    if o is not None and (tuple(o.shape) != tuple(q.shape) or o.dtype != q.dtype):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)} and dtype {q.dtype}, "
+                         f"got {tuple(o.shape)} {o.dtype}")
+
+
+def _check_devices(q, k, v, o):
+    for name, t in (("q", q), ("k", k), ("v", v)) + ((("out", o),) if o is not None else ()):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be on q's CUDA device ({q.device}), got {t.device}")
+
+
+def _check_tokens(q, k, layout, cu_q, n_q, cu_k, n_k):
+    """Varlen: the packed tensors must hold the tokens cu_seqlens names."""
+    tq = q.shape[0] if layout == "NHD" else q.shape[1]
+    tk = k.shape[0] if layout == "NHD" else k.shape[1]
+    if n_q > 0 and cu_q[n_q] > tq:
+        raise ValueError(f"cu_seqlens_q ends at {cu_q[n_q]} but q holds {tq} tokens")
+    if n_k > 0 and cu_k[n_k] > tk:
+        raise ValueError(f"cu_seqlens_kv ends at {cu_k[n_k]} but k and v hold {tk} tokens")
 
 
 def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q=False,
@@ -55,6 +95,7 @@ def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q
         raise ValueError(f"tensor_layout must be 'HND' or 'NHD', got {tensor_layout!r}")
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    _check_shapes(q, k, v, o, tensor_layout, varlen)
     if pv_mode not in _abi.PV_MODES:
         raise ValueError(f"pv_mode must be 'fp8' or 'half', got {pv_mode!r}")
     d = _abi.Desc()
@@ -83,6 +124,7 @@ def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q
     d.pv_mode = _abi.PV_MODES[pv_mode]
     d.kv_split = _abi.KV_SPLIT_AUTO if kv_split == "auto" else int(kv_split)
     d.qk_block = int(qk_block)
+    _check_devices(q, k, v, o)
     return d
 
 
@@ -160,13 +202,18 @@ def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=Fa
         bufs = {name: bufs[name] for name in sizes}
     qb = _abi.QuantBufs(**{name: (t.data_ptr() if sizes[name] else None) for name, t in bufs.items()})
     cq, n = _cu(cu_seqlens_q)
-    ck, _ = _cu(cu_seqlens_kv)
+    ck, nk = _cu(cu_seqlens_kv)
+    if varlen:
+        if nk != n:
+            raise ValueError("cu_seqlens_q and cu_seqlens_kv must have the same length")
+        _check_tokens(q, k, tensor_layout, cq, n, ck, nk)
     _abi.check("sage_quant_qkv",
                lib().sage_quant_qkv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), cq, ck, n,
                                     ctypes.byref(qb), _ptr(ws), ws.numel(), _stream(q)))
     bufs["_desc"] = desc
     bufs["_workspace"] = ws
     bufs["_sizes"] = sizes
+    bufs["_q_shape"] = (tuple(q.shape), q.dtype)
     return bufs
 
 
@@ -185,6 +232,11 @@ def sage_attn_fwd_quantized(bufs, out, *, cu_seqlens_q=None, cu_seqlens_kv=None,
     desc = bufs["_desc"]
     cq, n = _cu(cu_seqlens_q)
     ck, _ = _cu(cu_seqlens_kv)
+    shape = bufs.get("_q_shape")
+    if shape is not None and (tuple(out.shape) != shape[0] or out.dtype != shape[1]
+                              or out.device != bufs["q_codes"].device):
+        raise ValueError(f"out must have the quantized q's shape {shape[0]} and dtype "
+                         f"{shape[1]} on its device")
     qb = quant_bufs_struct(bufs)
     ws = bufs["_workspace"]
     _abi.check("sage_attn_fwd_quantized",
@@ -212,6 +264,20 @@ def sage_debug_qk_int32(bufs, *, cu_seqlens_q=None, cu_seqlens_kv=None, device=N
                lib().sage_debug_qk_int32(ctypes.byref(desc), cq, ck, n, ctypes.byref(qb),
                                          _ptr(out), _stream(out)))
     return out[:total]
+
+
+def sage_debug_e4m3_encode(first: int, count: int, out=None, device="cuda"):
+    """E4M3 codes (uint8 device tensor of `count` bytes) of the FP32 values
+    whose bit patterns are first .. first+count-1, converted by the library's
+    own device conversion (test hook)."""
+    if out is None:
+        out = torch.empty(max(1, count), dtype=torch.uint8, device=device)
+    elif out.dtype != torch.uint8 or not out.is_cuda or out.numel() < count:
+        raise ValueError("out must be a CUDA uint8 tensor of at least count bytes")
+    _abi.check("sage_debug_e4m3_encode",
+               lib().sage_debug_e4m3_encode(ctypes.c_uint32(first), ctypes.c_uint32(count),
+                                            _ptr(out), _stream(out)))
+    return out[:count]
 
 
 def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
@@ -250,6 +316,7 @@ def sage_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, tensor_layout=
     ck, nk = _cu(cu_seqlens_kv)
     if nk != n:
         raise ValueError("cu_seqlens_q and cu_seqlens_kv must have the same length")
+    _check_tokens(q, k, tensor_layout, cq, n, ck, nk)
     lse = None
     if return_lse:
         tq = cq[n] if n > 0 else 0

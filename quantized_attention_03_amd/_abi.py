@@ -23,7 +23,7 @@ QK_BLOCK, KV_TILE = 64, 128
 
 EXPORTS = ["sage_desc_init", "sage_quant_buf_sizes", "sage_workspace_size", "sage_quant_qkv",
            "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_attn_fwd_quantized",
-           "sage_debug_qk_int32", "sage_kv_split_size",
+           "sage_debug_qk_int32", "sage_debug_e4m3_encode", "sage_kv_split_size",
            "sage_status_string", "sage_abi_version"]
 
 
@@ -84,6 +84,7 @@ def lib():
                                           ctypes.c_size_t, P]),
         "sage_kv_split_size": (I32, [D, ip, ip, I32, ip]),
         "sage_debug_qk_int32": (I32, [D, ip, ip, I32, ctypes.POINTER(QuantBufs), P, P]),
+        "sage_debug_e4m3_encode": (I32, [ctypes.c_uint32, ctypes.c_uint32, P, P]),
         "sage_status_string": (ctypes.c_char_p, [I32]),
         "sage_abi_version": (I32, []),
     }

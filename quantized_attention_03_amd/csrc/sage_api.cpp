@@ -665,12 +665,22 @@ sage_status sage_debug_qk_int32(const sage_attn_desc* desc, const int32_t* cuq,
     for (KParams P : make_params(p)) {
         P.kv_tiles = 0;           // the dump covers every key of every row
         P.nsplit = 1;
-        DumpBase db{};
+        P.causal = 0;
         if (!P.tab.uniform)
-            for (int j = 0; j < P.tab.n; ++j) db.base[j] = gbase[P.tab.sid[j]];
-        SAGE_TRY(launch_qk_dump(P, bufs->q_codes, bufs->k_codes, s_out, db,
+            for (int j = 0; j < P.tab.n; ++j) P.tab.dump0[j] = gbase[P.tab.sid[j]];
+        SAGE_TRY(launch_qk_dump(P, bufs->q_codes, bufs->k_codes, s_out,
                                 static_cast<hipStream_t>(stream)));
     }
+    return SAGE_OK;
+}
+
+sage_status sage_debug_e4m3_encode(uint32_t first, uint32_t count, uint8_t* out, void* stream) {
+    if (count > 0 && !out) return SAGE_ERR_NULL;
+    if (!aligned16(out)) return SAGE_ERR_ALIGN;
+    if ((uint64_t)first + count > (uint64_t{1} << 32)) return SAGE_ERR_SHAPE;
+    sage_status e = check_arch();
+    if (e != SAGE_OK) return e;
+    SAGE_TRY(launch_e4m3_dump(first, count, out, static_cast<hipStream_t>(stream)));
     return SAGE_OK;
 }
 

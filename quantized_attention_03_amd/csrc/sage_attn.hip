@@ -542,9 +542,8 @@ __device__ inline void pack_p(const float (&p)[4][16], v8i* pb, v4i* ph) {
                 // second the high half, so the word's prior contents do not
                 // matter: it is seeded with a value that dies here (no zeroing
                 // move)
-                uint32_t u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0], p[b][r0 + 1],
-                                                             __float_as_uint(p[b][r0]), false);
-                u = __builtin_amdgcn_cvt_pk_fp8_f32(p[b][r0 + 2], p[b][r0 + 3], u, true);
+                uint32_t u = e4m3_pk<false>(p[b][r0], p[b][r0 + 1], __float_as_uint(p[b][r0]));
+                u = e4m3_pk<true>(p[b][r0 + 2], p[b][r0 + 3], u);
                 pb[kh][wd] = (int)u;
             }
     }
@@ -644,7 +643,7 @@ __device__ inline uint32_t f2h_bits(float f) {
 //   every wave waits for its copies before each barrier.
 //   bias(t): three buffers, as it is read up to epoch 2t+2.
 // ---------------------------------------------------------------------------
-template <int D, int DT, bool HAS_DS, bool PVH, int QB>
+template <int D, int DT, bool HAS_DS, bool PVH, int QB, bool DUMP = false>
 __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __restrict__ qc,
                                                  const float* __restrict__ qsc,
                                                  const int8_t* __restrict__ kc,
@@ -676,7 +675,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     if (w.nt_w > w.t0) {
         const int64_t qrow0 = si.rq * P.hq + (int64_t)w.head * si.npq;
         load_q<D>(qc + (qrow0 + my_q) * D, qf);
-        sq = qsc[(qrow0 + w.q0) / QB];
+        if constexpr (!DUMP) sq = qsc[(qrow0 + w.q0) / QB];
     } else {
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) qf[c] = v4i{0, 0, 0, 0};
@@ -737,7 +736,8 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
             stage_k<D, FWD_NT, HAS_DS, PVH>(kst0 + ((r + 1) & 1) * T::KBYTES,
                                             dst0 + ((r + 1) % 3) * T::DSBYTES, off, kbase, dsb,
                                             si.npk, t + 1, w.hpw);
-        stage_v<D, FWD_NT, PVH>(vst0 + (r & 1) * T::VBYTES, off, vbase, si.npk, t);
+        if constexpr (!DUMP)   // (the Q.K^T export reads no V)
+            stage_v<D, FWD_NT, PVH>(vst0 + (r & 1) * T::VBYTES, off, vbase, si.npk, t);
         if (t < w.nt_w) {
             const uint8_t* ks_ = kst0 + (r & 1) * T::KBYTES;
             if constexpr (PVH || !PIPE) {
@@ -746,10 +746,10 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                 if (r > 0) pv_prev(r - 1);
                 qk_tile<D>(ks_, qf, sacc);
             } else {
-                mfma_phase<D, DEFER, NPS>(vst0 + ((r - 1) & 1) * T::VBYTES, ks_, r > 0, pb, pd,
-                                          sacc, acc, qf, alpha_prev, l_run);
+                mfma_phase<D, DEFER, NPS>(vst0 + ((r - 1) & 1) * T::VBYTES, ks_, !DUMP && r > 0,
+                                          pb, pd, sacc, acc, qf, alpha_prev, l_run);
             }
-        } else if (t == w.nt_w && r > 0) {
+        } else if (!DUMP && t == w.nt_w && r > 0) {
             // this wave's rows are done: flush its last tile
             pv_prev(r - 1);
         }
@@ -760,6 +760,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         // keeps a masked key's -inf * c at -inf)
         constexpr int NB = KVT / QB;             // key blocks of a tile (2 or 4)
         auto cs = [&](int b) {
+            if constexpr (DUMP) return 0.0f;
             const float ks = kscb[NB * t + b];
             return fmaxf(HAS_DS ? sq * ks : sq * ks * P.sml2, FLT_MIN);
         };
@@ -770,7 +771,19 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         __builtin_amdgcn_s_setprio(0);
         bar();
         // ---- softmax phase ----
-        if (t < w.nt_w) {
+        if (DUMP && t < w.nt_w && my_q < nq) {
+            // the test export: the exact int32 scores of the tile's keys
+            int32_t* out = reinterpret_cast<int32_t*>(o) +
+                           (P.tab.uniform ? (int64_t)w.s * P.hq * nq * nkv : P.tab.dump0[w.s]) +
+                           ((int64_t)w.head * nq + my_q) * nkv;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int j = t * KVT + 32 * b + 16 * h + rr;
+                    if (j < nkv) out[j] = sacc[b][rr] - SBIAS_I;
+                }
+        } else if (!DUMP && t < w.nt_w) {
             const int kt0 = t * KVT + 16 * h;     // key of sacc[b][r] = kt0 + 32b + r
             const float* dsl = HAS_DS ? reinterpret_cast<const float*>(dst0 + (r % 3) * T::DSBYTES) +
                                             (w.head - w.head0) * KVT
@@ -797,8 +810,9 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         }
         bar();
     }
-    if (w.nt_w > w.t0 && w.nt_w == w.nt_wg) pv_prev(w.nt_wg - 1 - w.t0);
+    if (!DUMP && w.nt_w > w.t0 && w.nt_w == w.nt_wg) pv_prev(w.nt_wg - 1 - w.t0);
     if (grp == 0) bar();   // balance group 1's leading barrier
+    if constexpr (DUMP) return;
 
     // epilogue: lanes l and l+32 hold the same row's partial sums.  The
     // wave's 32 output rows are assembled in LDS (rows of RS bytes, 16-byte
@@ -1137,51 +1151,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 }
 
 // ---------------------------------------------------------------------------
-// Q.K^T dump for tests: the same key-tile staging and qk_tile as the fused
-// kernel (4-wave workgroups); the int32 scores are written instead of used.
+// Test export of the E4M3 conversion: thread i converts the FP32 bit patterns
+// first + 4i .. first + 4i + 3 and packs them into one word exactly as the
+// fused kernel packs its P operand (low half, then high half).
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(WG) void k_qk_dump(KParams P, const int8_t* __restrict__ qc,
-                                                const int8_t* __restrict__ kc,
-                                                int32_t* __restrict__ out, DumpBase db) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    const Work w = decode_work<4>(P);
-    const SeqInfo& si = w.si;
-    const int lane = threadIdx.x & 63;
-    const int h = lane >> 5, qi = lane & 31;
-    const int my_q = w.q0 + qi;
-    const int nq = si.nq, nkv = si.nkv;
-    const int64_t krow0 = (si.rk * P.hkv + (int64_t)w.hkv * si.npk);
-    const int8_t* kbase = kc + krow0 * D;
-    // the dump covers every key (no causal cut)
-    const int nt = (nkv + KVT - 1) / KVT;
-    DmaOffsets<D, WG> off;
-    off.init(si.npk);
-    v4i qf[D / 32];
-    if (w.q0 < nq) {
-        const int64_t qrow0 = si.rq * P.hq + (int64_t)w.head * si.npq;
-        load_q<D>(qc + (qrow0 + my_q) * D, qf);
+__global__ __launch_bounds__(WG) void k_e4m3_dump(uint32_t first, uint32_t count,
+                                                  uint8_t* __restrict__ out) {
+    const uint32_t i = blockIdx.x * WG + threadIdx.x;
+    const uint32_t e0 = 4u * i;
+    if (e0 >= count) return;
+    float x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(first + e0 + k);
+    uint32_t u = e4m3_pk<false>(x[0], x[1], __float_as_uint(x[0]));
+    u = e4m3_pk<true>(x[2], x[3], u);
+    if (e0 + 4 <= count) {
+        *reinterpret_cast<uint32_t*>(out + e0) = u;
     } else {
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) qf[c] = v4i{0, 0, 0, 0};
-    }
-    const int64_t base = P.tab.uniform ? (int64_t)w.s * P.hq * nq * nkv : db.base[w.s];
-    for (int t = 0; t < nt; ++t) {
-        stage_k<D, WG, false>(smem, nullptr, off, kbase, nullptr, si.npk, t, 1);
-        bar();
-        v16i sacc[4];
-        qk_tile<D>(smem, qf, sacc);
-        if (w.q0 < nq && my_q < nq) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = t * KVT + 32 * b + 16 * h + r;
-                    if (j < nkv)
-                        out[base + ((int64_t)w.head * nq + my_q) * nkv + j] = sacc[b][r] - SBIAS_I;
-                }
-        }
-        bar();
+        for (uint32_t k = 0; e0 + k < count; ++k) out[e0 + k] = (uint8_t)(u >> (8 * k));
     }
 }
 
@@ -1310,17 +1297,29 @@ hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const floa
 #undef SAGE_AQ
 }
 
-hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,
-                          const DumpBase& db, hipStream_t st) {
-    const int nblocks = wg_count_host(P, 4);
+namespace {
+template <int D>
+hipError_t qk_dump_d(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,
+                     hipStream_t st) {
+    static std::atomic<uint64_t> attr_set{0};
+    auto* kern = &k_attn<D, 0, false, false, QBLK, true>;
+    hipError_t e = lds_attr(reinterpret_cast<const void*>(kern), lds_bytes<D, false, false>(),
+                            attr_set);
+    if (e != hipSuccess) return e;
+    const int nblocks = wg_count_host(P, FWD_WAVES);
     if (nblocks <= 0) return hipSuccess;
-    if (P.d == 64)
-        k_qk_dump<64><<<nblocks, WG, Tile<64>::KBYTES, st>>>(P, qc, kc, s_out, db);
-    else if (P.d == 96)
-        k_qk_dump<96><<<nblocks, WG, Tile<96>::KBYTES, st>>>(P, qc, kc, s_out, db);
-    else
-        k_qk_dump<128><<<nblocks, WG, Tile<128>::KBYTES, st>>>(P, qc, kc, s_out, db);
+    kern<<<nblocks, FWD_NT, lds_bytes<D, false, false>(), st>>>(
+        P, qc, nullptr, kc, nullptr, nullptr, nullptr, nullptr, nullptr,
+        reinterpret_cast<uint16_t*>(s_out), nullptr);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,
+                          hipStream_t st) {
+    if (P.d == 64) return qk_dump_d<64>(P, qc, kc, s_out, st);
+    if (P.d == 96) return qk_dump_d<96>(P, qc, kc, s_out, st);
+    return qk_dump_d<128>(P, qc, kc, s_out, st);
 }
 
 
@@ -1416,6 +1415,14 @@ hipError_t launch_merge(const MergeArgs& M, int dtype, hipStream_t st) {
     const int64_t nb = (M.rows_total + 3) / 4;   // four rows (waves) per workgroup
     if (dtype == 0) k_merge<0><<<(unsigned)nb, 256, 0, st>>>(M);
     else k_merge<1><<<(unsigned)nb, 256, 0, st>>>(M);
+    return hipGetLastError();
+}
+
+hipError_t launch_e4m3_dump(uint32_t first, uint32_t count, uint8_t* out, hipStream_t st) {
+    if (count == 0) return hipSuccess;
+    const uint32_t threads = (count + 3) / 4;
+    const uint32_t blocks = (threads + WG - 1) / WG;
+    k_e4m3_dump<<<blocks, WG, 0, st>>>(first, count, out);
     return hipGetLastError();
 }
 

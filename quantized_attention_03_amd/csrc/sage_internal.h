@@ -33,6 +33,8 @@ struct SeqTab {
     int64_t rq[MAXSEQ], rk[MAXSEQ];     // padded row bases in the code buffers
     int32_t sid[MAXSEQ];                // sequence index for [S][H][d] arrays and lse
     int64_t lse_base[MAXSEQ];           // first lse element of sequence s (head 0)
+    int64_t dump0[MAXSEQ];              // first element of sequence s in the int32
+                                        // Q.K^T test export (varlen)
 };
 
 struct KParams {
@@ -78,6 +80,15 @@ struct SeqInfo {
 };
 
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Two FP32 values converted to OCP E4M3 (round to nearest even) by the
+// hardware's v_cvt_pk_fp8_f32 and written into the low (HI = false) or high
+// 16 bits of `old`: every E4M3 code of the library (V codes, the P operand)
+// and the test export of the conversion go through this one helper.
+template <bool HI>
+__device__ inline uint32_t e4m3_pk(float a, float b, uint32_t old) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
 
 __device__ inline SeqInfo seq_info(const KParams& P, int s) {
     const SeqTab& t = P.tab;
@@ -194,10 +205,14 @@ bool use_decode_kernel(const KParams& P);
 // LDS stages of a wave do not fit four times.
 int decode_waves_per_cu(int d, bool pv_half, bool has_ds, int group);
 hipError_t launch_merge(const MergeArgs& M, int dtype, hipStream_t st);
-struct DumpBase {
-    int64_t base[MAXSEQ];               // first element of sequence s in the dump
-};
+// The int32 Q.K^T of every (row, key) of the launch's sequences, written by
+// the fused kernel's own staging and Q.K^T code (the test export; P.causal
+// and the key split must be off, P.tab.dump0 set for varlen tables).
 hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,
-                          const DumpBase& db, hipStream_t st);
+                          hipStream_t st);
+// E4M3 codes of the FP32 bit patterns first, first+1, ..., first+count-1,
+// converted four per word as the fused kernel packs its P operand (the test
+// export of the conversion).
+hipError_t launch_e4m3_dump(uint32_t first, uint32_t count, uint8_t* out, hipStream_t st);
 
 }  // namespace sage

@@ -485,7 +485,7 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
                 // a zero scale gives +0 codes (never the -0 of a negative x * 0)
                 const float y0 = inv[e] > 0.0f ? x0 * inv[e] : 0.0f;
                 const float y1 = inv[e + 1] > 0.0f ? x1 * inv[e + 1] : 0.0f;
-                const uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0u, false);
+                const uint32_t pk = e4m3_pk<false>(y0, y1, 0u);
                 word[e] |= (pk & 0xffu) << (8 * u);
                 word[e + 1] |= ((pk >> 8) & 0xffu) << (8 * u);
             }

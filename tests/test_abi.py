@@ -24,7 +24,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     L = qa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -248,3 +248,15 @@ def test_empty_problem_is_a_no_op():
     # happens before the arch check, which an empty problem still performs)
     st = _fwd(d, q=0, k=0, v=0, o=0, ws=0, ws_bytes=0)
     assert _abi.STATUS_NAMES[st] in ("SAGE_OK", "SAGE_ERR_HIP", "SAGE_ERR_ARCH")
+
+
+def test_e4m3_export_argument_errors():
+    # each case fails before any HIP call
+    L = qa.lib()
+    u32 = ctypes.c_uint32
+    name = lambda st: _abi.STATUS_NAMES[st]
+    assert name(L.sage_debug_e4m3_encode(u32(0), u32(16), None, None)) == "SAGE_ERR_NULL"
+    assert name(L.sage_debug_e4m3_encode(u32(0), u32(16), ctypes.c_void_p(FAKE + 4),
+                                         None)) == "SAGE_ERR_ALIGN"
+    assert name(L.sage_debug_e4m3_encode(u32(0xFFFFFFF0), u32(32), ctypes.c_void_p(FAKE),
+                                         None)) == "SAGE_ERR_SHAPE"

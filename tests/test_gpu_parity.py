@@ -48,6 +48,11 @@ CASES = {
                            seqlens_q=[5, 0, 70, 33], seqlens_kv=[0, 40, 129, 1]),
     "varlen_empty_smooth_all": R(W["varlen_d96"], Hq=2, Hkv=2, smooth_q=True, smooth_v=True,
                                  causal=False, seqlens_q=[0, 17, 64], seqlens_kv=[9, 0, 200]),
+    # more sequences than one launch's table holds (32): several tables, each
+    # ordered by cost, in one call
+    "varlen_40_seqs": R(W["varlen_d128"], d=64, Hq=4, Hkv=2, seed=16,
+                        seqlens_q=[int(x) for x in np.random.default_rng(16).integers(0, 150, 40)],
+                        seqlens_kv=[int(x) for x in np.random.default_rng(17).integers(0, 300, 40)]),
 }
 
 
@@ -164,3 +169,31 @@ def test_quantized_entry_matches_full_call(case):
     torch.cuda.synchronize()
     assert torch.equal(o2.view(torch.int16), o_full.view(torch.int16))
     assert torch.equal(lse2.view(torch.int32), lse_full.view(torch.int32))
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_strided_output_matches_contiguous(layout):
+    """o (and q) as views into wider tensors: the output is written through
+    its own strides, leaving the rest of the wider tensor untouched."""
+    w = R(W["causal_gqa"], B=2, Hq=4, Hkv=2, Nq=200, Nkv=260, layout=layout, seed=22)
+    pu.say(f"[strided output {layout}]")
+    q, k, v, meta = pu.gpu_inputs(w)
+    o_ref, lse_ref = pu.run_fwd(w, q, k, v, meta)
+    if layout == "NHD":
+        wide = torch.full((2, 200, 7, 128), 7.0, dtype=q.dtype, device="cuda")
+        o_view = wide[:, :, 2:6]
+    else:
+        wide = torch.full((2, 4, 230, 160), 7.0, dtype=q.dtype, device="cuda")
+        o_view = wide[:, :, 10:210, :128]
+    assert not o_view.is_contiguous()
+    o, lse = pu.qa.sage_attn_fwd(q, k, v, tensor_layout=layout, is_causal=True,
+                                 return_lse=True, out=o_view)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(lse, lse_ref)
+    untouched = torch.ones_like(wide, dtype=torch.bool)
+    if layout == "NHD":
+        untouched[:, :, 2:6] = False
+    else:
+        untouched[:, :, 10:210, :128] = False
+    assert bool((wide[untouched] == 7.0).all())
