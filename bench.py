@@ -7,10 +7,19 @@ already resident in HBM).  The metric is attention TOPS with the headline
 formula 4*B*Hq*Nq*Nkv*d, halved for causal.
 
 Prints ONE JSON line.  Besides the standard fields it carries
-  roofline     : the fused kernel (the dominant launch) timed alone with HIP
-                 events on its stream, algorithmic ops (4*d per visible
-                 (q, k) pair) per launch / average launch time, against the
-                 dense INT8/FP8 MFMA peak of MI355X (5.0 POPS);
+  roofline     : the fused kernel (the dominant launch) against the dense
+                 INT8/FP8 MFMA peak of MI355X (5.0 POPS): algorithmic ops
+                 (4*d per visible (q, k) pair) per launch / its average
+                 duration.  The call is split into its two halves
+                 (sage_quant_qkv, then sage_attn_fwd_quantized on the same
+                 buffers: the same launches as sage_attn_fwd), and each half
+                 is timed in a loop of its own with HIP events on the launch
+                 stream around the loop; kernel_ms is the fused kernel's
+                 half, prepass_ms the other, measured, not a difference, and
+                 halves_sum_ms their sum next to ms_per_step;
+  n32k         : the same figures for the long-context varlen workload at
+                 d=128 (four packed sequences, keys up to 32768 per
+                 sequence), the metric's N=32K point;
   cpu_baseline : the CPU oracle (same recipe, plain C) timed on a bounded
                  sample of the same workload on the host cores.
 --pv half times the 16-bit P.V variant instead (P and V in the input's type
@@ -22,7 +31,7 @@ time has passed (the clocks settle); the JSON line reports how many ran.
 arithmetic intensity (ops per algorithmic byte of the fused kernel) is below
 the ridge of 5.0 POPS / 8 TB/s is reported against HBM instead: achieved =
 algorithmic bytes (Q, K, V codes and scales, O, split partials written and
-read back) per call / the kernel-only call's time, peak 8 TB/s.
+read back) per call / the fused kernel's time, peak 8 TB/s.
 """
 from __future__ import annotations
 
@@ -40,6 +49,7 @@ PEAK_TOPS = 5000.0           # MI355X dense INT8 / FP8 MFMA peak (T-ops/s)
 PEAK_16 = 2500.0             # ... dense fp16 / bf16 MFMA peak
 PEAK_HBM = 8000.0            # MI355X HBM3E bandwidth (GB/s)
 WORKLOAD = "causal_gqa"
+SECOND = "varlen_d128"         # the N=32K point, reported next to the N=8K one
 
 
 def _parse():
@@ -58,6 +68,8 @@ def _parse():
     ap.add_argument("--qk-block", type=int, choices=(64, 32), default=64,
                     help="tokens per Q/K quantization block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-second", action="store_true",
+                    help="skip the N=32K point (varlen_d128) that the default workload adds")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows per query head")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the reference "
@@ -130,6 +142,7 @@ def cpu_baseline(w, q, k, v, rows_per_head: int, pv: str = "fp8", split: int = 0
     dt = time.perf_counter() - t0
     ops = 4.0 * w.d * pairs
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "cpu_model": host_cpu_model(),
             "sample": f"same-recipe forward of {sum(len(r) for r in rows)} query rows per head "
                       f"group ({rows_per_head} evenly spaced rows x {w.Hq} heads, {pairs} visible "
                       f"pairs, {dt:.1f} s wall), pre-pass excluded"}
@@ -150,25 +163,25 @@ def kernel_bytes(w, pv: str, nsplit: int) -> float:
     return tot
 
 
-def main():
-    args = _parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the library has no multi-GPU path "
-              "(the forward pass shards over batch and heads with no exchange)",
-              file=sys.stderr)
-        sys.exit(2)
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def measure(w, args, dev):
+    """Time one workload: the whole call (the step) and its two halves.
+    Returns the inputs and a dict of timings (ms)."""
     import torch
-
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
 
     import quantized_attention_03_amd as qa
     import synth
 
-    w = synth.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
     q, k, v, meta = synth.make_inputs(w, device=dev)
     kv_split = args.kv_split if args.kv_split == "auto" else int(args.kv_split)
     kw = dict(tensor_layout=w.layout, is_causal=w.causal, smooth_q=w.smooth_q,
@@ -193,6 +206,7 @@ def main():
             qa.sage_attn_fwd(q, k, v, out=o, workspace=ws, **kw)
 
     stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
     # W untimed steps, continued until the clocks have settled (min-warmup-s
     # of wall time): with a short warm-up the timed loop still ran part of
     # the time at lower clocks (7% slower at W = 10 on causal_gqa)
@@ -204,7 +218,7 @@ def main():
         if warm % 10 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = ev(), ev()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
@@ -214,8 +228,7 @@ def main():
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
     # the same steps timed one by one (median and minimum of the whole call)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [(ev(), ev()) for _ in range(args.steps)]
     for a, b in evs:
         a.record(stream)
         step()
@@ -223,38 +236,99 @@ def main():
     torch.cuda.synchronize()
     per_step = sorted(a.elapsed_time(b) for a, b in evs)
 
-    # the fused kernel alone, on buffers quantized once (one launch per call)
+    # The call's two halves, each timed in a loop of its own with events only
+    # around the loop: the pre-pass (sage_quant_qkv) into buffers of the same
+    # layout as the call's workspace, and the fused kernel
+    # (sage_attn_fwd_quantized) on them -- together the same launches as
+    # sage_attn_fwd.  (An event recorded between the two halves of every
+    # call slows the fused kernel by about 18% in the kernel trace, so the
+    # halves are not timed inside one loop.)
     bufs = qa.sage_quant_qkv(q, k, v, **kw, **cu)
-    o2 = torch.empty_like(q)
-    for _ in range(max(3, args.warmup)):
-        qa.sage_attn_fwd_quantized(bufs, o2, **cu)
-    torch.cuda.synchronize()
-    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ka.record(stream)
-    for _ in range(args.steps):
-        qa.sage_attn_fwd_quantized(bufs, o2, **cu)
-    kb.record(stream)
-    torch.cuda.synchronize()
-    kern_ms = ka.elapsed_time(kb) / args.steps
-    # the pre-pass share of a call: the whole call minus the fused kernel
-    # (timing sage_quant_qkv alone would mostly time the Python binding)
-    pre_ms = max(ms - kern_ms, 0.0)
 
-    formula = w.formula_ops()
-    exact = w.exact_ops()
-    value = formula / (ms * 1e-3) / 1e12
-    achieved = exact / (kern_ms * 1e-3) / 1e12
+    def half_loop(fn):
+        t1 = time.perf_counter()
+        n = 0
+        while n < 10 or time.perf_counter() - t1 < 0.1:
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+        ka, kb = ev(), ev()
+        ka.record(stream)
+        for _ in range(args.steps):
+            fn()
+        kb.record(stream)
+        torch.cuda.synchronize()
+        return ka.elapsed_time(kb) / args.steps
+
+    pre_ms = half_loop(lambda: qa.sage_quant_qkv(q, k, v, **kw, **cu, bufs=bufs))
+    kern_ms = half_loop(lambda: qa.sage_attn_fwd_quantized(bufs, o, **cu))
+    res = {"ms": ms, "ms_median": per_step[len(per_step) // 2], "ms_min": per_step[0],
+           "kernel_ms": kern_ms, "prepass_ms": pre_ms, "wall": wall, "warm": warm,
+           "split": qa.kv_split_size(desc, cu.get("cu_seqlens_q"), cu.get("cu_seqlens_kv"))}
+    del bufs, ws, o
+    return (q, k, v), res
+
+
+def roofline(w, args, r):
+    """The fused kernel against its roofline, from the timings of measure()."""
     half = args.pv == "half"
+    exact = w.exact_ops()
     # half the ops are INT8 Q.K^T, half P.V in the operand type
     peak = PEAK_TOPS if not half else 1.0 / (0.5 / PEAK_TOPS + 0.5 / PEAK_16)
-    split = qa.kv_split_size(desc, cu.get("cu_seqlens_q"), cu.get("cu_seqlens_kv"))
+    split = r["split"]
     max_nkv = max(nkv for _, nkv in w.seq_lens())
     nsplit = math.ceil(max_nkv / split) if split else 1
     kbytes = kernel_bytes(w, args.pv, nsplit)
+    kern_ms = r["kernel_ms"]
     # a split key range whose GQA group x queries fit one wave's 32 rows runs
     # the one-wave decode kernel
     dec = bool(split) and (w.Hq // w.Hkv) * max(1, max(nq for nq, _ in w.seq_lens())) <= 32
     hbm_bound = exact / kbytes < peak * 1e12 / (PEAK_HBM * 1e9)
+    pvt = ("f16" if w.dtype == "f16" else "bf16") if half else "fp8"
+    if not hbm_bound:
+        achieved = exact / (kern_ms * 1e-3) / 1e12
+        rl = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+              "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    else:
+        gbs = kbytes / (kern_ms * 1e-3) / 1e9
+        rl = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
+              "frac": round(gbs / PEAK_HBM, 4), "bytes_per_launch": kbytes}
+    rl["traffic"] = (measured_traffic(w.name, "k_decode")
+                     if dec and not half and args.kv_split == "auto" and args.qk_block == 64 else
+                     None if half or split or args.qk_block != 64 else measured_traffic(w.name))
+    rl["kernel"] = ((f"k_decode (one wave per kv head and split, INT8-QK / softmax / "
+                     f"{pvt.upper()}-PV)" if dec else
+                     f"k_attn (fused INT8-QK / softmax / {pvt.upper()}-PV)")
+                    + (f" + k_merge ({nsplit} splits of {split} keys)" if split else ""))
+    rl["kernel_ms"] = round(kern_ms, 4)
+    rl["ops_per_launch"] = exact
+    return rl
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the forward pass shards over batch and heads with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    (q, k, v), r = measure(w, args, dev)
+    ms = r["ms"]
+    formula = w.formula_ops()
+    exact = w.exact_ops()
+    value = formula / (ms * 1e-3) / 1e12
+    half = args.pv == "half"
     io = "fp16 io" if w.dtype == "f16" else "bf16 io"
     pvt = ("f16" if w.dtype == "f16" else "bf16") if half else "fp8"
     line = {
@@ -264,10 +338,10 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_steps_run": warm,
+        "warmup_steps_run": r["warm"],
         "ms_per_step": round(ms, 4),
-        "ms_median": round(per_step[len(per_step) // 2], 4),
-        "ms_min": round(per_step[0], 4),
+        "ms_median": round(r["ms_median"], 4),
+        "ms_min": round(r["ms_min"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -279,29 +353,36 @@ def main():
                                f"{', 16-bit P.V' if half else ''}"
                                f"{', 32-token Q/K blocks' if args.qk_block == 32 else ''}",
                    "global_batch": w.B, "seq_len": w.Nq, "parallelism": "single-gpu"},
-        "roofline": ({"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
-                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
-                     if not hbm_bound else
-                     {"bound": "hbm", "achieved": round(kbytes / (kern_ms * 1e-3) / 1e9, 1),
-                      "peak": PEAK_HBM, "unit": "GB/s",
-                      "frac": round(kbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM, 4),
-                      "bytes_per_launch": kbytes}) | {
-                     "traffic": (measured_traffic(w.name, "k_decode")
-                                 if dec and not half and args.kv_split == "auto"
-                                 and args.qk_block == 64 else
-                                 None if half or split or args.qk_block != 64
-                                 else measured_traffic(w.name)),
-                     "kernel": (f"k_decode (one wave per kv head and split, INT8-QK / "
-                                f"softmax / {pvt.upper()}-PV)" if dec else
-                                f"k_attn (fused INT8-QK / softmax / {pvt.upper()}-PV)")
-                               + (f" + k_merge ({nsplit} splits of {split} keys)" if split else ""),
-                     "kernel_ms": round(kern_ms, 4), "ops_per_launch": exact},
-        "prepass_ms": round(pre_ms, 4),   # whole call minus the fused kernel
+        "roofline": roofline(w, args, r),
+        # the call's two halves, each timed in its own loop (their sum is
+        # within a few percent of ms_per_step)
+        "prepass_ms": round(r["prepass_ms"], 4),
+        "kernel_ms": round(r["kernel_ms"], 4),
+        "halves_sum_ms": round(r["prepass_ms"] + r["kernel_ms"], 4),
         "exact_pair_tops": round(exact / (ms * 1e-3) / 1e12, 2),
-        "wall_s": round(wall, 3),
+        "wall_s": round(r["wall"], 3),
     }
+    if w.varlen:
+        line["config"]["workload"] = (f"{w.name}: {len(w.seq_lens())} packed sequences "
+                                      f"(Nq, Nkv) = {w.seq_lens()}, H={w.Hq} d={w.d} "
+                                      f"{w.dtype} {w.layout}{' causal bottom-right' if w.causal else ''}")
+        line["config"]["seq_len"] = max(nkv for _, nkv in w.seq_lens())
+    second = None if args.no_second or args.workload != WORKLOAD else SECOND
+    if second:
+        w2 = synth.WORKLOADS[second]
+        _, r2 = measure(w2, args, dev)
+        rl2 = roofline(w2, args, r2)
+        line["n32k"] = {
+            "workload": f"{w2.name}: {len(w2.seq_lens())} packed sequences (Nq, Nkv) = "
+                        f"{w2.seq_lens()}, H={w2.Hq} d={w2.d} {w2.dtype} {w2.layout} causal "
+                        f"bottom-right",
+            "value": round(w2.formula_ops() / (r2["ms"] * 1e-3) / 1e12, 2),
+            "exact_pair_tops": round(w2.exact_ops() / (r2["ms"] * 1e-3) / 1e12, 2),
+            "unit": "TOPS", "ms_per_step": round(r2["ms"], 4),
+            "prepass_ms": round(r2["prepass_ms"], 4), "kernel_ms": round(r2["kernel_ms"], 4),
+            "frac": rl2["frac"], "achieved": rl2["achieved"]}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, args.pv, split,
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, args.pv, r["split"],
                                             args.qk_block)
     print(json.dumps(line), flush=True)
 
