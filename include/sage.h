@@ -267,6 +267,25 @@ SAGE_API sage_status sage_attn_fwd_varlen(const sage_attn_desc* desc, const int3
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sage_attn_fwd_noalloc -- sage_attn_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments and checks as
+ * sage_attn_fwd without the workspace: the workspace is the library's own
+ * static device array of SAGE_NOALLOC_WS_MAX bytes, one per device, held
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).  Problems whose workspace
+ * (sage_workspace_size) exceeds SAGE_NOALLOC_WS_MAX return
+ * SAGE_ERR_WORKSPACE.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents (nothing in it has to start at zero):
+ * calls that overlap on one GPU (different streams, or host threads) race
+ * and must be serialized by the caller.
+ */
+#define SAGE_NOALLOC_WS_MAX ((size_t)64 << 20)
+SAGE_API sage_status sage_attn_fwd_noalloc(const sage_attn_desc* desc, const void* q,
+                                           const void* k, const void* v, void* o, float* lse,
+                                           void* stream);
+
+/*
  * sage_attn_fwd_quantized -- the fused kernel alone, on tensors that
  * sage_quant_qkv wrote for the same descriptor and cu_seqlens (dense when
  * cu_seqlens_q == NULL).  Lets a caller quantize K/V once and attend to them

@@ -26,6 +26,7 @@ from . import _abi
 from ._abi import BF16, F16, HND, NHD, KV_TILE, QK_BLOCK, SageError, lib
 
 __all__ = ["sageattn", "sdpa", "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_quant_qkv",
+           "sage_attn_fwd_noalloc",
            "sage_attn_fwd_quantized", "kv_split_size",
            "sage_debug_qk_int32", "sage_debug_e4m3_encode", "workspace_size", "quant_buf_sizes", "make_desc",
            "SageError", "lib", "abi_version"]
@@ -299,6 +300,23 @@ def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=Fal
                lib().sage_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                    _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q)))
     return (o, lse) if return_lse else o
+
+
+def sage_attn_fwd_noalloc(q, k, v, out, *, tensor_layout="HND", is_causal=False,
+                          smooth_q=False, smooth_k=True, smooth_v=False, sm_scale=None,
+                          lse=None, pv_mode="fp8", kv_split=0, qk_block=64):
+    """Dense forward pass into the caller's `out` (and optional FP32 `lse`
+    [B, hq, nq]) with the library's own static workspace: the call allocates
+    nothing, on the device or through torch (for code that cannot).  Calls
+    that overlap on one GPU race (they share its workspace)."""
+    desc = make_desc(q, k, v, out, tensor_layout=tensor_layout, is_causal=is_causal,
+                     smooth_q=smooth_q, smooth_k=smooth_k, smooth_v=smooth_v,
+                     sm_scale=sm_scale, pv_mode=pv_mode, kv_split=kv_split,
+                     qk_block=qk_block)
+    _abi.check("sage_attn_fwd_noalloc",
+               lib().sage_attn_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(out), _ptr(lse), _stream(q)))
+    return out
 
 
 def sage_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, tensor_layout="NHD",

@@ -20,9 +20,11 @@ PV_MODES = {"fp8": PV_FP8, "half": PV_HALF}
 KV_SPLIT_AUTO = -1
 HND, NHD = 0, 1
 QK_BLOCK, KV_TILE = 64, 128
+NOALLOC_WS_MAX = 64 << 20     # SAGE_NOALLOC_WS_MAX
 
 EXPORTS = ["sage_desc_init", "sage_quant_buf_sizes", "sage_workspace_size", "sage_quant_qkv",
            "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_attn_fwd_quantized",
+           "sage_attn_fwd_noalloc",
            "sage_debug_qk_int32", "sage_debug_e4m3_encode", "sage_kv_split_size",
            "sage_status_string", "sage_abi_version"]
 
@@ -79,6 +81,7 @@ def lib():
         "sage_quant_qkv": (I32, [D, P, P, P, ip, ip, I32, ctypes.POINTER(QuantBufs), P,
                                  ctypes.c_size_t, P]),
         "sage_attn_fwd": (I32, [D, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "sage_attn_fwd_noalloc": (I32, [D, P, P, P, P, P, P]),
         "sage_attn_fwd_varlen": (I32, [D, ip, ip, I32, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "sage_attn_fwd_quantized": (I32, [D, ip, ip, I32, ctypes.POINTER(QuantBufs), P, P, P,
                                           ctypes.c_size_t, P]),

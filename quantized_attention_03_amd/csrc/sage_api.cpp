@@ -601,6 +601,20 @@ sage_status sage_attn_fwd(const sage_attn_desc* desc, const void* q, const void*
     return forward(desc, nullptr, nullptr, 0, false, q, k, v, o, lse, ws, ws_bytes, stream);
 }
 
+sage_status sage_attn_fwd_noalloc(const sage_attn_desc* desc, const void* q, const void* k,
+                                  const void* v, void* o, float* lse, void* stream) {
+    // the checks of sage_attn_fwd, then the workspace: the static array of
+    // this device (no allocation of any kind)
+    Plan p;
+    sage_status e = make_plan(desc, nullptr, nullptr, 0, false, &p);
+    if (e != SAGE_OK) return e;
+    if (ws_layout(p, true).total > NOALLOC_WS_MAX) return SAGE_ERR_WORKSPACE;
+    if ((e = check_arch()) != SAGE_OK) return e;
+    void* ws = nullptr;
+    SAGE_TRY(noalloc_workspace(&ws));
+    return forward(desc, nullptr, nullptr, 0, false, q, k, v, o, lse, ws, NOALLOC_WS_MAX, stream);
+}
+
 sage_status sage_attn_fwd_varlen(const sage_attn_desc* desc, const int32_t* cuq,
                                  const int32_t* cuk, int32_t nseq, const void* q, const void* k,
                                  const void* v, void* o, float* lse, void* ws, size_t ws_bytes,

@@ -47,6 +47,8 @@
 #include <algorithm>
 #include <atomic>
 #include <cfloat>
+#include <mutex>
+#include <vector>
 
 #include "sage_internal.h"
 
@@ -1424,6 +1426,33 @@ hipError_t launch_e4m3_dump(uint32_t first, uint32_t count, uint8_t* out, hipStr
     const uint32_t blocks = (threads + WG - 1) / WG;
     k_e4m3_dump<<<blocks, WG, 0, st>>>(first, count, out);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The workspace of the allocation-free entry point: a file-scope device array
+// (each device the library runs on holds its own copy until the process
+// ends).  In host code `scratch` only stands for the symbol: its device
+// address on a device comes from hipGetSymbolAddress with that device
+// current, taken once per device and kept; only that address is passed on.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[NOALLOC_WS_MAX];
+
+hipError_t noalloc_workspace(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::vector<void*> addr;     // per device id; nullptr until taken
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (!addr[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace sage

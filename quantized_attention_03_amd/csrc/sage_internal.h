@@ -210,6 +210,13 @@ hipError_t launch_merge(const MergeArgs& M, int dtype, hipStream_t st);
 // and the key split must be off, P.tab.dump0 set for varlen tables).
 hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, int32_t* s_out,
                           hipStream_t st);
+// The workspace of sage_attn_fwd_noalloc: the library's own static device
+// array (NOALLOC_WS_MAX bytes, 256-byte aligned), one per device.  Returns
+// its device address on the current device, taken once per device with
+// hipGetSymbolAddress and kept.
+constexpr size_t NOALLOC_WS_MAX = size_t{64} << 20;
+hipError_t noalloc_workspace(void** ptr);
+
 // E4M3 codes of the FP32 bit patterns first, first+1, ..., first+count-1,
 // converted four per word as the fused kernel packs its P operand (the test
 // export of the conversion).

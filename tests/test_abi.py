@@ -24,7 +24,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     L = qa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -260,3 +260,20 @@ def test_e4m3_export_argument_errors():
                                          None)) == "SAGE_ERR_ALIGN"
     assert name(L.sage_debug_e4m3_encode(u32(0xFFFFFFF0), u32(32), ctypes.c_void_p(FAKE),
                                          None)) == "SAGE_ERR_SHAPE"
+
+
+def test_noalloc_refuses_large_workspace_before_any_gpu_call():
+    # B=2, H=32, N=4096, d=128: about 100 MB of workspace, beyond the 64 MiB array
+    L = qa.lib()
+    d = _abi.Desc()
+    L.sage_desc_init(ctypes.byref(d), _abi.BF16, _abi.NHD, 2, 32, 32, 4096, 4096, 128)
+    ws = ctypes.c_size_t(0)
+    assert L.sage_workspace_size(ctypes.byref(d), None, None, 0, ctypes.byref(ws)) == 0
+    assert ws.value > _abi.NOALLOC_WS_MAX
+    f = ctypes.c_void_p(FAKE)
+    assert _abi.STATUS_NAMES[L.sage_attn_fwd_noalloc(ctypes.byref(d), f, f, f, f, None, None)] \
+        == "SAGE_ERR_WORKSPACE"
+    # and the descriptor checks come first, as in sage_attn_fwd
+    d.head_dim = 80
+    assert _abi.STATUS_NAMES[L.sage_attn_fwd_noalloc(ctypes.byref(d), f, f, f, f, None, None)] \
+        == "SAGE_ERR_HEAD_DIM"
