@@ -71,6 +71,11 @@ def _parse():
     ap.add_argument("--no-second", action="store_true",
                     help="skip the N=32K point (varlen_d128) that the default workload adds")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows per query head")
+    ap.add_argument("--no-micro", action="store_true",
+                    help="skip the measured INT8/FP8 matrix peak beside the published one")
+    ap.add_argument("--micro", action="store_true",
+                    help="only print the measured rates of the INT8 and FP8 matrix "
+                         "instructions, v_exp_f32 and v_fma_f32, then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the reference "
                          "kernel for scaling the HBM byte counters), then exit")
@@ -269,6 +274,19 @@ def measure(w, args, dev):
     return (q, k, v), res
 
 
+def micro_rates(ops, reps=16384):
+    """Measured rates of the matrix instructions (TOPS) and of v_exp_f32 (G
+    results/s) and v_fma_f32 (TFLOP/s), one timed launch each."""
+    import quantized_attention_03_amd as qa
+    unit = {"i8": ("TOPS", 1e12), "f8": ("TFLOP/s", 1e12), "exp": ("Gexp/s", 1e9),
+            "fma": ("TFLOP/s", 1e12)}
+    out = {}
+    for op in ops:
+        u, sc = unit[op]
+        out[op] = {"rate": round(qa.sage_micro_rate(op, reps) / sc, 1), "unit": u}
+    return out
+
+
 def roofline(w, args, r):
     """The fused kernel against its roofline, from the timings of measure()."""
     half = args.pv == "half"
@@ -317,6 +335,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.micro:
+        print(json.dumps(micro_rates(("i8", "f8", "exp", "fma"))), flush=True)
         return
 
     import synth
@@ -381,6 +402,14 @@ def main():
             "unit": "TOPS", "ms_per_step": round(r2["ms"], 4),
             "prepass_ms": round(r2["prepass_ms"], 4), "kernel_ms": round(r2["kernel_ms"], 4),
             "frac": rl2["frac"], "achieved": rl2["achieved"]}
+    rl = line["roofline"]
+    if not args.no_micro and rl["bound"] == "mfma" and not half:
+        # half the ops run on each instruction, so their times add
+        m = micro_rates(("i8", "f8"))
+        mix = 1.0 / (0.5 / m["i8"]["rate"] + 0.5 / m["f8"]["rate"])
+        rl["peak_measured"] = {"i8": m["i8"]["rate"], "f8": m["f8"]["rate"],
+                               "mix": round(mix, 1), "unit": "TOPS"}
+        rl["frac_of_measured"] = round(rl["achieved"] / mix, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, args.pv, r["split"],
                                             args.qk_block)

@@ -338,6 +338,22 @@ SAGE_API sage_status sage_debug_qk_int32(const sage_attn_desc* desc, const int32
 SAGE_API sage_status sage_debug_e4m3_encode(uint32_t first, uint32_t count, uint8_t* out,
                                             void* stream);
 
+/*
+ * sage_micro_rate -- measured throughput of one execution unit the fused
+ * kernel depends on, to set beside the part's published peak: the dense INT8
+ * matrix instruction of Q.K^T (v_mfma_i32_32x32x32_i8) and the FP8 one of P.V
+ * (v_mfma_scale_f32_32x32x64_f8f6f4), in operations (2 per multiply-add) per
+ * second; v_exp_f32 in results per second; v_fma_f32 in flops per second.
+ * One launch of independent dependency chains over 4 workgroups of 512
+ * threads per compute unit, `reps` iterations each (1 .. 2^20; 4096 takes
+ * about 2 ms for the matrix operations), timed with events on `stream` after
+ * a warm-up launch.  Blocks until the launches end.  Errors: SAGE_ERR_NULL
+ * (rate), SAGE_ERR_FLAGS (op), SAGE_ERR_SHAPE (reps), SAGE_ERR_ARCH,
+ * SAGE_ERR_HIP.  Source: ComfyUI blog feature item 2 (INT8 Q.K^T, FP8 P.V).
+ */
+typedef enum { SAGE_MICRO_I8 = 0, SAGE_MICRO_F8 = 1, SAGE_MICRO_EXP = 2, SAGE_MICRO_FMA = 3 } sage_micro_op;
+SAGE_API sage_status sage_micro_rate(int32_t op, int32_t reps, double* rate, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 SAGE_API const char* sage_status_string(sage_status status);
 

@@ -281,6 +281,21 @@ def sage_debug_e4m3_encode(first: int, count: int, out=None, device="cuda"):
     return out[:count]
 
 
+def sage_micro_rate(op: str, reps: int = 4096, device="cuda") -> float:
+    """Measured rate of one execution unit on `device`: "i8" and "f8" matrix
+    operations (2 per multiply-add) per second, "exp" results per second,
+    "fma" flops per second (one timed launch after a warm-up; blocks)."""
+    if op not in _abi.MICRO_OPS:
+        raise ValueError(f"op must be one of {sorted(_abi.MICRO_OPS)}")
+    dev = torch.device(device)
+    rate = ctypes.c_double(0.0)
+    with torch.cuda.device(dev):
+        st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        _abi.check("sage_micro_rate",
+                   lib().sage_micro_rate(_abi.MICRO_OPS[op], int(reps), ctypes.byref(rate), st))
+    return rate.value
+
+
 def sage_attn_fwd(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,
                   smooth_k=True, smooth_v=False, sm_scale=None, return_lse=False,
                   out=None, workspace=None, pv_mode="fp8", kv_split=0, qk_block=64):

@@ -26,7 +26,8 @@ EXPORTS = ["sage_desc_init", "sage_quant_buf_sizes", "sage_workspace_size", "sag
            "sage_attn_fwd", "sage_attn_fwd_varlen", "sage_attn_fwd_quantized",
            "sage_attn_fwd_noalloc",
            "sage_debug_qk_int32", "sage_debug_e4m3_encode", "sage_kv_split_size",
-           "sage_status_string", "sage_abi_version"]
+           "sage_micro_rate", "sage_status_string", "sage_abi_version"]
+MICRO_OPS = {"i8": 0, "f8": 1, "exp": 2, "fma": 3}   # sage_micro_op
 
 
 class Desc(ctypes.Structure):
@@ -88,6 +89,7 @@ def lib():
         "sage_kv_split_size": (I32, [D, ip, ip, I32, ip]),
         "sage_debug_qk_int32": (I32, [D, ip, ip, I32, ctypes.POINTER(QuantBufs), P, P]),
         "sage_debug_e4m3_encode": (I32, [ctypes.c_uint32, ctypes.c_uint32, P, P]),
+        "sage_micro_rate": (I32, [I32, I32, ctypes.POINTER(ctypes.c_double), P]),
         "sage_status_string": (ctypes.c_char_p, [I32]),
         "sage_abi_version": (I32, []),
     }

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsage.so")
-SOURCES = ["sage_api.cpp", "sage_prepass.hip", "sage_attn.hip"]
+SOURCES = ["sage_api.cpp", "sage_prepass.hip", "sage_attn.hip", "sage_micro.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -698,6 +698,16 @@ sage_status sage_debug_e4m3_encode(uint32_t first, uint32_t count, uint8_t* out,
     return SAGE_OK;
 }
 
+sage_status sage_micro_rate(int32_t op, int32_t reps, double* rate, void* stream) {
+    if (!rate) return SAGE_ERR_NULL;
+    if (op < SAGE_MICRO_I8 || op > SAGE_MICRO_FMA) return SAGE_ERR_FLAGS;
+    if (reps < 1 || reps > (1 << 20)) return SAGE_ERR_SHAPE;
+    sage_status e = check_arch();
+    if (e != SAGE_OK) return e;
+    SAGE_TRY(micro_rate(op, reps, rate, static_cast<hipStream_t>(stream)));
+    return SAGE_OK;
+}
+
 const char* sage_status_string(sage_status s) {
     switch (s) {
         case SAGE_OK: return "ok";

@@ -222,4 +222,9 @@ hipError_t noalloc_workspace(void** ptr);
 // export of the conversion).
 hipError_t launch_e4m3_dump(uint32_t first, uint32_t count, uint8_t* out, hipStream_t st);
 
+// Micro-benchmark rates (sage_micro.hip): the operation and its units per
+// second, one timed launch over NUM_CU x 4 workgroups after a warm-up launch.
+enum MicroOp { MICRO_I8 = 0, MICRO_F8 = 1, MICRO_EXP = 2, MICRO_FMA = 3 };
+hipError_t micro_rate(int op, int reps, double* per_s, hipStream_t st);
+
 }  // namespace sage

@@ -24,7 +24,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     L = qa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -260,6 +260,20 @@ def test_e4m3_export_argument_errors():
                                          None)) == "SAGE_ERR_ALIGN"
     assert name(L.sage_debug_e4m3_encode(u32(0xFFFFFFF0), u32(32), ctypes.c_void_p(FAKE),
                                          None)) == "SAGE_ERR_SHAPE"
+
+
+def test_micro_rate_argument_errors():
+    # each case fails before any HIP call
+    L = qa.lib()
+    name = lambda st: _abi.STATUS_NAMES[st]
+    r = ctypes.c_double(0.0)
+    assert name(L.sage_micro_rate(0, 16, None, None)) == "SAGE_ERR_NULL"
+    assert name(L.sage_micro_rate(4, 16, ctypes.byref(r), None)) == "SAGE_ERR_FLAGS"
+    assert name(L.sage_micro_rate(-1, 16, ctypes.byref(r), None)) == "SAGE_ERR_FLAGS"
+    assert name(L.sage_micro_rate(0, 0, ctypes.byref(r), None)) == "SAGE_ERR_SHAPE"
+    assert name(L.sage_micro_rate(1, (1 << 20) + 1, ctypes.byref(r), None)) == "SAGE_ERR_SHAPE"
+    with pytest.raises(ValueError):
+        qa.sage_micro_rate("bf16")
 
 
 def test_noalloc_refuses_large_workspace_before_any_gpu_call():
