@@ -65,6 +65,10 @@ def lib():
         "orc_quant_int8_blocks": (None, [P, i64, i32, i32, P, P]),
         "orc_quant_fp8_channels": (None, [P, i64, i32, P, P]),
         "orc_delta_s": (None, [P, P, i64, i32, P]),
+        "orc_block_mean": (None, [P, i64, i32, i32, P]),
+        "orc_smooth_blocks": (None, [P, P, i64, i32, i32, P]),
+        "orc_mu_code": (None, [P, i32, P, P, P]),
+        "orc_delta_s_block": (None, [P, P, P, f32, P, P, i64, i32, i32, P]),
         "orc_qk_int32": (None, [P, P, i64, i64, i32, P]),
         "orc_attn_recipe_rows": (None, [P, P, P, P, P, P, P, P, i64, i64, i32, f32,
                                         i32, i32, i32, i64, P, i64, P, P, P]),
@@ -163,6 +167,45 @@ def delta_s(mu_q, ks) -> np.ndarray:
     return out
 
 
+def block_mean(x, blk: int = BLK) -> np.ndarray:
+    """Channel means of each `blk`-token block (sage_oracle.c, orc_block_mean)."""
+    x = _c(x, np.float32)
+    n, d = x.shape
+    nb = -(-n // blk)
+    mu = np.empty((max(1, nb), d), np.float32)
+    lib().orc_block_mean(_p(x), n, d, blk, _p(mu))
+    return mu[:nb]
+
+
+def smooth_blocks(x, mu, blk: int = BLK) -> np.ndarray:
+    x = _c(x, np.float32)
+    n, d = x.shape
+    out = np.empty_like(x)
+    lib().orc_smooth_blocks(_p(x), _p(_c(mu, np.float32)), n, d, blk, _p(out))
+    return out
+
+
+def mu_code(x):
+    """(hi, lo, scale) of one block-mean deviation vector (orc_mu_code)."""
+    x = _c(x, np.float32)
+    d = x.shape[0]
+    hi, lo = np.empty(d, np.int8), np.empty(d, np.int8)
+    sc = np.empty(1, np.float32)
+    lib().orc_mu_code(_p(x), d, _p(hi), _p(lo), _p(sc))
+    return hi, lo, np.float32(sc[0])
+
+
+def delta_s_block(ds_seq, hi, lo, scale, kc, ks, blk: int = BLK) -> np.ndarray:
+    """Score compensation of one Q block (orc_delta_s_block)."""
+    kc = _c(kc, np.int8)
+    n, d = kc.shape
+    out = np.empty(max(1, n), np.float32)
+    lib().orc_delta_s_block(_p(None if ds_seq is None else _c(ds_seq, np.float32)),
+                            _p(_c(hi, np.int8)), _p(_c(lo, np.int8)), float(scale), _p(kc),
+                            _p(_c(ks, np.float32)), n, d, blk, _p(out))
+    return out[:n]
+
+
 def qk_int32(qc, kc) -> np.ndarray:
     qc, kc = _c(qc, np.int8), _c(kc, np.int8)
     nq, d = qc.shape
@@ -237,7 +280,7 @@ class Problem:
     seqs: list                  # [(nq, nkv)] per sequence (B entries)
     varlen: bool = False
     causal: bool = False
-    smooth_q: bool = False
+    smooth_q: bool | str = False   # False, True (one mean per sequence) or "block"
     smooth_k: bool = True
     smooth_v: bool = False
     sm_scale: float | None = None
@@ -289,6 +332,7 @@ def merge_heads(prob: Problem, per_seq):
 class Prepass:
     """Logical pre-pass results per sequence s (lists indexed by s)."""
     mu_q: list = field(default_factory=list)     # [Hq, d] FP32 or None
+    mu_qb: list = field(default_factory=list)    # smooth_q "block": [Hq, nqb, d] FP32
     mu_k: list = field(default_factory=list)     # [Hkv, d] FP32 or None
     mu_v: list = field(default_factory=list)     # [Hkv, d] FP32 or None
     qc: list = field(default_factory=list)       # [Hq, nq, d] int8
@@ -298,7 +342,10 @@ class Prepass:
     vc: list = field(default_factory=list)       # [Hkv, nkv, d] e4m3 bytes, or
                                                  # 16-bit patterns (pv_mode "half")
     vs: list = field(default_factory=list)       # [Hkv, d] FP32 (None for "half")
-    ds: list = field(default_factory=list)       # [Hq, nkv] FP32 or None
+    ds: list = field(default_factory=list)       # [Hq, nkv] FP32 or None; with
+                                                 # smooth_q "block": [Hq, nqb, nkv]
+    mu_code: list = field(default_factory=list)  # "block": [Hq, nqb, 2, d] int8 (hi, lo)
+    mu_cscale: list = field(default_factory=list)  # "block": [Hq, nqb] FP32
 
 
 def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
@@ -322,17 +369,33 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
             vc, vs = quant_fp8_channels(smooth(vf, mu_v))
         return mu_k, mu_v, k_s, kc, ks, vc, vs
 
-    def q_unit(u, k_s):
+    blockwise = prob.smooth_q == "block"
+
+    def q_unit(u, kvu):
         s, h = u
         qf = decode16(qh[s][h], prob.dtype)
+        if blockwise:
+            # one mean per quantization block: the sequence mean's compensation
+            # from the unquantized K_s, plus each block's deviation from it
+            # through its code and the INT8 key codes
+            mu_bar = channel_mean(qf)
+            ds_seq = delta_s(mu_bar, kvu[2])
+            mu_b = block_mean(qf, prob.qk_block)
+            qc, qs = quant_int8_blocks(smooth_blocks(qf, mu_b, prob.qk_block), prob.qk_block)
+            codes = [mu_code(m - mu_bar) for m in mu_b]      # FP32 difference per channel
+            ds = np.stack([delta_s_block(ds_seq, hi, lo, sc, kvu[3], kvu[4], prob.qk_block)
+                           for hi, lo, sc in codes])
+            code = np.stack([np.stack([hi, lo]) for hi, lo, _ in codes])
+            csc = np.array([sc for _, _, sc in codes], np.float32)
+            return (mu_bar, mu_b), qc, qs, ds, code, csc
         mu_q = channel_mean(qf) if prob.smooth_q else None
         qc, qs = quant_int8_blocks(smooth(qf, mu_q), prob.qk_block)
-        ds = delta_s(mu_q, k_s) if prob.smooth_q else None
-        return mu_q, qc, qs, ds
+        ds = delta_s(mu_q, kvu[2]) if prob.smooth_q else None
+        return mu_q, qc, qs, ds, None, None
 
     with ThreadPoolExecutor(max_workers=threads or os.cpu_count()) as ex:
         kv = list(ex.map(kv_unit, [(s, h) for s in range(S) for h in range(prob.Hkv)]))
-        qq = list(ex.map(lambda u: q_unit(u, kv[u[0] * prob.Hkv + u[1] // G][2]),
+        qq = list(ex.map(lambda u: q_unit(u, kv[u[0] * prob.Hkv + u[1] // G]),
                          [(s, h) for s in range(S) for h in range(prob.Hq)]))
     R = Prepass()
     for s in range(S):
@@ -344,10 +407,17 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
         R.ks.append(np.stack([x[4] for x in ks_]))
         R.vc.append(np.stack([x[5] for x in ks_]))
         R.vs.append(np.stack([x[6] for x in ks_]) if prob.pv_mode != "half" else None)
-        R.mu_q.append(np.stack([x[0] for x in qs_]) if prob.smooth_q else None)
+        if blockwise:
+            R.mu_q.append(np.stack([x[0][0] for x in qs_]))
+            R.mu_qb.append(np.stack([x[0][1] for x in qs_]))
+        else:
+            R.mu_q.append(np.stack([x[0] for x in qs_]) if prob.smooth_q else None)
+            R.mu_qb.append(None)
         R.qc.append(np.stack([x[1] for x in qs_]))
         R.qs.append(np.stack([x[2] for x in qs_]))
         R.ds.append(np.stack([x[3] for x in qs_]) if prob.smooth_q else None)
+        R.mu_code.append(np.stack([x[4] for x in qs_]) if blockwise else None)
+        R.mu_cscale.append(np.stack([x[5] for x in qs_]) if blockwise else None)
     return R
 
 
@@ -366,8 +436,24 @@ def forward_rows(prob: Problem, pre: Prepass, rows=None, bkv: int = 128,
         s, h = u
         nq = prob.seqs[s][0]
         r = np.arange(nq) if rows is None else np.asarray(rows[s])
+        if prob.smooth_q == "block":
+            # each query block has its own compensation: its rows in one call each
+            blocks = r // prob.qk_block
+            parts = {b: one_rows(s, h, r[blocks == b], pre.ds[s][h][b]) for b in np.unique(blocks)}
+            d = prob.d
+            out = np.empty((len(r), d), np.float32)
+            lse = np.empty(len(r), np.float32)
+            tb = np.empty((len(r), d), np.float32) if tie else None
+            for b, res in parts.items():
+                sel = blocks == b
+                out[sel], lse[sel] = res[0], res[1]
+                if tie:
+                    tb[sel] = res[2]
+            return (out, lse, tb) if tie else (out, lse)
+        return one_rows(s, h, r, None if pre.ds[s] is None else pre.ds[s][h])
+
+    def one_rows(s, h, r, ds):
         hk = h // G
-        ds = None if pre.ds[s] is None else pre.ds[s][h]
         mu_v = None if pre.mu_v[s] is None else pre.mu_v[s][hk]
         if prob.pv_mode == "half":
             return attn_recipe_half_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk],

@@ -257,6 +257,88 @@ ORC_EXPORT void orc_delta_s(const float* mu_q, const float* ks, int64_t n_kv, in
 }
 
 /* ------------------------------------------------------------------------ */
+/* Per-block Q smoothing ([SA2] "Main concepts" item 2 subtracts the channel */
+/* mean of Q; the pages fix neither the span of the mean nor how the score   */
+/* compensation is formed -- the choices below are readings).               */
+/* ------------------------------------------------------------------------ */
+
+/* Channel means of each quantization block of Q: blocks of `blk` tokens
+   aligned to the sequence start (the last one may be short).  Per block and
+   channel, the block's tokens are summed in order in FP32 and the sum is
+   divided by the block's token count with one correctly rounded FP32
+   division.  x [n][d]; mu [ceil(n/blk)][d].                                 */
+ORC_EXPORT void orc_block_mean(const float* x, int64_t n, int d, int blk, float* mu) {
+    for (int64_t b0 = 0, bi = 0; b0 < n; b0 += blk, ++bi) {
+        int64_t b1 = b0 + blk < n ? b0 + blk : n;
+        for (int c = 0; c < d; ++c) {
+            float sum = 0.0f;
+            for (int64_t t = b0; t < b1; ++t) sum = sum + x[t * d + c];
+            mu[bi * d + c] = sum / (float)(b1 - b0);
+        }
+    }
+}
+
+/* x_s = fl32(x - mu_b) with mu_b the mean of the token's own block. */
+ORC_EXPORT void orc_smooth_blocks(const float* x, const float* mu, int64_t n, int d, int blk,
+                                  float* xs) {
+    for (int64_t t = 0; t < n; ++t)
+        for (int c = 0; c < d; ++c) xs[t * d + c] = x[t * d + c] - mu[(t / blk) * d + c];
+}
+
+/* A block mean's deviation from the sequence mean as an integer code of 15
+   bits with one FP32 scale, so that the block's share of the score
+   compensation is an integer product with the INT8 key codes: for the
+   vector x (x = fl32(mu_b - mu_q) per channel), a = max_c |x_c|; a == 0
+   gives scale 0 and zero codes; otherwise inv = fl32(16256/a),
+   scale = fl32(a/16256) (16256 = 127*128), and per channel y = fl32(x_c*inv),
+   hi = clamp(rne(y/128), -127, 127), lo = rne(y - 128*hi) (|lo| <= 64), so
+   that x_c ~ scale*(128*hi + lo) within scale/2.  hi, lo: [d] int8.        */
+ORC_EXPORT void orc_mu_code(const float* x, int d, int8_t* hi, int8_t* lo, float* scale) {
+    float a = 0.0f;
+    for (int c = 0; c < d; ++c) {
+        float v = fabsf(x[c]);
+        if (v > a) a = v;
+    }
+    if (a == 0.0f) {
+        *scale = 0.0f;
+        for (int c = 0; c < d; ++c) hi[c] = lo[c] = 0;
+        return;
+    }
+    float inv = 16256.0f / a;
+    *scale = a / 16256.0f;
+    for (int c = 0; c < d; ++c) {
+        float y = x[c] * inv;
+        float h = nearbyintf(y / 128.0f);                  /* exact scaling */
+        if (h > 127.0f) h = 127.0f;
+        if (h < -127.0f) h = -127.0f;
+        float l = nearbyintf(y - 128.0f * h);              /* exact difference */
+        hi[c] = (int8_t)h;
+        lo[c] = (int8_t)l;
+    }
+}
+
+/* The score compensation of one Q block smoothed by its own mean mu_b.
+   Subtracting mu_b from the block's queries changes each score q_i.k_j by
+   mu_b.k_j = mu_q.k_j + (mu_b - mu_q).k_j.  The first term is the sequence's
+   compensation ds_seq_j (orc_delta_s, from the unquantized K_s); the block's
+   deviation is added from its code and the same INT8 key codes the scores
+   use: ds_j = fl32(ds_seq_j + fl32(fl32(T_j) * fl32(scale * k_scale[j/blk])))
+   with the exact integer T_j = sum_c (128*hi_c + lo_c) * kc[j][c].
+   ds_seq [nkv] (NULL: 0); kc [nkv][d]; k_scale per `blk` keys; ds [nkv].    */
+ORC_EXPORT void orc_delta_s_block(const float* ds_seq, const int8_t* hi, const int8_t* lo,
+                                  float scale, const int8_t* kc, const float* k_scale,
+                                  int64_t nkv, int d, int blk, float* ds) {
+    for (int64_t j = 0; j < nkv; ++j) {
+        int64_t T = 0;
+        for (int c = 0; c < d; ++c)
+            T += (128 * (int64_t)hi[c] + (int64_t)lo[c]) * (int64_t)kc[j * d + c];
+        float f = scale * k_scale[j / blk];
+        float corr = (float)T * f;
+        ds[j] = ds_seq ? ds_seq[j] + corr : corr;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Attention                                                                 */
 /* ------------------------------------------------------------------------ */
 

@@ -113,7 +113,7 @@ class Workload:
     Nkv: int
     d: int
     causal: bool = False
-    smooth_q: bool = False
+    smooth_q: bool | str = False    # False, True (one mean per sequence) or "block"
     smooth_k: bool = True
     smooth_v: bool = False
     sm_scale: float | None = None
@@ -123,6 +123,8 @@ class Workload:
     q_outlier_mult: float = 1.0
     qv_mean_sigma: float = 0.0      # per-channel mean of Q and V ~ N(0, sigma^2)
     qv_outlier_mult: float = 1.0    # 1 outlier channel of Q and V per head
+    q_drift_sigma: float = 0.0      # Q offset drifting along the tokens: per (b,h,c)
+                                    # A + (2t/(N-1) - 1) * B with A, B ~ N(0, sigma^2)
     seqlens_q: list = field(default_factory=list)   # varlen only
     seqlens_kv: list = field(default_factory=list)
 
@@ -181,6 +183,11 @@ WORKLOADS = {
                            causal=True, seed=4, k_off_sigma=3.0,
                            seqlens_q=[a for a, _ in C5_LENS],
                            seqlens_kv=[b for _, b in C5_LENS]),
+    # video DiT with a Q offset that drifts along the sequence, smoothed per
+    # 64-token query block
+    "video_dit_block": Workload("video_dit_block", "bf16", "NHD", 1, 48, 48, 17776, 17776, 64,
+                                smooth_q="block", smooth_v=True, seed=6, qv_mean_sigma=1.5,
+                                qv_outlier_mult=10.0, q_drift_sigma=3.0),
     # one new query per sequence against a 32K-token context (decode)
     "decode_gqa": Workload("decode_gqa", "f16", "HND", 8, 32, 8, 1, 32768, 128,
                            causal=True, seed=5, k_off_sigma=3.0),
@@ -188,6 +195,7 @@ WORKLOADS = {
 
 # tensor ids inside one seed
 TID_Q, TID_K, TID_V, TID_KOFF, TID_QOUT, TID_QMEAN, TID_VMEAN, TID_QVOUT = range(8)
+TID_QDRIFT_A, TID_QDRIFT_B = 8, 9
 
 
 def _lens(w: Workload):
@@ -252,6 +260,19 @@ def make_inputs(w: Workload, device="cpu"):
     if w.qv_mean_sigma:
         q = add_per_channel(q, w.qv_mean_sigma * per_seq_head(TID_QMEAN, w.Hq), segq)
         v = add_per_channel(v, w.qv_mean_sigma * per_seq_head(TID_VMEAN, w.Hkv), segk)
+    if w.q_drift_sigma:
+        a = w.q_drift_sigma * per_seq_head(TID_QDRIFT_A, w.Hq)
+        b = w.q_drift_sigma * per_seq_head(TID_QDRIFT_B, w.Hq)
+        if segq is None:
+            n = lq[0]
+            ramp = (2.0 * torch.arange(n, dtype=torch.float64, device=device) / max(1, n - 1)
+                    - 1.0)
+            q = q + a[:, :, None, :] + ramp[None, None, :, None] * b[:, :, None, :]
+        else:
+            for s_, t0, n in segq:
+                ramp = (2.0 * torch.arange(n, dtype=torch.float64, device=device) /
+                        max(1, n - 1) - 1.0)
+                q[:, t0:t0 + n, :] += a[s_][:, None, :] + ramp[None, :, None] * b[s_][:, None, :]
     if w.qv_outlier_mult != 1.0:
         chq = choose_channels(w.seed, TID_QVOUT, S * w.Hq, d, 1, device)
         q = scale_channels(q, chq, w.qv_outlier_mult, w.Hq, segq)
