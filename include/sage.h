@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 2
+#define SAGE_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SAGE_API __attribute__((visibility("default")))
@@ -135,6 +135,17 @@ typedef enum { SAGE_PV_FP8 = 0, SAGE_PV_HALF = 1 } sage_pv_mode;
  * head_dim], HND = [heads, tokens, head_dim]. */
 typedef enum { SAGE_HND = 0, SAGE_NHD = 1 } sage_layout;
 
+/* smooth_q = SAGE_SMOOTH_Q_BLOCK: each Q quantization block is smoothed by
+ * its own channel mean mu_b (SageAttention2 summary, "Main concepts" item 2:
+ * Q is smoothed by subtracting its channel mean before quantization; here the
+ * mean is taken per block).  The scores then owe mu_b.k_j: the sequence
+ * mean's share mu_q.k_j is the score bias delta_s (as with smooth_q = 1), and
+ * the block's deviation (mu_b - mu_q).k_j is formed inside the fused kernel
+ * from a 15-bit code of the deviation and the INT8 key codes.  Requires
+ * SAGE_PV_FP8 (SAGE_ERR_FLAGS otherwise); a split key range then always uses
+ * the fused kernel (never the one-wave decode kernel). */
+#define SAGE_SMOOTH_Q_BLOCK 2
+
 /* Problem descriptor.  Strides are in elements for (batch, head, token); the
  * head_dim stride is 1.  A stride triple of all zeros means "contiguous in
  * `layout`" (the dense shapes above; for varlen calls the packed shapes, where
@@ -151,7 +162,9 @@ typedef struct {
     int64_t v_stride[3];
     int64_t o_stride[3];
     int32_t is_causal;       /* 0/1, bottom-right aligned                         */
-    int32_t smooth_q;        /* 0/1 (SA2-style Q smoothing, with score bias)     */
+    int32_t smooth_q;        /* 0/1 (SA2-style Q smoothing, with score bias), or
+                                SAGE_SMOOTH_Q_BLOCK (one Q mean per quantization
+                                block; FP8 P.V only)                             */
     int32_t smooth_k;        /* 0/1 (default 1)                                   */
     int32_t smooth_v;        /* 0/1 (SA2-style V smoothing, mean added back)     */
     float sm_scale;          /* <= 0 selects 1/sqrt(head_dim)                     */
@@ -173,7 +186,8 @@ SAGE_API void sage_desc_init(sage_attn_desc* desc, int32_t dtype, int32_t layout
  * Sequences are s = 0..S-1 (S = batch for dense calls).  Per sequence,
  * npq_s = nq_s rounded up to SAGE_QK_BLOCK and npk_s = nkv_s rounded up to
  * SAGE_KV_TILE; row bases rq_s = sum_{s'<s} npq_s' and rk_s = sum npk_s'.
- *   mu_q    [S][hq][d]  FP32, only if smooth_q (may be NULL otherwise)
+ *   mu_q    [S][hq][d]  FP32, only if smooth_q (the sequence mean; may be
+ *           NULL otherwise)
  *   mu_k    [S][hkv][d] FP32, only if smooth_k
  *   mu_v    [S][hkv][d] FP32, only if smooth_v
  *   q_codes int8: element (s,h,n,c) at ((rq_s*hq + h*npq_s + n)*d + c);
@@ -188,6 +202,16 @@ SAGE_API void sage_desc_init(sage_attn_desc* desc, int32_t dtype, int32_t layout
  *           input's type (v, or v - mu_v rounded into that type)
  *   v_scale FP32 [S][hkv][d] (unused with SAGE_PV_HALF: size 0, may be NULL)
  *   delta_s FP32: (s,h,n) at rk_s*hq + h*npk_s + n, only if smooth_q
+ * With smooth_q = SAGE_SMOOTH_Q_BLOCK also, per (s,h,blk) at index
+ * ib = (rq_s*hq + h*npq_s)/QB + blk (the index of q_scale; blocks without a
+ * valid token hold zeros):
+ *   mu_qb       FP32 [ib][d]: the block's channel mean (its valid tokens
+ *               summed in order in FP32, divided by their count); q_codes
+ *               are then of q - mu_qb
+ *   mu_q_code   int8 [ib][2][d]: hi, lo of x = fl32(mu_qb - mu_q): with
+ *               a = max |x|, y = x * fl32(16256/a), hi = clamp(rne(y/128),
+ *               +-127), lo = rne(y - 128*hi)
+ *   mu_q_cscale FP32 [ib]: fl32(a/16256) (0 when a = 0)
  * All pointers 16-byte aligned.
  */
 typedef struct {
@@ -201,11 +225,15 @@ typedef struct {
     uint8_t* v_codes;
     float* v_scale;
     float* delta_s;
+    float* mu_qb;
+    int8_t* mu_q_code;
+    float* mu_q_cscale;
 } sage_quant_bufs;
 
 /* Byte sizes of each sage_quant_bufs member for a problem (0 when unused). */
 typedef struct {
     size_t mu_q, mu_k, mu_v, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, delta_s;
+    size_t mu_qb, mu_q_code, mu_q_cscale;
 } sage_quant_sizes;
 
 /* Sizes for a dense call (cu_seqlens_* NULL, nseq ignored) or a varlen call

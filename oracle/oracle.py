@@ -344,6 +344,8 @@ class Prepass:
     vs: list = field(default_factory=list)       # [Hkv, d] FP32 (None for "half")
     ds: list = field(default_factory=list)       # [Hq, nkv] FP32 or None; with
                                                  # smooth_q "block": [Hq, nqb, nkv]
+    ds_seq: list = field(default_factory=list)   # "block": [Hq, nkv] FP32, the sequence
+                                                 # mean's share of ds
     mu_code: list = field(default_factory=list)  # "block": [Hq, nqb, 2, d] int8 (hi, lo)
     mu_cscale: list = field(default_factory=list)  # "block": [Hq, nqb] FP32
 
@@ -383,11 +385,13 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
             mu_b = block_mean(qf, prob.qk_block)
             qc, qs = quant_int8_blocks(smooth_blocks(qf, mu_b, prob.qk_block), prob.qk_block)
             codes = [mu_code(m - mu_bar) for m in mu_b]      # FP32 difference per channel
+            nkv = kvu[3].shape[0]
             ds = np.stack([delta_s_block(ds_seq, hi, lo, sc, kvu[3], kvu[4], prob.qk_block)
-                           for hi, lo, sc in codes])
-            code = np.stack([np.stack([hi, lo]) for hi, lo, _ in codes])
+                           for hi, lo, sc in codes]) if codes else np.zeros((0, nkv), np.float32)
+            code = (np.stack([np.stack([hi, lo]) for hi, lo, _ in codes]) if codes
+                    else np.zeros((0, 2, prob.d), np.int8))
             csc = np.array([sc for _, _, sc in codes], np.float32)
-            return (mu_bar, mu_b), qc, qs, ds, code, csc
+            return (mu_bar, mu_b, ds_seq), qc, qs, ds, code, csc
         mu_q = channel_mean(qf) if prob.smooth_q else None
         qc, qs = quant_int8_blocks(smooth(qf, mu_q), prob.qk_block)
         ds = delta_s(mu_q, kvu[2]) if prob.smooth_q else None
@@ -410,9 +414,11 @@ def prepass(prob: Problem, q, k, v, threads: int | None = None) -> Prepass:
         if blockwise:
             R.mu_q.append(np.stack([x[0][0] for x in qs_]))
             R.mu_qb.append(np.stack([x[0][1] for x in qs_]))
+            R.ds_seq.append(np.stack([x[0][2] for x in qs_]))
         else:
             R.mu_q.append(np.stack([x[0] for x in qs_]) if prob.smooth_q else None)
             R.mu_qb.append(None)
+            R.ds_seq.append(None)
         R.qc.append(np.stack([x[1] for x in qs_]))
         R.qs.append(np.stack([x[2] for x in qs_]))
         R.ds.append(np.stack([x[3] for x in qs_]) if prob.smooth_q else None)

@@ -118,7 +118,12 @@ def make_desc(q, k, v, o=None, *, tensor_layout="HND", is_causal=False, smooth_q
         for i, x in enumerate(_strides(t, tensor_layout, varlen)):
             arr[i] = x
     d.is_causal = int(bool(is_causal))
-    d.smooth_q = int(bool(smooth_q))
+    if smooth_q == "block":
+        d.smooth_q = _abi.SMOOTH_Q_BLOCK
+    elif smooth_q in (False, True, 0, 1, None):
+        d.smooth_q = int(bool(smooth_q))
+    else:
+        raise ValueError(f"smooth_q must be False, True or 'block', got {smooth_q!r}")
     d.smooth_k = int(bool(smooth_k))
     d.smooth_v = int(bool(smooth_v))
     d.sm_scale = float(sm_scale) if sm_scale else 0.0
@@ -176,7 +181,8 @@ def quant_buf_sizes(desc, cu_seqlens_q=None, cu_seqlens_kv=None) -> dict:
 _BUF_DT = {"mu_q": torch.float32, "mu_k": torch.float32, "mu_v": torch.float32,
            "q_codes": torch.int8, "q_scale": torch.float32, "k_codes": torch.int8,
            "k_scale": torch.float32, "v_codes": torch.uint8, "v_scale": torch.float32,
-           "delta_s": torch.float32}
+           "delta_s": torch.float32, "mu_qb": torch.float32, "mu_q_code": torch.int8,
+           "mu_q_cscale": torch.float32}
 
 
 def sage_quant_qkv(q, k, v, *, tensor_layout="HND", is_causal=False, smooth_q=False,

@@ -45,7 +45,9 @@ class Desc(ctypes.Structure):
 
 
 _BUF_FIELDS = ["mu_q", "mu_k", "mu_v", "q_codes", "q_scale", "k_codes", "k_scale", "v_codes",
-               "v_scale", "delta_s"]
+               "v_scale", "delta_s", "mu_qb", "mu_q_code", "mu_q_cscale"]
+ABI_VERSION = 3
+SMOOTH_Q_BLOCK = 2           # SAGE_SMOOTH_Q_BLOCK
 
 
 class QuantBufs(ctypes.Structure):
@@ -96,6 +98,10 @@ def lib():
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
         fn.restype, fn.argtypes = res, args
+    if L.sage_abi_version() != ABI_VERSION:
+        raise LibraryMissing(
+            f"{LIB_PATH} has ABI version {L.sage_abi_version()}, the binding expects "
+            f"{ABI_VERSION}: rebuild it with `python -m quantized_attention_03_amd.build`")
     _lib = L
     return L
 

@@ -30,6 +30,7 @@ struct Plan {
     Strides qs{}, ks{}, vs{}, os{};
     float sm_scale = 0.0f;
     bool causal = false, smooth_q = false, smooth_k = false, smooth_v = false;
+    bool smooth_q_blk = false;        // one Q mean per quantization block (smooth_q = 2)
     bool pv_half = false;             // 16-bit P.V operands (SAGE_PV_HALF)
     int32_t kv_split_req = 0;         // descriptor's kv_split (-1 auto, 0 none, keys)
     int32_t kv_split = 0;             // effective keys per split (0: no split)
@@ -44,6 +45,7 @@ struct Plan {
 // sage_quant_qkv (whose quantized tensors are caller buffers).
 struct WsLayout {
     size_t mu_q, mu_k, mu_v, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, delta_s;
+    size_t mu_qb, mu_q_code, mu_q_cscale;
     size_t part_q, part_k, part_v, part_vmax, v_amax;
     size_t split_o, split_ml;         // partials of a split key range
     size_t total;
@@ -69,6 +71,10 @@ sage_quant_sizes quant_sizes(const Plan& p) {
     z.v_codes = (size_t)p.rows_k * p.hkv * d * (p.pv_half ? 2 : 1);
     z.v_scale = p.pv_half ? 0 : S * p.hkv * d * 4;
     z.delta_s = p.smooth_q ? (size_t)p.rows_k * p.hq * 4 : 0;
+    const size_t nqb = p.smooth_q_blk ? (size_t)p.rows_q * p.hq / p.qb : 0;
+    z.mu_qb = nqb * d * 4;
+    z.mu_q_code = nqb * 2 * d;
+    z.mu_q_cscale = nqb * 4;
     return z;
 }
 
@@ -92,6 +98,9 @@ WsLayout ws_layout(const Plan& p, bool quant_in_ws) {
         w.v_codes = take(z.v_codes);
         w.v_scale = take(z.v_scale);
         w.delta_s = take(z.delta_s);
+        w.mu_qb = take(z.mu_qb);
+        w.mu_q_code = take(z.mu_q_code);
+        w.mu_q_cscale = take(z.mu_q_cscale);
     }
     const size_t d = p.d;
     w.part_q = take(p.smooth_q ? (size_t)p.rows_q / QBLK * p.hq * d * 4 : 0);
@@ -129,12 +138,14 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
     const sage_attn_desc& D = *desc;
     if (D.dtype != SAGE_F16 && D.dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
     if (D.layout != SAGE_HND && D.layout != SAGE_NHD) return SAGE_ERR_LAYOUT;
-    if (!flag_ok(D.is_causal) || !flag_ok(D.smooth_q) || !flag_ok(D.smooth_k) ||
+    if (!flag_ok(D.is_causal) || !(flag_ok(D.smooth_q) || D.smooth_q == SAGE_SMOOTH_Q_BLOCK) ||
+        !flag_ok(D.smooth_k) ||
         !flag_ok(D.smooth_v) || (D.pv_mode != SAGE_PV_FP8 && D.pv_mode != SAGE_PV_HALF) ||
         !(D.kv_split == SAGE_KV_SPLIT_AUTO || D.kv_split == 0 ||
           (D.kv_split > 0 && D.kv_split % SAGE_KV_TILE == 0 && D.kv_split <= (1 << 24))) ||
         !(D.qk_block == 0 || D.qk_block == 64 || D.qk_block == 32) ||
-        !std::isfinite(D.sm_scale))
+        !std::isfinite(D.sm_scale) ||
+        (D.smooth_q == SAGE_SMOOTH_Q_BLOCK && D.pv_mode != SAGE_PV_FP8))
         return SAGE_ERR_FLAGS;
     if (D.head_dim != 64 && D.head_dim != 96 && D.head_dim != 128) return SAGE_ERR_HEAD_DIM;
     if (D.hq < 1 || D.hkv < 1 || D.hq > 65536 || D.hkv > 65536) return SAGE_ERR_SHAPE;
@@ -155,7 +166,8 @@ sage_status make_plan(const sage_attn_desc* desc, const int32_t* cuq, const int3
     p.hkv = D.hkv;
     p.group = D.hq / D.hkv;
     p.causal = D.is_causal;
-    p.smooth_q = D.smooth_q;
+    p.smooth_q = D.smooth_q != 0;
+    p.smooth_q_blk = D.smooth_q == SAGE_SMOOTH_Q_BLOCK;
     p.smooth_k = D.smooth_k;
     p.smooth_v = D.smooth_v;
     p.pv_half = D.pv_mode == SAGE_PV_HALF;
@@ -254,6 +266,7 @@ std::vector<KParams> make_params(const Plan& p) {
     base.kv_tiles = p.kv_split / KVT;
     base.nsplit = p.kv_split ? p.nsplit : 1;
     base.rows_total = p.rows_total;
+    base.bqs = p.smooth_q_blk;
     std::vector<KParams> out;
     if (!p.varlen) {
         if (p.S == 0) return out;
@@ -437,6 +450,9 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
         qa.q_scale = b.q_scale;
         qa.k_scale = b.k_scale;
         qa.delta_s = p.smooth_q ? b.delta_s : nullptr;
+        qa.mu_qb = p.smooth_q_blk ? b.mu_qb : nullptr;
+        qa.mq_code = p.smooth_q_blk ? b.mu_q_code : nullptr;
+        qa.mq_scale = p.smooth_q_blk ? b.mu_q_cscale : nullptr;
         qa.nq = chunk_blocks(P, true, p.hq, true);
         qa.nk = chunk_blocks(P, false, p.hkv, true);
         // 16-bit V: 64-token chunks (128-byte rows already); E4M3 V: one
@@ -465,6 +481,9 @@ sage_quant_bufs bufs_in_ws(const Plan& p, uint8_t* ws, const WsLayout& w) {
     b.v_codes = reinterpret_cast<uint8_t*>(ws + w.v_codes);
     b.v_scale = p.pv_half ? nullptr : reinterpret_cast<float*>(ws + w.v_scale);
     b.delta_s = p.smooth_q ? reinterpret_cast<float*>(ws + w.delta_s) : nullptr;
+    b.mu_qb = p.smooth_q_blk ? reinterpret_cast<float*>(ws + w.mu_qb) : nullptr;
+    b.mu_q_code = p.smooth_q_blk ? reinterpret_cast<int8_t*>(ws + w.mu_q_code) : nullptr;
+    b.mu_q_cscale = p.smooth_q_blk ? reinterpret_cast<float*>(ws + w.mu_q_cscale) : nullptr;
     return b;
 }
 
@@ -477,7 +496,8 @@ sage_status run_attn(const Plan& p, std::vector<KParams> kp, int dtype, const sa
         P.part_o = part_o;
         P.part_ml = part_ml;
         SAGE_TRY(launch_attn(P, dtype, b.q_codes, b.q_scale, b.k_codes, b.k_scale, b.v_codes,
-                             b.v_scale, ds, mu_v, o, lse, st));
+                             b.v_scale, ds, mu_v, o, lse, p.smooth_q_blk ? b.mu_q_code : nullptr,
+                             p.smooth_q_blk ? b.mu_q_cscale : nullptr, st));
     }
     if (p.kv_split && p.rows_total > 0) {
         MergeArgs m{};
@@ -578,12 +598,13 @@ sage_status sage_quant_qkv(const sage_attn_desc* desc, const void* q, const void
             !out->k_scale || !out->v_codes || (!p.pv_half && !out->v_scale) ||
             (p.smooth_q && !out->mu_q) ||
             (p.smooth_k && !out->mu_k) || (p.smooth_v && !out->mu_v) ||
-            (p.smooth_q && !out->delta_s))
+            (p.smooth_q && !out->delta_s) ||
+            (p.smooth_q_blk && (!out->mu_qb || !out->mu_q_code || !out->mu_q_cscale)))
             return SAGE_ERR_NULL;
     }
     const void* ptrs[] = {q, k, v, out->q_codes, out->k_codes, out->v_codes, out->q_scale,
                           out->k_scale, out->v_scale, out->mu_q, out->mu_k, out->mu_v,
-                          out->delta_s};
+                          out->delta_s, out->mu_qb, out->mu_q_code, out->mu_q_cscale};
     for (const void* ptr : ptrs)
         if (!aligned16(ptr)) return SAGE_ERR_ALIGN;
     const WsLayout w = ws_layout(p, false);
@@ -633,10 +654,11 @@ sage_status sage_attn_fwd_quantized(const sage_attn_desc* desc, const int32_t* c
     const bool empty = p.S == 0 || p.total_q == 0;
     if (!empty && (!o || !b->q_codes || !b->q_scale || !b->k_codes || !b->k_scale ||
                    !b->v_codes || (!p.pv_half && !b->v_scale) || (p.smooth_q && !b->delta_s) ||
-                   (p.smooth_v && !b->mu_v)))
+                   (p.smooth_v && !b->mu_v) ||
+                   (p.smooth_q_blk && (!b->mu_q_code || !b->mu_q_cscale))))
         return SAGE_ERR_NULL;
     const void* ptrs[] = {o, b->q_codes, b->k_codes, b->v_codes, b->q_scale, b->k_scale,
-                          b->v_scale, b->mu_v, b->delta_s};
+                          b->v_scale, b->mu_v, b->delta_s, b->mu_q_code, b->mu_q_cscale};
     for (const void* ptr : ptrs)
         if (!aligned16(ptr)) return SAGE_ERR_ALIGN;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return SAGE_ERR_ALIGN;

@@ -199,6 +199,7 @@ struct Work {
     int s;                    // index of the sequence in the launch's table
     int hkv, head, q0;        // q0 = first query row of this wave
     int head0, hpw;           // first query head of the workgroup, heads per workgroup
+    int wg_row0;              // first query row of the workgroup's tile
     int t0;                   // first key tile of the workgroup's split (0 unsplit)
     int nt_wg, nt_w;          // end (exclusive) of the key tiles of the workgroup /
                               // of this wave; tiles t0 .. end-1 are processed
@@ -244,6 +245,7 @@ __device__ inline Work decode_work(const KParams& P) {
     w.hpw = hpw;
     w.head = w.head0 + hw;
     const int wg_row0 = qt * rows;
+    w.wg_row0 = wg_row0;
     w.q0 = wg_row0 + rw * 32;
     const int wg_last = min(wg_row0 + rows, nq) - 1;
     const int end_wg = P.causal ? min(nkv, wg_last + nkv - nq + 1) : nkv;
@@ -580,11 +582,13 @@ __device__ inline void rescale(v16f* acc, float alpha) {
 // instructions, two Q.K chunks), so that their latency passes under earlier
 // matrix work instead of being waited for at every pair of reads; K chunk 0
 // is read first and arrives under the P.V.  With DEFER the previous tile's
-// P operand and row sum are formed here too, from its FP32 p in pd.
-template <int D, bool DEFER, int NPS>
+// P operand and row sum are formed here too, from its FP32 p in pd.  `mid`
+// runs between the P.V and the Q.K^T instructions (before the score
+// accumulators are live).
+template <int D, bool DEFER, int NPS, typename Mid>
 __device__ inline void mfma_phase(const uint8_t* Vs, const uint8_t* Ks, bool pv, v8i* pb,
                                   const float (&pd)[4][16], v16i* sacc, v16f* acc, const v4i* qf,
-                                  float alpha, float& l_run) {
+                                  float alpha, float& l_run, Mid mid) {
     constexpr int NC = D / 32;
     constexpr int NPV = 2 * NC;                // P.V instructions, kh-major
     v4i ka[NC][4];
@@ -604,6 +608,7 @@ __device__ inline void mfma_phase(const uint8_t* Vs, const uint8_t* Ks, bool pv,
         }
         if constexpr (DEFER) row_sum<NPS>(pd, alpha, l_run);
     }
+    mid();
     if constexpr (NC > 1) k_ops<D>(Ks, 1, ka[1]);
     __builtin_amdgcn_sched_barrier(0);
     sbias_init(sacc);
@@ -615,6 +620,137 @@ __device__ inline void mfma_phase(const uint8_t* Vs, const uint8_t* Ks, bool pv,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Per-block Q smoothing (SageAttention2 summary, "Main concepts" item 2: Q is
+// smoothed by its channel mean; here one mean per Q quantization block).  A
+// workgroup's rows form NPAIR (query head, Q block) pairs: pair p is head
+// slot p % hpw and block p / hpw of the workgroup's row tile.  The scores of
+// pair p owe ds_seq_j + (mu_b - mu_q).k_j: the sequence's compensation
+// ds_seq (the per-head bias stage, copied from the pre-pass) plus the block's
+// deviation, formed here from its 15-bit code (128*hi + lo, one FP32 scale)
+// and the INT8 key codes of the tile with v_mfma_i32_16x16x64_i8.  The
+// codes sit in a 16-row LDS table (row p: hi of pair p, row 8 + p: lo), and
+// each tile's compensations in a per-pair bias stage (two, alternating).
+// ---------------------------------------------------------------------------
+template <int QB>
+struct Bqs {
+    static constexpr int NPAIR = 256 / QB;          // pairs of a workgroup (4 or 8)
+    static constexpr int STAGE = NPAIR * KVT * 4;   // bytes of one per-pair bias stage
+    static constexpr int TROW = 128;                // table bytes per code row
+    static constexpr int TABLE = 16 * TROW;
+    static constexpr int BYTES = 2 * STAGE + TABLE + 64;   // + 8 scales (padded)
+};
+
+// Index of (sequence, head, Q block) in the per-block pre-pass arrays.
+__device__ inline int64_t qblock_index(const KParams& P, const SeqInfo& si, int head, int qb_len,
+                                       int gblk) {
+    return (si.rq * P.hq + (int64_t)head * si.npq) / qb_len + gblk;
+}
+
+// Load the workgroup's code table and scales into LDS (threads 0..135).
+// Pairs past NPAIR, blocks past the padded sequence and channels past D are
+// zero (their products vanish).
+template <int D, int QB>
+__device__ inline void bqs_load(const KParams& P, const Work& w, const int8_t* mcode,
+                                const float* mcs, uint8_t* tab, float* tsc) {
+    using B = Bqs<QB>;
+    const int tid = threadIdx.x;
+    const SeqInfo& si = w.si;
+    auto pair_index = [&](int p, int64_t* ib) {
+        if (p >= B::NPAIR) return false;
+        const int gblk = w.wg_row0 / QB + p / w.hpw;
+        if (gblk * QB >= si.npq) return false;
+        *ib = qblock_index(P, si, w.head0 + p % w.hpw, QB, gblk);
+        return true;
+    };
+    if (tid < 128) {
+        const int row = tid >> 3, g = tid & 7;
+        v4i val = {0, 0, 0, 0};
+        int64_t ib;
+        if (16 * g < D && pair_index(row & 7, &ib))
+            val = *reinterpret_cast<const v4i*>(mcode + ib * 2 * D + (row >> 3) * D + 16 * g);
+        *reinterpret_cast<v4i*>(tab + row * B::TROW + 16 * g) = val;
+    } else if (tid < 136) {
+        int64_t ib;
+        tsc[tid - 128] = pair_index(tid - 128, &ib) ? mcs[ib] : 0.0f;
+    }
+}
+
+// The per-pair compensations of one key tile, by the four waves of group 0:
+// wave wi covers the tile's LDS rows 32wi .. 32wi+31 in two 16-row MFMA
+// tiles, for every pair at once (B columns 0..7: hi codes, 8..15: lo codes).
+// bqs_mfma issues the matrix instructions and bqs_store combines and writes
+// the results (where in the MFMA phase: see the fused kernel).  The 16x16
+// result gives lane (column c, k-group g) the rows 4g .. 4g+3 of its tile
+// for column c; the lo sum of pair c comes from the lane 8 columns over (a
+// DPP rotation by 8 within the 16-lane row).
+// Rows 4g .. 4g+3 hold four consecutive keys (key_of_row), written as one
+// float4.  The deviation term is fl32(fl32(T) * fl32(s_mu * s_k)), added to
+// ds_seq without contraction.
+template <int D, int QB>
+__device__ inline void bqs_mfma(const uint8_t* Ks, const uint8_t* tab, v4i* acc) {
+    using T = Tile<D>;
+    using B = Bqs<QB>;
+    constexpr int NS = (D + 63) / 64;               // 64-channel steps
+    // (at d = 128 the thread index passes through an empty asm so that the
+    // addresses below are formed here on every tile rather than hoisted out
+    // of the loop, where they would hold registers through the whole kernel)
+    int tid = threadIdx.x;
+    if constexpr (D == 128) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wi = (tid >> 6) & 3;
+    const int col = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) acc[m] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int g = 4 * s + kg;                   // 16-channel granule
+        const v4i b = *reinterpret_cast<const v4i*>(tab + col * B::TROW + 16 * g);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int row = 32 * wi + 16 * m + col; // A row of this lane
+            const v4i a = *reinterpret_cast<const v4i*>(Ks + row * T::KRS +
+                                                        ((g ^ swz<T::KRS>(row)) << 4));
+            acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[m], 0, 0, 0);
+        }
+    }
+}
+
+// kst: the tile's key-block scales in global memory.
+template <int D, int QB>
+__device__ inline void bqs_store(const v4i* acc, const float* hds, float* pst, const float* tsc,
+                                 const float* kst, int hpw) {
+#pragma clang fp contract(off)
+    using B = Bqs<QB>;
+    int tid = threadIdx.x;                          // (d = 128: not hoisted, as in bqs_mfma)
+    if constexpr (D == 128) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wi = (tid >> 6) & 3;
+    const int col = lane & 15, kg = lane >> 4;
+    int lo[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            lo[m][i] = __builtin_amdgcn_mov_dpp(acc[m][i], 0x128, 0xf, 0xf, false);   // row_ror:8
+    if (col < B::NPAIR) {
+        const float smu = tsc[col];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int kk = key_of_row(32 * wi + 16 * m + 4 * kg);
+            const float ks = kst[kk / QB];
+            const float f = smu * ks;
+            // (16-byte integer accesses, as the operand reads: typed float
+            // accesses make the compiler wait here for the phase's copies)
+            const v4i base = *reinterpret_cast<const v4i*>(hds + (col % hpw) * KVT + kk);
+            v4i out;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float corr = (float)(acc[m][i] * 128 + lo[m][i]) * f;
+                out[i] = __float_as_int(__int_as_float(base[i]) + corr);
+            }
+            *reinterpret_cast<v4i*>(pst + col * KVT + kk) = out;
+        }
+    }
+}
 
 template <int DT>
 __device__ inline uint32_t f2h_bits(float f) {
@@ -645,7 +781,13 @@ __device__ inline uint32_t f2h_bits(float f) {
 //   every wave waits for its copies before each barrier.
 //   bias(t): three buffers, as it is read up to epoch 2t+2.
 // ---------------------------------------------------------------------------
-template <int D, int DT, bool HAS_DS, bool PVH, int QB, bool DUMP = false>
+// With BQS (per-block Q smoothing; implies HAS_DS and the FP8 P.V), group 0
+// also forms each tile's per-pair compensations at the start of its MFMA
+// phase, from the tile's K codes and per-head bias stage (both complete at
+// that point); the softmax phases of both groups read them from the per-pair
+// stage of the tile (two stages: tile t is written in epoch 2t and read in
+// epochs 2t+1 and 2t+2).
+template <int D, int DT, bool HAS_DS, bool PVH, int QB, bool DUMP = false, bool BQS = false>
 __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __restrict__ qc,
                                                  const float* __restrict__ qsc,
                                                  const int8_t* __restrict__ kc,
@@ -655,7 +797,10 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                                                  const float* __restrict__ ds,
                                                  const float* __restrict__ mu_v,
                                                  uint16_t* __restrict__ o,
-                                                 float* __restrict__ lse) {
+                                                 float* __restrict__ lse,
+                                                 const int8_t* __restrict__ mcode,
+                                                 const float* __restrict__ mcs) {
+    static_assert(!BQS || (HAS_DS && !PVH && !DUMP), "per-block Q smoothing: FP8 P.V with bias");
     extern __shared__ __align__(16) uint8_t smem[];
     using T = Tile<D, PVH>;
     const Work w = decode_work<FWD_WAVES>(P);
@@ -696,6 +841,10 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     uint8_t* kst0 = smem;
     uint8_t* vst0 = smem + 2 * T::KBYTES;
     uint8_t* dst0 = vst0 + 2 * T::VBYTES;      // score-bias stages (HAS_DS)
+    uint8_t* bq0 = dst0 + 3 * T::DSBYTES;      // per-pair stages, code table, scales (BQS)
+    uint8_t* btab = bq0 + 2 * Bqs<QB>::STAGE;
+    float* btsc = reinterpret_cast<float*>(btab + Bqs<QB>::TABLE);
+    const int my_pair = (32 * ((threadIdx.x >> 6) / w.hpw)) / QB * w.hpw + (threadIdx.x >> 6) % w.hpw;
     DmaOffsets<D, FWD_NT, PVH> off;
     off.init(si.npk);
 
@@ -703,6 +852,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     // Stage buffers are chosen by the tile's place r = t - t0 in the split.
     if (w.nt_wg > w.t0)
         stage_k<D, FWD_NT, HAS_DS, PVH>(kst0, dst0, off, kbase, dsb, si.npk, w.t0, w.hpw);
+    if constexpr (BQS) bqs_load<D, QB>(P, w, mcode, mcs, btab, btsc);
     bar();
     if (grp == 1) bar();
 
@@ -730,16 +880,48 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         if constexpr (DEFER) row_sum<NPS>(pd, alpha_prev, l_run);
     };
 
+    constexpr int NB = KVT / QB;             // key blocks of a tile (2 or 4)
     for (int t = w.t0; t < w.nt_wg; ++t) {
         const int r = t - w.t0;
         // ---- MFMA phase ----
         __builtin_amdgcn_s_setprio(2);
+        // BQS: group 0 forms the tile's per-pair compensations.  d = 128 has
+        // no registers to hold the sums through the P.V, and does all of it
+        // before the phase's copies are issued (so that its reads do not wait
+        // for them); d = 64 and 96 issue the matrix instructions here and
+        // store the results between the P.V and the Q.K^T.
+        constexpr bool BQS_EARLY = D == 128;
+        v4i bacc[2];
+        auto bqs_fin = [&]() {
+            if constexpr (BQS) {
+                if (grp == 0)
+                    bqs_store<D, QB>(bacc,
+                                  reinterpret_cast<const float*>(dst0 + (r % 3) * T::DSBYTES),
+                                  reinterpret_cast<float*>(bq0 + (r & 1) * Bqs<QB>::STAGE), btsc,
+                                  kscb + NB * t, w.hpw);
+            }
+        };
+        DmaOffsets<D, FWD_NT, PVH> offt = off;
+        if constexpr (BQS && BQS_EARLY) {
+            if (grp == 0) bqs_mfma<D, QB>(kst0 + (r & 1) * T::KBYTES, btab, bacc);
+            bqs_fin();
+        }
+        // at d = 128 the copies' per-lane addresses are formed on every tile:
+        // held through the loop they are what the registers cannot afford,
+        // and a reload between the copies waits for them
+        if constexpr (BQS && D == 128) asm volatile("" : "+v"(offt.k0), "+v"(offt.v0));
         if (t + 1 < w.nt_wg)
             stage_k<D, FWD_NT, HAS_DS, PVH>(kst0 + ((r + 1) & 1) * T::KBYTES,
-                                            dst0 + ((r + 1) % 3) * T::DSBYTES, off, kbase, dsb,
+                                            dst0 + ((r + 1) % 3) * T::DSBYTES, offt, kbase, dsb,
                                             si.npk, t + 1, w.hpw);
         if constexpr (!DUMP)   // (the Q.K^T export reads no V)
-            stage_v<D, FWD_NT, PVH>(vst0 + (r & 1) * T::VBYTES, off, vbase, si.npk, t);
+            stage_v<D, FWD_NT, PVH>(vst0 + (r & 1) * T::VBYTES, offt, vbase, si.npk, t);
+        if constexpr (BQS && !BQS_EARLY) {
+            if (grp == 0) bqs_mfma<D, QB>(kst0 + (r & 1) * T::KBYTES, btab, bacc);
+        }
+        auto bqs_mid = [&]() {
+            if constexpr (!BQS_EARLY) bqs_fin();
+        };
         if (t < w.nt_w) {
             const uint8_t* ks_ = kst0 + (r & 1) * T::KBYTES;
             if constexpr (PVH || !PIPE) {
@@ -749,18 +931,20 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                 qk_tile<D>(ks_, qf, sacc);
             } else {
                 mfma_phase<D, DEFER, NPS>(vst0 + ((r - 1) & 1) * T::VBYTES, ks_, !DUMP && r > 0,
-                                          pb, pd, sacc, acc, qf, alpha_prev, l_run);
+                                          pb, pd, sacc, acc, qf, alpha_prev, l_run, bqs_mid);
             }
-        } else if (!DUMP && t == w.nt_w && r > 0) {
-            // this wave's rows are done: flush its last tile
-            pv_prev(r - 1);
+        } else {
+            if (!DUMP && t == w.nt_w && r > 0) {
+                // this wave's rows are done: flush its last tile
+                pv_prev(r - 1);
+            }
+            bqs_mid();
         }
         // the tile's score scales, loaded ahead of the softmax phase (the
         // empty asm keeps the compiler from sinking the loads past the barrier)
         // (a zero scale -- an all-zero block -- is raised to the smallest
         // normal float, which leaves every score unchanged after rounding and
         // keeps a masked key's -inf * c at -inf)
-        constexpr int NB = KVT / QB;             // key blocks of a tile (2 or 4)
         auto cs = [&](int b) {
             if constexpr (DUMP) return 0.0f;
             const float ks = kscb[NB * t + b];
@@ -787,9 +971,11 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                 }
         } else if (!DUMP && t < w.nt_w) {
             const int kt0 = t * KVT + 16 * h;     // key of sacc[b][r] = kt0 + 32b + r
-            const float* dsl = HAS_DS ? reinterpret_cast<const float*>(dst0 + (r % 3) * T::DSBYTES) +
-                                            (w.head - w.head0) * KVT
-                                      : nullptr;
+            const float* dsl =
+                BQS ? reinterpret_cast<const float*>(bq0 + (r & 1) * Bqs<QB>::STAGE) + my_pair * KVT
+                : HAS_DS ? reinterpret_cast<const float*>(dst0 + (r % 3) * T::DSBYTES) +
+                               (w.head - w.head0) * KVT
+                         : nullptr;
             const bool need_mask =
                 (t + 1) * KVT > nkv || (P.causal && (t + 1) * KVT - 1 > wave_diag);
             // acc (the tiles before t, at the previous max) is rescaled by
@@ -1189,10 +1375,10 @@ int wg_count_host(const KParams& P, int waves) {
     return tot;
 }
 
-template <int D, bool HAS_DS, bool PVH>
+template <int D, bool HAS_DS, bool PVH, bool BQS = false, int QB = QBLK>
 constexpr int lds_bytes() {
     return 2 * Tile<D, PVH>::KBYTES + 2 * Tile<D, PVH>::VBYTES +
-           (HAS_DS ? 3 * Tile<D, PVH>::DSBYTES : 0);
+           (HAS_DS ? 3 * Tile<D, PVH>::DSBYTES : 0) + (BQS ? Bqs<QB>::BYTES : 0);
 }
 
 // Allow a kernel its dynamic LDS beyond the default, once per device (the
@@ -1211,18 +1397,20 @@ hipError_t lds_attr(const void* kernel, int bytes, std::atomic<uint64_t>& done) 
     return hipSuccess;
 }
 
-template <int D, int DT, bool HAS_DS, bool PVH, int QB>
+template <int D, int DT, bool HAS_DS, bool PVH, int QB, bool BQS = false>
 hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const int8_t* kc,
                   const float* ksc, const uint8_t* vc, const float* vsc, const float* ds,
-                  const float* mu_v, void* o, float* lse, hipStream_t st) {
+                  const float* mu_v, void* o, float* lse, const int8_t* mcode, const float* mcs,
+                  hipStream_t st) {
     static std::atomic<uint64_t> attr_set{0};
-    hipError_t e = lds_attr(reinterpret_cast<const void*>(&k_attn<D, DT, HAS_DS, PVH, QB>),
-                            lds_bytes<D, HAS_DS, PVH>(), attr_set);
+    constexpr int LDS = lds_bytes<D, HAS_DS, PVH, BQS, QB>();
+    auto* kern = &k_attn<D, DT, HAS_DS, PVH, QB, false, BQS>;
+    hipError_t e = lds_attr(reinterpret_cast<const void*>(kern), LDS, attr_set);
     if (e != hipSuccess) return e;
     const int nblocks = wg_count_host(P, FWD_WAVES) * P.nsplit;
     if (nblocks <= 0) return hipSuccess;
-    k_attn<D, DT, HAS_DS, PVH, QB><<<nblocks, FWD_NT, lds_bytes<D, HAS_DS, PVH>(), st>>>(
-        P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, static_cast<uint16_t*>(o), lse);
+    kern<<<nblocks, FWD_NT, LDS, st>>>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v,
+                                       static_cast<uint16_t*>(o), lse, mcode, mcs);
     return hipGetLastError();
 }
 
@@ -1256,7 +1444,7 @@ int decode_waves_per_cu(int d, bool pv_half, bool has_ds, int group) {
 }
 
 bool use_decode_kernel(const KParams& P) {
-    if (P.kv_tiles <= 0) return false;
+    if (P.kv_tiles <= 0 || P.bqs) return false;
     int mq = 0;
     const int n = P.tab.uniform ? 1 : P.tab.n;
     for (int s = 0; s < n; ++s) mq = std::max(mq, P.tab.nq[s]);
@@ -1265,15 +1453,23 @@ bool use_decode_kernel(const KParams& P) {
 
 hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const float* qsc,
                        const int8_t* kc, const float* ksc, const uint8_t* vc, const float* vsc,
-                       const float* ds, const float* mu_v, void* o, float* lse, hipStream_t st) {
+                       const float* ds, const float* mu_v, void* o, float* lse,
+                       const int8_t* mcode, const float* mcs, hipStream_t st) {
     const bool dec = use_decode_kernel(P);
+    if (P.bqs && (!ds || !mcode || !mcs || P.pv_half)) return hipErrorInvalidValue;
 #define SAGE_AQ(D, DT, PVH, QB)                                                                  \
     do {                                                                                         \
         if (dec)                                                                                 \
             return ds ? decode_d<D, DT, true, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, st) \
                       : decode_d<D, DT, false, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, st); \
-        return ds ? attn_d<D, DT, true, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st) \
-                  : attn_d<D, DT, false, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, st); \
+        if constexpr (!PVH)                                                                      \
+            if (P.bqs)                                                                           \
+                return attn_d<D, DT, true, false, QB, true>(P, qc, qsc, kc, ksc, vc, vsc, ds,   \
+                                                            mu_v, o, lse, mcode, mcs, st);      \
+        return ds ? attn_d<D, DT, true, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse, \
+                                                 nullptr, nullptr, st)                           \
+                  : attn_d<D, DT, false, PVH, QB>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v, o, lse,\
+                                                  nullptr, nullptr, st);                         \
     } while (0)
 #define SAGE_AH(D, DT, PVH)                    \
     do {                                       \
@@ -1312,7 +1508,7 @@ hipError_t qk_dump_d(const KParams& P, const int8_t* qc, const int8_t* kc, int32
     if (nblocks <= 0) return hipSuccess;
     kern<<<nblocks, FWD_NT, lds_bytes<D, false, false>(), st>>>(
         P, qc, nullptr, kc, nullptr, nullptr, nullptr, nullptr, nullptr,
-        reinterpret_cast<uint16_t*>(s_out), nullptr);
+        reinterpret_cast<uint16_t*>(s_out), nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 }  // namespace

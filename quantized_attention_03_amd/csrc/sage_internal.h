@@ -52,6 +52,7 @@ struct KParams {
     // split-major over rows_total rows (the lse row index)
     int32_t kv_tiles, nsplit;
     int64_t rows_total;
+    int32_t bqs;                        // per-block Q smoothing (bias formed in the kernel)
     float* part_o;                      // [nsplit][rows_total][d]
     float* part_ml;                     // [nsplit][rows_total][2]: m (log2 units), l
     SeqTab tab;
@@ -181,6 +182,11 @@ struct QuantArgs {
     int8_t *q_codes, *k_codes;
     uint8_t* v_codes;     // E4M3 codes, or 16-bit values when v_half
     float *q_scale, *k_scale, *delta_s;
+    // per-block Q smoothing (mu_q is then the sequence mean): the block means,
+    // the codes of their deviations from mu_q and the codes' scales
+    float* mu_qb;
+    int8_t* mq_code;
+    float* mq_scale;
     int32_t nq, nk, nv;   // workgroups: Q blocks, K blocks, V chunks
     int32_t v_half;       // V operand kept 16-bit (no scale) instead of E4M3
 };
@@ -190,10 +196,11 @@ int stat_chunks_per_wg(int d);
 hipError_t launch_stats(const KParams& P, int dtype, const StatJobs& J, hipStream_t st);
 hipError_t launch_finalize(const KParams& P, const FinJobs& J, hipStream_t st);
 hipError_t launch_quant(const KParams& P, int dtype, const QuantArgs& A, hipStream_t st);
+// mcode, mcs: the per-block Q smoothing codes and scales (P.bqs), else NULL.
 hipError_t launch_attn(const KParams& P, int dtype, const int8_t* qc, const float* qsc,
                        const int8_t* kc, const float* ksc, const uint8_t* vc,
                        const float* vsc, const float* ds, const float* mu_v, void* o,
-                       float* lse, hipStream_t st);
+                       float* lse, const int8_t* mcode, const float* mcs, hipStream_t st);
 // Workgroups of one fused-kernel launch before any key split.
 int attn_base_wgs(const KParams& P);
 // Whether a split launch runs the one-wave decode kernel: every sequence's

@@ -284,19 +284,35 @@ __global__ __launch_bounds__(WG) void k_finalize(KParams P, FinJobs J) {
 // ---------------------------------------------------------------------------
 // QB: tokens per quantization block (64: the workgroup's whole chunk; 32:
 // each half of it gets its own absmax and scale).
-template <int DT, int D, bool DELTA, int QB = QBLK>
+// With BQ (Q of a problem with per-block Q smoothing; `mu` is then NULL and
+// `bq.mu_bar` the sequence mean), each quantization block is smoothed by its
+// own channel mean (its valid tokens summed in order in FP32, divided by
+// their count), and the block's deviation from the sequence mean,
+// x = fl32(mu_b - mu_bar), is written as a 15-bit code: a = max |x|,
+// inv = 16256/a, scale = a/16256, y = x*inv, hi = clamp(rne(y/128), +-127),
+// lo = rne(y - 128*hi); blocks without a valid token get zeros.
+struct BlockQ {
+    const float* mu_bar;   // [S][hq][d]
+    float* mu_b;           // per block [d]
+    int8_t* code;          // per block [2][d]: hi, lo
+    float* cscale;         // per block
+};
+
+template <int DT, int D, bool DELTA, int QB = QBLK, bool BQ = false>
 __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restrict__ x,
                                       Strides xs, int is_q, int heads,
                                       const float* __restrict__ mu, int8_t* __restrict__ codes,
                                       float* __restrict__ scales,
                                       const float* __restrict__ mu_q,
-                                      float* __restrict__ delta_s, int blkid, float* smf) {
+                                      float* __restrict__ delta_s, int blkid, float* smf,
+                                      BlockQ bq = BlockQ{}) {
     constexpr int GPR = D / 8;              // granules per token row
     constexpr int NG = QBLK * GPR;          // granules per block
     constexpr int PER = (NG + WG - 1) / WG; // granules per thread
     constexpr int NSUB = QBLK / QB;         // quantization blocks per chunk (1 or 2)
     float* red = smf;                       // NSUB * WG / 64 floats
-    float* ks_lds = smf + 2 * (WG / 64);    // QBLK * D floats (DELTA)
+    float* ks_lds = smf + 2 * (WG / 64);    // QBLK * D floats (DELTA, BQ)
+    float* mub_lds = ks_lds + QBLK * D;     // NSUB * D floats (BQ)
 
     int local;
     ChunkCount cnt{&P, is_q != 0, heads, 1};
@@ -314,18 +330,82 @@ __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restri
     float amax[NSUB];
 #pragma unroll
     for (int k = 0; k < NSUB; ++k) amax[k] = 0.0f;
+    if constexpr (BQ) {
+        // the chunk's raw values through LDS; thread c < NSUB*D sums channel
+        // c % D of sub-block c / D down its valid tokens, in order
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int gi = threadIdx.x + i * WG;
+            const int r = gi / GPR, cg = (gi % GPR) * 8;
+            const int t = blk * QBLK + r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) val[i][e] = 0.0f;
+            if (gi < NG && t < n) load8<DT>(x + el0 + (int64_t)t * xs.n + cg, val[i]);
+            if (gi < NG) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ks_lds[r * D + cg + e] = val[i][e];
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < NSUB * D) {
+            const int sub = threadIdx.x / D, ch = threadIdx.x % D;
+            const int nvalid = min(QB, n - (blk * QBLK + sub * QB));
+            float sum = 0.0f;
+            for (int r = 0; r < nvalid; ++r) sum = sum + ks_lds[(sub * QB + r) * D + ch];
+            const float m = nvalid > 0 ? sum / (float)nvalid : 0.0f;
+            mub_lds[sub * D + ch] = m;
+            bq.mu_b[(row0 / QB + blk * NSUB + sub) * D + ch] = m;
+        }
+        __syncthreads();
+        // the deviation codes: wave `sub` codes sub-block sub
+        const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (wv < NSUB) {
+            const int nvalid = min(QB, n - (blk * QBLK + wv * QB));
+            const float* mb = bq.mu_bar + ((int64_t)si.sid * heads + h) * D;
+            float dv[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int c = lane + 64 * k;
+                dv[k] = (c < D && nvalid > 0) ? mub_lds[wv * D + c] - mb[c] : 0.0f;
+            }
+            const float a = wave_max(fmaxf(fabsf(dv[0]), fabsf(dv[1])));
+            const float inv = a > 0.0f ? 16256.0f / a : 0.0f;
+            const int64_t ib = row0 / QB + blk * NSUB + wv;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int c = lane + 64 * k;
+                if (c < D) {
+                    const float y = dv[k] * inv;
+                    const float hi = fminf(fmaxf(rintf(y * 0.0078125f), -127.0f), 127.0f);
+                    const float lo = rintf(y - 128.0f * hi);
+                    bq.code[ib * 2 * D + c] = (int8_t)(int)hi;
+                    bq.code[ib * 2 * D + D + c] = (int8_t)(int)lo;
+                }
+            }
+            if (lane == 0) bq.cscale[ib] = a > 0.0f ? a / 16256.0f : 0.0f;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int gi = threadIdx.x + i * WG;
         const int r = gi / GPR, cg = (gi % GPR) * 8;
         const int t = blk * QBLK + r;
+        if constexpr (!BQ) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) val[i][e] = 0.0f;
+            for (int e = 0; e < 8; ++e) val[i][e] = 0.0f;
+        }
         if (gi < NG && t < n) {
-            load8<DT>(x + el0 + (int64_t)t * xs.n + cg, val[i]);
-            if (muh) {
+            if constexpr (BQ) {
+                // (the raw values are already in registers)
+                const float* mb = mub_lds + (NSUB == 1 || r < QB ? 0 : D);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) val[i][e] = val[i][e] - muh[cg + e];
+                for (int e = 0; e < 8; ++e) val[i][e] = val[i][e] - mb[cg + e];
+            } else {
+                load8<DT>(x + el0 + (int64_t)t * xs.n + cg, val[i]);
+                if (muh) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) val[i][e] = val[i][e] - muh[cg + e];
+                }
             }
             float m = 0.0f;
 #pragma unroll
@@ -583,17 +663,23 @@ __device__ inline void half_v_chunk(const KParams& P, const uint16_t* __restrict
 // All quantization of a problem in one launch: the Q blocks, then the K
 // blocks (with the score bias when Q is smoothed), then the V chunks.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool DELTA, int QB>
+template <int DT, int D, bool DELTA, int QB, bool BQ = false>
 __global__ __launch_bounds__(WG) void k_quant(KParams P, QuantArgs A) {
-    constexpr int QK_LDS = (2 * (WG / 64) + (DELTA ? QBLK * D : 0)) * 4;
+    constexpr int QK_LDS = (2 * (WG / 64) + (DELTA || BQ ? QBLK * D : 0) + (BQ ? 2 * D : 0)) * 4;
     constexpr int VL = quant_v_lds_bytes<D>() > half_v_lds_bytes<D>() ? quant_v_lds_bytes<D>()
                                                                       : half_v_lds_bytes<D>();
     constexpr int LDS = QK_LDS > VL ? QK_LDS : VL;
     __shared__ __align__(16) uint8_t sm[LDS];
     int blk = blockIdx.x;
     if (blk < A.nq) {
-        quant_qk_block<DT, D, false, QB>(P, A.q, P.qs, 1, P.hq, A.mu_q, A.q_codes, A.q_scale,
-                                     nullptr, nullptr, blk, reinterpret_cast<float*>(sm));
+        if constexpr (BQ)
+            quant_qk_block<DT, D, false, QB, true>(
+                P, A.q, P.qs, 1, P.hq, nullptr, A.q_codes, A.q_scale, nullptr, nullptr, blk,
+                reinterpret_cast<float*>(sm), BlockQ{A.mu_q, A.mu_qb, A.mq_code, A.mq_scale});
+        else
+            quant_qk_block<DT, D, false, QB>(P, A.q, P.qs, 1, P.hq, A.mu_q, A.q_codes,
+                                             A.q_scale, nullptr, nullptr, blk,
+                                             reinterpret_cast<float*>(sm));
         return;
     }
     blk -= A.nq;
@@ -637,10 +723,12 @@ hipError_t launch_finalize(const KParams& P, const FinJobs& J, hipStream_t st) {
 template <int DT, int D>
 static void quant_d(const KParams& P, const QuantArgs& A, int nb, hipStream_t st) {
     if (P.qb == 32) {
-        if (A.delta_s) k_quant<DT, D, true, 32><<<nb, WG, 0, st>>>(P, A);
+        if (A.mq_code) k_quant<DT, D, true, 32, true><<<nb, WG, 0, st>>>(P, A);
+        else if (A.delta_s) k_quant<DT, D, true, 32><<<nb, WG, 0, st>>>(P, A);
         else k_quant<DT, D, false, 32><<<nb, WG, 0, st>>>(P, A);
     } else {
-        if (A.delta_s) k_quant<DT, D, true, QBLK><<<nb, WG, 0, st>>>(P, A);
+        if (A.mq_code) k_quant<DT, D, true, QBLK, true><<<nb, WG, 0, st>>>(P, A);
+        else if (A.delta_s) k_quant<DT, D, true, QBLK><<<nb, WG, 0, st>>>(P, A);
         else k_quant<DT, D, false, QBLK><<<nb, WG, 0, st>>>(P, A);
     }
 }

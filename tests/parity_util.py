@@ -83,11 +83,30 @@ def unpack_quant(w, bufs, pv="fp8", qb=64):
         R.mu_q.append(host["mu_q"].reshape(-1, hq, d)[s] if w.smooth_q else None)
         R.mu_k.append(host["mu_k"].reshape(-1, hkv, d)[s] if w.smooth_k else None)
         R.mu_v.append(host["mu_v"].reshape(-1, hkv, d)[s] if w.smooth_v else None)
+        blockwise = w.smooth_q == "block"
         if w.smooth_q:
             ds = host["delta_s"][rk * hq:rk * hq + hq * npk].reshape(hq, npk)
-            R.ds.append(ds[:, :nkv])
+            # per-block smoothing: the buffer holds the sequence mean's share;
+            # the blocks' compensations are formed inside the fused kernel
+            (R.ds_seq if blockwise else R.ds).append(ds[:, :nkv])
+            (R.ds if blockwise else R.ds_seq).append(None)
         else:
             R.ds.append(None)
+            R.ds_seq.append(None)
+        if blockwise:
+            nb, nbp = -(-nq // qb), npq // qb
+            b0 = rq * hq // qb
+            mub = host["mu_qb"][b0 * d:(b0 + hq * nbp) * d].reshape(hq, nbp, d)
+            code = host["mu_q_code"][b0 * 2 * d:(b0 + hq * nbp) * 2 * d].reshape(hq, nbp, 2, d)
+            csc = host["mu_q_cscale"][b0:b0 + hq * nbp].reshape(hq, nbp)
+            pads_ok &= not mub[:, nb:].any() and not code[:, nb:].any() and not csc[:, nb:].any()
+            R.mu_qb.append(mub[:, :nb])
+            R.mu_code.append(code[:, :nb])
+            R.mu_cscale.append(csc[:, :nb])
+        else:
+            R.mu_qb.append(None)
+            R.mu_code.append(None)
+            R.mu_cscale.append(None)
         rq += npq
         rk += npk
     return R, pads_ok
@@ -99,7 +118,8 @@ def bits(a):
 
 
 def assert_prepass_equal(gpu: orc.Prepass, ref: orc.Prepass, w):
-    for name in ("mu_q", "mu_k", "mu_v", "qc", "qs", "kc", "ks", "vc", "vs"):
+    for name in ("mu_q", "mu_k", "mu_v", "qc", "qs", "kc", "ks", "vc", "vs", "mu_qb", "mu_code",
+                 "mu_cscale"):
         for s, (g, r) in enumerate(zip(getattr(gpu, name), getattr(ref, name))):
             if r is None:
                 assert g is None, name
@@ -109,7 +129,9 @@ def assert_prepass_equal(gpu: orc.Prepass, ref: orc.Prepass, w):
                 bad = np.argwhere(bits(g) != bits(r))
                 raise AssertionError(f"{name}[seq {s}] differs at {len(bad)} places, first "
                                      f"{bad[:3].tolist()}: gpu {g[tuple(bad[0])]} ref {r[tuple(bad[0])]}")
-    for s, (g, r) in enumerate(zip(gpu.ds, ref.ds)):
+    blockwise = w.smooth_q == "block"
+    for s, (g, r) in enumerate(zip(gpu.ds_seq if blockwise else gpu.ds,
+                                   ref.ds_seq if blockwise else ref.ds)):
         if r is not None:
             assert g.shape == r.shape, ("ds", s, g.shape, r.shape)
             if r.size:

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = qa.lib()
-    assert L.sage_abi_version() == 2
+    assert L.sage_abi_version() == 3
     for code in range(14):
         assert L.sage_status_string(code)
     assert L.sage_status_string(999) == b"unknown status"
@@ -176,6 +176,27 @@ def test_finer_qk_block_sizes():
     assert b["q_scale"] == 2 * a["q_scale"] and b["k_scale"] == 2 * a["k_scale"]
     assert {k: v for k, v in b.items() if k not in ("q_scale", "k_scale")} == \
         {k: v for k, v in a.items() if k not in ("q_scale", "k_scale")}
+
+
+def test_block_q_smoothing_sizes_and_flags():
+    """smooth_q = SAGE_SMOOTH_Q_BLOCK adds the per-block means, deviation
+    codes and scales (one per Q block, the index of q_scale), keeps everything
+    else of smooth_q = 1, and is refused with 16-bit P.V or an unknown value."""
+    hq, dd = 8, 128
+    for qb in (64, 32):
+        a = qa.quant_buf_sizes(_desc(smooth_q=1, qk_block=qb))
+        b = qa.quant_buf_sizes(_desc(smooth_q=_abi.SMOOTH_Q_BLOCK, qk_block=qb))
+        nqb = 2 * hq * _pad(100, 64) // qb                 # B = 2, nq = 100
+        assert b["mu_qb"] == nqb * dd * 4 and b["mu_q_code"] == nqb * 2 * dd
+        assert b["mu_q_cscale"] == nqb * 4 == b["q_scale"]
+        assert a["mu_qb"] == a["mu_q_code"] == a["mu_q_cscale"] == 0
+        assert {k: v for k, v in b.items() if not k.startswith("mu_q")} == \
+            {k: v for k, v in a.items() if not k.startswith("mu_q")}
+        assert b["mu_q"] == a["mu_q"]
+    name = lambda st: _abi.STATUS_NAMES[st]
+    assert name(_ws(_desc(smooth_q=_abi.SMOOTH_Q_BLOCK, pv_mode=_abi.PV_HALF))[0]) == "SAGE_ERR_FLAGS"
+    assert name(_ws(_desc(smooth_q=3))[0]) == "SAGE_ERR_FLAGS"
+    assert _ws(_desc(smooth_q=_abi.SMOOTH_Q_BLOCK))[0] == 0
 
 
 def test_half_pv_sizes():
