@@ -382,8 +382,10 @@ SAGE_API sage_status sage_debug_e4m3_encode(uint32_t first, uint32_t count, uint
 typedef enum { SAGE_MICRO_I8 = 0, SAGE_MICRO_F8 = 1, SAGE_MICRO_EXP = 2, SAGE_MICRO_FMA = 3 } sage_micro_op;
 SAGE_API sage_status sage_micro_rate(int32_t op, int32_t reps, double* rate, void* stream);
 
-/* Human-readable name of a status code (static storage). */
-SAGE_API const char* sage_status_string(sage_status status);
+/* Human-readable name of a status code (static storage); any other value
+ * gives "unknown status".  (The code is taken as an integer, so that a value
+ * outside the enumeration is well defined.) */
+SAGE_API const char* sage_status_string(int32_t status);
 
 /* SAGE_ABI_VERSION of the built library. */
 SAGE_API int32_t sage_abi_version(void);

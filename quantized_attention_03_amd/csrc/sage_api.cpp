@@ -730,7 +730,7 @@ sage_status sage_micro_rate(int32_t op, int32_t reps, double* rate, void* stream
     return SAGE_OK;
 }
 
-const char* sage_status_string(sage_status s) {
+const char* sage_status_string(int32_t s) {
     switch (s) {
         case SAGE_OK: return "ok";
         case SAGE_ERR_NULL: return "null pointer";
