@@ -7,6 +7,9 @@
 //   s_ij = (qc_i . kc_j) * sq_i * sk_j * sm_scale (+ ds_j * sm_scale)
 //   online softmax over 128-key tiles, p^ = e4m3(448 * 2^(s*log2e - m)),
 //   l accumulated from the FP32 p, o_i = sum p^ v^ * (v_scale / 448) / l (+ mu_v).
+// ds_j compensates Q smoothing: mu_q . k_j for one mean per sequence, plus,
+// with one mean per Q block, the block's deviation from it, formed here from
+// its code and the INT8 key codes (see Bqs below).
 //
 // Design for CDNA4:
 //  * A wave owns 32 query rows of one query head.  With GQA, the waves of a
@@ -33,15 +36,14 @@
 //  * Ping-pong: a workgroup has 8 waves in two groups of 4; the two waves
 //    that share a SIMD belong to different groups.  Each group alternates an
 //    MFMA phase and a softmax phase, offset by one phase from the other
-//    group, with a workgroup barrier between phases.  The softmax phase is
-//    the score half of tile t (exact S, row max, exponent FMA, v_exp_f32);
-//    the MFMA phase holds the P.V of tile t-1 with its operand half (FP8
-//    packing of p, the alpha rescale of O, the row sum of p) and then
-//    Q.K(t)^T.  A single wave issues VALU work only about every fifth
-//    cycle, about half of what the SIMD takes from two waves, so the work
-//    that does not depend on the new scores is moved to the wave whose
-//    matrix instructions are in flight; the MFMA phase runs at raised
-//    priority.
+//    group, with a workgroup barrier between phases.  The MFMA phase holds
+//    the alpha rescale of O and the P.V of tile t-1, then Q.K(t)^T, at
+//    raised priority; the softmax phase the score half of tile t (exact S,
+//    row max, exponent FMA, v_exp_f32) and its operand half (the row sum of
+//    p and the FP8 packing).  At d = 64, where the softmax phase is the whole
+//    bound, the operand half moves to the next MFMA phase, under its matrix
+//    instructions (a single wave issues VALU work only about every fifth
+//    cycle, about half of what the SIMD takes from two waves).
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
 #include <algorithm>
@@ -419,10 +421,13 @@ __device__ inline float swap_sum(float x) {
 // bytes 0..15 and 16..31) -- or, with 16-bit operands (PVH), p itself
 // rounded into the type DT, eight keys per ph entry as pv_tile_h reads them
 // (pack_p).
-template <bool MASK, bool HAS_DS, bool PVH = false, int QB = QBLK>
+// PRESUB: the scores in sacc are already exact (the bias subtracted in the
+// MFMA phase, as float bits).
+template <bool MASK, bool HAS_DS, bool PVH = false, int QB = QBLK, bool PRESUB = false>
 __device__ inline float score_exp(v16i* sacc, float (&p)[4][16], float c0, float c1, float c2,
                                   float c3, const float* dsl, float sml2, int kt0, int lim,
                                   float& m_run) {
+    constexpr float SB = PRESUB ? 0.0f : SBIAS_F;
     constexpr float POFF = PVH ? 0.0f : LOG2_448;
     auto cof = [&](int b) {
         if constexpr (QB == 32) return b == 0 ? c0 : (b == 1 ? c1 : (b == 2 ? c2 : c3));
@@ -449,7 +454,8 @@ __device__ inline float score_exp(v16i* sacc, float (&p)[4][16], float c0, float
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) p[b][r] = __int_as_float(sacc[b][r]) - SBIAS_F;
+            for (int r = 0; r < 16; ++r)
+                p[b][r] = PRESUB ? __int_as_float(sacc[b][r]) : __int_as_float(sacc[b][r]) - SB;
         auto fmax16 = [&](int b) {
             float l1[5];
 #pragma unroll
@@ -480,7 +486,8 @@ __device__ inline float score_exp(v16i* sacc, float (&p)[4][16], float c0, float
             const float c = cof(b);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float y = fmaf(__int_as_float(sacc[b][r]) - SBIAS_F, c, dsl[32 * b + 16 * h + r]);
+                const float sv = PRESUB ? __int_as_float(sacc[b][r]) : __int_as_float(sacc[b][r]) - SB;
+                float y = fmaf(sv, c, dsl[32 * b + 16 * h + r]);
                 if (MASK) y = 32 * b + r > th ? -INFINITY : y;
                 p[b][r] = y;
                 mt = fmaxf(mt, y);
@@ -554,13 +561,14 @@ __device__ inline void pack_p(const float (&p)[4][16], v8i* pb, v4i* ph) {
 }
 
 // The whole online softmax of one tile (both halves in one place).
-template <bool MASK, bool HAS_DS, bool PVH = false, int DT = 0, int QB = QBLK, int NPS = 8>
+template <bool MASK, bool HAS_DS, bool PVH = false, int DT = 0, int QB = QBLK, int NPS = 8,
+          bool PRESUB = false>
 __device__ inline float softmax_tile(v16i* sacc, v8i* pb, v4i* ph, float c0, float c1, float c2,
                                      float c3, const float* dsl, float sml2, int kt0, int lim,
                                      float& m_run, float& l_run) {
     float p[4][16];
-    const float alpha = score_exp<MASK, HAS_DS, PVH, QB>(sacc, p, c0, c1, c2, c3, dsl, sml2, kt0,
-                                                         lim, m_run);
+    const float alpha = score_exp<MASK, HAS_DS, PVH, QB, PRESUB>(sacc, p, c0, c1, c2, c3, dsl,
+                                                                 sml2, kt0, lim, m_run);
     row_sum<NPS>(p, alpha, l_run);
     pack_p<PVH, DT>(p, pb, ph);
     return alpha;
@@ -867,6 +875,12 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     constexpr bool DEFER = D == 64 && !PVH;
     // software-pipelined LDS operand reads in the MFMA phase (FP8 path)
     constexpr bool PIPE = true;
+    // With the score bias at d = 128, the exact scores (the accumulator bias
+    // subtracted) are formed at the end of the MFMA phase, in place, where
+    // the waves wait at the barrier, instead of in the softmax phase (3%
+    // faster there; without the bias it measured 3% slower on causal_gqa and
+    // neutral on llm_prefill and at d = 96).
+    constexpr bool PRESUB = !PVH && !DUMP && HAS_DS && D == 128;
     v16i sacc[4];               // a tile's biased int32 scores (Q.K^T)
     float pd[4][16];            // with DEFER: the previous tile's FP32 p (else unused)
     float alpha_prev = 1.0f;   // rescale owed to acc before its next P.V
@@ -906,10 +920,12 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
             if (grp == 0) bqs_mfma<D, QB>(kst0 + (r & 1) * T::KBYTES, btab, bacc);
             bqs_fin();
         }
-        // at d = 128 the copies' per-lane addresses are formed on every tile:
-        // held through the loop they are what the registers cannot afford,
-        // and a reload between the copies waits for them
-        if constexpr (BQS && D == 128) asm volatile("" : "+v"(offt.k0), "+v"(offt.v0));
+        // at d = 128 with the block bias or with 16-bit P and the score bias,
+        // the copies' per-lane addresses are formed on every tile: held
+        // through the loop they are what the registers cannot afford, and a
+        // reload between the copies waits for them
+        if constexpr (D == 128 && (BQS || (PVH && HAS_DS)))
+            asm volatile("" : "+v"(offt.k0), "+v"(offt.v0));
         if (t + 1 < w.nt_wg)
             stage_k<D, FWD_NT, HAS_DS, PVH>(kst0 + ((r + 1) & 1) * T::KBYTES,
                                             dst0 + ((r + 1) % 3) * T::DSBYTES, offt, kbase, dsb,
@@ -932,6 +948,16 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
             } else {
                 mfma_phase<D, DEFER, NPS>(vst0 + ((r - 1) & 1) * T::VBYTES, ks_, !DUMP && r > 0,
                                           pb, pd, sacc, acc, qf, alpha_prev, l_run, bqs_mid);
+                if constexpr (PRESUB) {
+                    // (the empty asm keeps each subtraction here)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) {
+                            sacc[b][rr] = __float_as_int(__int_as_float(sacc[b][rr]) - SBIAS_F);
+                            asm volatile("" : "+v"(sacc[b][rr]));
+                        }
+                }
             }
         } else {
             if (!DUMP && t == w.nt_w && r > 0) {
@@ -982,17 +1008,17 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
             // alpha in the next MFMA phase, before the P.V of tile t
             if constexpr (DEFER) {
                 if (need_mask)
-                    alpha_prev = score_exp<true, HAS_DS, PVH, QB>(sacc, pd, c0, c1, c2, c3, dsl,
+                    alpha_prev = score_exp<true, HAS_DS, PVH, QB, PRESUB>(sacc, pd, c0, c1, c2, c3, dsl,
                                                                   P.sml2, kt0, lim, m_run);
                 else
-                    alpha_prev = score_exp<false, HAS_DS, PVH, QB>(sacc, pd, c0, c1, c2, c3, dsl,
+                    alpha_prev = score_exp<false, HAS_DS, PVH, QB, PRESUB>(sacc, pd, c0, c1, c2, c3, dsl,
                                                                    P.sml2, kt0, lim, m_run);
             } else {
                 if (need_mask)
-                    alpha_prev = softmax_tile<true, HAS_DS, PVH, DT, QB, NPS>(
+                    alpha_prev = softmax_tile<true, HAS_DS, PVH, DT, QB, NPS, PRESUB>(
                         sacc, pb, ph, c0, c1, c2, c3, dsl, P.sml2, kt0, lim, m_run, l_run);
                 else
-                    alpha_prev = softmax_tile<false, HAS_DS, PVH, DT, QB, NPS>(
+                    alpha_prev = softmax_tile<false, HAS_DS, PVH, DT, QB, NPS, PRESUB>(
                         sacc, pb, ph, c0, c1, c2, c3, dsl, P.sml2, kt0, lim, m_run, l_run);
             }
         }
