@@ -13,6 +13,10 @@ It then checks, against the oracle on the same seeded inputs:
   cosine 0.999 of the same-recipe oracle, and cosine 0.99 of exact FP64
   attention;
 * the LSE against the oracle's.
+
+A second set of 64 cases (seeds of their own) draws the same way and then
+smooths Q per quantization block (FP8 P.V), with a Q offset that drifts
+along the sequence.
 """
 import numpy as np
 import pytest
@@ -25,9 +29,20 @@ from tests import parity_util as pu
 pytestmark = pytest.mark.gpu
 
 NCASES = 256
+NBLOCK = 64
 
 
 def _draw(i: int):
+    if i >= NCASES:
+        # per-block Q smoothing: a case of its own seed with that mode
+        w, _, qb, split = _draw_plain(5000 + i)
+        import dataclasses
+        return dataclasses.replace(w, name=f"fuzz{i}", smooth_q="block",
+                                   q_drift_sigma=1.5), "fp8", qb, split
+    return _draw_plain(i)
+
+
+def _draw_plain(i: int):
     rng = np.random.default_rng(1000 + i)
     d = int(rng.choice([64, 96, 128]))
     hkv = int(rng.choice([1, 2, 3]))
@@ -68,7 +83,7 @@ def _kw(w, pv, qb, split):
                 qk_block=qb, kv_split=split)
 
 
-@pytest.mark.parametrize("i", range(NCASES))
+@pytest.mark.parametrize("i", range(NCASES + NBLOCK))
 def test_fuzz_case(i):
     w, pv, qb, split = _draw(i)
     pu.say(f"[fuzz {i}] pv={pv} qk_block={qb} kv_split={split} {w}")

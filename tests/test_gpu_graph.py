@@ -4,8 +4,9 @@ once and replayed several times, with eager work and synchronizations
 between the replays.  Every replay must reproduce the eager result bit for
 bit, and a replay after the inputs change in place must match an eager call
 on the new inputs.  Cases: the fused kernel, the split key range with the
-one-wave decode kernel and its merge, and a varlen problem with every
-smoothing flag in the 16-bit P.V mode."""
+one-wave decode kernel and its merge, a varlen problem with every smoothing
+flag in the 16-bit P.V mode, and per-block Q smoothing (the block bias formed
+in the fused kernel) with a split key range."""
 import pytest
 import torch
 
@@ -24,6 +25,8 @@ CASES = {
     "varlen_half_smooth": (R(W["varlen_d128"], Hq=4, Hkv=2, seqlens_q=[100, 0, 37],
                              seqlens_kv=[130, 20, 300], smooth_q=True, smooth_v=True),
                            "half", 0),
+    "block_smoothing_split": (R(W["video_dit_block"], Hq=4, Hkv=2, Nq=200, Nkv=600),
+                              "fp8", 256),
 }
 
 
