@@ -72,6 +72,8 @@ def lib():
         "orc_qk_int32": (None, [P, P, i64, i64, i32, P]),
         "orc_attn_recipe_rows": (None, [P, P, P, P, P, P, P, P, i64, i64, i32, f32,
                                         i32, i32, i32, i64, P, i64, P, P, P]),
+        "orc_attn_recipe_rows_blockds": (None, [P, P, P, P, P, P, P, i64, P, i64, i64, i32, f32,
+                                                i32, i32, i32, i64, P, i64, P, P, P]),
         "orc_attn_recipe_half_rows": (None, [P, P, P, P, P, i32, P, P, i64, i64, i32, f32,
                                              i32, i32, i32, i64, P, i64, P, P, P]),
         "orc_attn_exact_rows": (None, [P, P, P, i64, i64, i32, f64, i32, P, i64, P, P]),
@@ -216,9 +218,10 @@ def qk_int32(qc, kc) -> np.ndarray:
 
 
 def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, rows, split=0,
-                     blk=BLK, tie=False):
+                     blk=BLK, tie=False, ds_rows=0):
     """The INT8-QK / FP8-PV recipe for selected rows.  Returns (out, lse), and
-    with tie=True also the rounding-tie bound [nrows, d] (sage_oracle.c)."""
+    with tie=True also the rounding-tie bound [nrows, d] (sage_oracle.c).
+    ds_rows > 0: ds is [Q blocks, nkv], one compensation per ds_rows rows."""
     qc, kc, vc = _c(qc, np.int8), _c(kc, np.int8), _c(vc, np.uint8)
     nq, d = qc.shape
     nkv = kc.shape[0]
@@ -226,12 +229,16 @@ def attn_recipe_rows(qc, qs, kc, ks, vc, vs, ds, mu_v, sm_scale, causal, bkv, ro
     out = np.empty((rows.size, d), np.float32)
     lse = np.empty(rows.size, np.float32)
     tb = np.empty((rows.size, d), np.float32) if tie else None
-    lib().orc_attn_recipe_rows(
-        _p(qc), _p(_c(qs, np.float32)), _p(kc), _p(_c(ks, np.float32)), _p(vc),
-        _p(_c(vs, np.float32)), _p(None if ds is None else _c(ds, np.float32)),
-        _p(None if mu_v is None else _c(mu_v, np.float32)), nq, nkv, d,
-        float(sm_scale), int(causal), int(bkv), int(blk), int(split), _p(rows), rows.size,
-        _p(out), _p(lse), _p(tb))
+    dsp = _p(None if ds is None else _c(ds, np.float32))
+    args = (_p(qc), _p(_c(qs, np.float32)), _p(kc), _p(_c(ks, np.float32)), _p(vc),
+            _p(_c(vs, np.float32)))
+    tail = (_p(None if mu_v is None else _c(mu_v, np.float32)), nq, nkv, d,
+            float(sm_scale), int(causal), int(bkv), int(blk), int(split), _p(rows), rows.size,
+            _p(out), _p(lse), _p(tb))
+    if ds_rows:
+        lib().orc_attn_recipe_rows_blockds(*args, dsp, int(ds_rows), *tail)
+    else:
+        lib().orc_attn_recipe_rows(*args, dsp, *tail)
     return (out, lse, tb) if tie else (out, lse)
 
 
@@ -442,23 +449,11 @@ def forward_rows(prob: Problem, pre: Prepass, rows=None, bkv: int = 128,
         s, h = u
         nq = prob.seqs[s][0]
         r = np.arange(nq) if rows is None else np.asarray(rows[s])
-        if prob.smooth_q == "block":
-            # each query block has its own compensation: its rows in one call each
-            blocks = r // prob.qk_block
-            parts = {b: one_rows(s, h, r[blocks == b], pre.ds[s][h][b]) for b in np.unique(blocks)}
-            d = prob.d
-            out = np.empty((len(r), d), np.float32)
-            lse = np.empty(len(r), np.float32)
-            tb = np.empty((len(r), d), np.float32) if tie else None
-            for b, res in parts.items():
-                sel = blocks == b
-                out[sel], lse[sel] = res[0], res[1]
-                if tie:
-                    tb[sel] = res[2]
-            return (out, lse, tb) if tie else (out, lse)
-        return one_rows(s, h, r, None if pre.ds[s] is None else pre.ds[s][h])
+        # per-block Q smoothing: ds is [Q blocks, nkv], row i takes block i / qk_block
+        ds_rows = prob.qk_block if prob.smooth_q == "block" else 0
+        return one_rows(s, h, r, None if pre.ds[s] is None else pre.ds[s][h], ds_rows)
 
-    def one_rows(s, h, r, ds):
+    def one_rows(s, h, r, ds, ds_rows=0):
         hk = h // G
         mu_v = None if pre.mu_v[s] is None else pre.mu_v[s][hk]
         if prob.pv_mode == "half":
@@ -469,7 +464,7 @@ def forward_rows(prob: Problem, pre: Prepass, rows=None, bkv: int = 128,
         return attn_recipe_rows(pre.qc[s][h], pre.qs[s][h], pre.kc[s][hk], pre.ks[s][hk],
                                 pre.vc[s][hk], pre.vs[s][hk], ds, mu_v,
                                 prob.scale, prob.causal, bkv, r, prob.kv_split, prob.qk_block,
-                                tie=tie)
+                                tie=tie, ds_rows=ds_rows)
 
     with ThreadPoolExecutor(max_workers=threads or os.cpu_count()) as ex:
         res = list(ex.map(one, units))

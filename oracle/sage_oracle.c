@@ -368,7 +368,9 @@ static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
  *   vdec        : the decoded V operand [nkv][d] (exact in FP32)
  *   out_scale   : FP32 [d] factor applied to acc at the end, or NULL (1)
  *   p_mode      : how p becomes the P.V operand (P_FP8 or P_F16 / P_BF16)
- *   delta_s     : FP32 [nkv] Q-smoothing compensation, or NULL
+ *   delta_s     : FP32 [nkv] Q-smoothing compensation, or NULL; with
+ *                 ds_rows > 0, FP32 [ceil(nq/ds_rows)][nkv]: row i takes
+ *                 row i / ds_rows (one compensation per Q block)
  *   mu_v        : FP32 [d] V mean to add back at the output, or NULL
  *   bkv         : key-tile width of the online softmax (p^ depends on it)
  *   split       : keys per split (a multiple of bkv), or 0 for one split
@@ -444,7 +446,8 @@ static float p_operand(float p, int p_mode) {
 
 static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc,
                         const float* k_scale, const float* vdec, const float* out_scale,
-                        int p_mode, const float* delta_s, const float* mu_v, int64_t nq,
+                        int p_mode, const float* delta_s_all, int64_t ds_rows,
+                        const float* mu_v, int64_t nq,
                         int64_t nkv, int d, float sm_scale, int causal, int bkv, int blk,
                         int64_t split, const int64_t* rows, int64_t nrows, float* out,
                         float* lse, float* tie) {
@@ -462,6 +465,8 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
         int64_t i = rows[r];
         int64_t jmax = last_visible(i, nq, nkv, causal);
         float sq = q_scale[i / blk];
+        const float* delta_s =
+            delta_s_all && ds_rows > 0 ? delta_s_all + (i / ds_rows) * nkv : delta_s_all;
         for (int64_t sp = 0; sp < nsplit; ++sp) {
             float* a = accs + sp * d;
             float* ta = ties + sp * d;
@@ -570,8 +575,28 @@ ORC_EXPORT void orc_attn_recipe_rows(const int8_t* qc, const float* q_scale,
     float* fac = (float*)malloc(sizeof(float) * (size_t)d);
     for (int64_t j = 0; j < nkv * d; ++j) vdec[j] = orc_e4m3_decode(vc[j]);
     for (int c = 0; c < d; ++c) fac[c] = v_scale[c] / 448.0f;
-    recipe_rows(qc, q_scale, kc, k_scale, vdec, fac, P_FP8, delta_s, mu_v, nq, nkv, d, sm_scale,
+    recipe_rows(qc, q_scale, kc, k_scale, vdec, fac, P_FP8, delta_s, 0, mu_v, nq, nkv, d, sm_scale,
                 causal, bkv, blk, split, rows, nrows, out, lse, tie);
+    free(vdec);
+    free(fac);
+}
+
+/* The same with one compensation per Q block (per-block Q smoothing):
+ * delta_s is FP32 [ceil(nq/ds_rows)][nkv] and row i takes row i / ds_rows. */
+ORC_EXPORT void orc_attn_recipe_rows_blockds(const int8_t* qc, const float* q_scale,
+                                             const int8_t* kc, const float* k_scale,
+                                             const uint8_t* vc, const float* v_scale,
+                                             const float* delta_s, int64_t ds_rows,
+                                             const float* mu_v, int64_t nq, int64_t nkv, int d,
+                                             float sm_scale, int causal, int bkv, int blk,
+                                             int64_t split, const int64_t* rows, int64_t nrows,
+                                             float* out, float* lse, float* tie) {
+    float* vdec = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1) * (size_t)d);
+    float* fac = (float*)malloc(sizeof(float) * (size_t)d);
+    for (int64_t j = 0; j < nkv * d; ++j) vdec[j] = orc_e4m3_decode(vc[j]);
+    for (int c = 0; c < d; ++c) fac[c] = v_scale[c] / 448.0f;
+    recipe_rows(qc, q_scale, kc, k_scale, vdec, fac, P_FP8, delta_s, ds_rows, mu_v, nq, nkv, d,
+                sm_scale, causal, bkv, blk, split, rows, nrows, out, lse, tie);
     free(vdec);
     free(fac);
 }
@@ -594,7 +619,7 @@ ORC_EXPORT void orc_attn_recipe_half_rows(const int8_t* qc, const float* q_scale
     float* vdec = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1) * (size_t)d);
     for (int64_t j = 0; j < nkv * d; ++j)
         vdec[j] = bf16 ? orc_bf16_decode(vh[j]) : orc_f16_decode(vh[j]);
-    recipe_rows(qc, q_scale, kc, k_scale, vdec, NULL, bf16 ? P_BF16 : P_F16, delta_s, mu_v, nq,
+    recipe_rows(qc, q_scale, kc, k_scale, vdec, NULL, bf16 ? P_BF16 : P_F16, delta_s, 0, mu_v, nq,
                 nkv, d, sm_scale, causal, bkv, blk, split, rows, nrows, out, lse, tie);
     free(vdec);
 }
