@@ -390,28 +390,19 @@ static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
  *
  * Rounding-tie bound.  p^ is a code picked by rounding p (times 448 for E4M3)
  * in FP32.  The plain FP32 evaluations of the exponent (another order of its
- * products, log2 units, a hardware exp2 within an ulp) move p by a few parts
- * in 2^24 of the terms' magnitudes, so where p lies that close to a rounding
- * midpoint of the operand format both neighbouring codes are correct results
- * of the recipe.  For each such key (relative distance to the midpoint below
- * tie_window) the bound adds one code step times |v| per channel, carried
- * through the rescales and the split merge like acc, and scaled like the
- * output (out_scale / L).  Everywhere else it is 0. */
+ * products, log2 units, a hardware exp2 within an ulp, a row maximum taken a
+ * few units in its last place higher) move p by a few parts in 2^24 of the
+ * terms' magnitudes, so every code that p rounds to within that window
+ * (tie_window, relative) is a correct result of the recipe.  Per key the
+ * bound adds the spread of those codes (the largest minus the smallest)
+ * times |v| per channel, carried through the rescales and the split merge
+ * like acc, and scaled like the output (out_scale / L).  The spread is one
+ * code step where a rounding midpoint lies within the window and 0 where
+ * none does; where the scores are so large that the window itself spans
+ * several codes (a row maximum of 2^16 or more in log2 units, whose own unit
+ * in the last place is then 2^-7 or coarser), it spans them all, the top
+ * code 448 included. */
 enum { P_FP8 = 0, P_F16 = 1, P_BF16 = 2 };
-
-/* Spacing of the operand format's representable values at x >= 0 (x in the
- * format's own units: p*448 for E4M3, p for fp16/bf16). */
-static double operand_step(double x, int p_mode) {
-    int e;
-    if (x <= 0.0) x = 0.0;
-    frexp(x, &e);                       /* x in [2^(e-1), 2^e) */
-    e -= 1;
-    switch (p_mode) {
-    case P_FP8:  return e < -6 ? ldexp(1.0, -9) : ldexp(1.0, e - 3);
-    case P_F16:  return e < -14 ? ldexp(1.0, -24) : ldexp(1.0, e - 10);
-    default:     return e < -126 ? ldexp(1.0, -133) : ldexp(1.0, e - 7);
-    }
-}
 
 /* Relative window within which a rounding midpoint counts as a tie: twice the
  * unit roundoff per rounding, six roundings per term, over the magnitudes of
@@ -422,18 +413,25 @@ static double tie_window(double terms, double m) {
     return ldexp(1.0, -23) * (6.0 * (terms + fabs(m)) + 16.0);
 }
 
-/* One code step of p's operand if p lies within the window of a rounding
- * midpoint, else 0 (in the operand's units, as p_operand returns it). */
+/* The operand format's value nearest x >= 0 in the format's own units (p*448
+ * for E4M3, saturating at 448; p for fp16/bf16), round to nearest even. */
+static double operand_round(double x, int p_mode) {
+    const float f = (float)x;
+    switch (p_mode) {
+    case P_FP8: return orc_e4m3_decode(orc_e4m3_encode_sat(f));
+    case P_F16: return orc_f16_decode(orc_f16_encode(f));
+    default:    return orc_bf16_decode(orc_bf16_encode(f));
+    }
+}
+
+/* Spread of p's operand over the window: the code of p moved up by the
+ * window less the code of p moved down by it (in the operand's units, as
+ * p_operand returns it). */
 static float tie_step(float p, int p_mode, double window) {
-    double x = p_mode == P_FP8 ? (double)(p * 448.0f) : (double)p;
+    const double x = p_mode == P_FP8 ? (double)(p * 448.0f) : (double)p;
     if (x <= 0.0) return 0.0f;
-    if (p_mode == P_FP8 && x >= 448.0) return 0.0f;        /* saturated top code */
-    /* the nearest midpoint within the window is the one of x's own binade:
-       the others lie at least a quarter step away */
-    double st = operand_step(x, p_mode);
-    double mid = floor(x / st) * st + 0.5 * st;
-    if (fabs(x - mid) > window * x) return 0.0f;
-    return (float)st;
+    const double lo = window < 1.0 ? x * (1.0 - window) : 0.0;
+    return (float)(operand_round(x * (1.0 + window), p_mode) - operand_round(lo, p_mode));
 }
 
 static float p_operand(float p, int p_mode) {

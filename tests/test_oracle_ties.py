@@ -15,7 +15,13 @@ output element, what such re-roundings can move it.  The checks:
 * the bound is zero on rows with no near-midpoint p, and such rows are few;
 * a row whose dominant key has p*448 just above an E4M3 midpoint (200,
   between the codes 192 and 208): the other code would move the row by more
-  than the 2e-2 bar, and the bound covers it.
+  than the 2e-2 bar, and the bound covers it;
+* logits of 10^6 and more (Q and K scaled up a thousandfold): there the row
+  maximum's own unit in the last place reaches 2^-3 .. 2^-1 (log2 units), so
+  the kernel's order lifts some exponents above log2 464 (where the hardware
+  E4M3 convert gives the NaN code) unless the maximum is raised first; with
+  the raise none is lifted, and the bound, whose window now spans several
+  codes (the top code 448 included), covers what the other codes move.
 """
 import math
 
@@ -54,6 +60,59 @@ def _codes_kernel_order(orc, S, sq, ks_row, sm):
     nm = (F32(math.log2(448.0)) - y.max(axis=1, keepdims=True)).astype(F32)
     x = (S.astype(np.float64) * c.astype(np.float64) + nm.astype(np.float64)).astype(F32)
     return orc.e4m3_encode(np.exp2(x.astype(np.float64)).astype(F32)).reshape(S.shape)
+
+
+def _codes_kernel_order_raised(orc, S, sq, ks_row, sm, raise_max=True):
+    """The kernel's order with its row-maximum raise: where |m2| >= 2^16 (log2
+    units), m2 = fl(m2 + 6*2^-23*(|m2| - 2^16)) before nm is formed.  Returns
+    the codes and the exponents x (FP32)."""
+    c = ((F32(1) * sq[:, None]).astype(F32) * ks_row[None, :]).astype(F32)
+    c = (c * F32(sm * math.log2(math.e))).astype(F32)
+    y = (S.astype(F32) * c).astype(F32)
+    m2 = y.max(axis=1, keepdims=True).astype(F32)
+    if raise_max:
+        d = np.maximum(np.abs(m2) - F32(65536.0), F32(0.0)).astype(F32)
+        m2 = (d.astype(np.float64) * (6.0 * 2.0 ** -23) + m2.astype(np.float64)).astype(F32)
+    nm = (F32(math.log2(448.0)) - m2).astype(F32)
+    x = (S.astype(np.float64) * c.astype(np.float64) + nm.astype(np.float64)).astype(F32)
+    return orc.e4m3_encode(np.exp2(x.astype(np.float64)).astype(F32)).reshape(S.shape), x
+
+
+def test_bound_covers_the_kernel_order_at_large_logits(orc):
+    import torch
+    w = synth.Workload(name="big", dtype="f16", layout="HND", B=1, Hq=4, Hkv=4, Nq=1024,
+                       Nkv=128, d=128, smooth_k=True, seed=17, k_off_sigma=2.0,
+                       qv_mean_sigma=1.0)
+    prob = orc.problem_from_workload(w, "fp8", 0, 64)
+    q, k, v, _ = synth.make_inputs(w, device="cpu")
+    q = (q.float() * 1000).to(torch.float16)
+    k = (k.float() * 1000).to(torch.float16)
+    u = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    pre = orc.prepass(prob, u(q), u(k), u(v))
+    _, _, tie = orc.forward_rows(prob, pre, bkv=128, tie=True)
+    lim = math.log2(464.0)
+    over_plain = flips = 0
+    for h in range(w.Hq):
+        qc, qs = pre.qc[0][h], pre.qs[0][h]
+        kc, ks, vc, vs = pre.kc[0][h], pre.ks[0][h], pre.vc[0][h], pre.vs[0][h]
+        vdec = orc.e4m3_decode(vc).astype(np.float64).reshape(vc.shape)
+        ks_row = ks[np.arange(w.Nkv) // 64].astype(F32)
+        sq = qs[np.arange(w.Nq) // 64].astype(F32)
+        S = qc.astype(np.int64) @ kc.astype(np.int64).T
+        co, p = _codes_oracle_order(orc, S, sq, ks_row, prob.scale)
+        _, x_plain = _codes_kernel_order_raised(orc, S, sq, ks_row, prob.scale, False)
+        ck, x = _codes_kernel_order_raised(orc, S, sq, ks_row, prob.scale)
+        over_plain += int((x_plain > lim).sum())
+        assert np.all(x <= math.log2(448.0) + 1e-6)       # no code above 448
+        for i in np.nonzero((co != ck).any(axis=1))[0]:
+            diff = np.nonzero(co[i] != ck[i])[0]
+            flips += diff.size
+            L = float(p[i].astype(np.float64).sum())
+            dp = (orc.e4m3_decode(ck[i, diff]).astype(np.float64)
+                  - orc.e4m3_decode(co[i, diff]))
+            delta = (dp @ vdec[diff]) * vs.astype(np.float64) / 448.0 / L
+            assert np.all(np.abs(delta) <= tie[0][h, i] * (1 + 1e-4) + 1e-7), (h, i, diff)
+    assert over_plain > 0 and flips > 0
 
 
 def test_bound_covers_other_evaluation_orders(orc):
