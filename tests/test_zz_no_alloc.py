@@ -1,6 +1,6 @@
 """The allocation-free entry point sage_attn_fwd_noalloc (the library's own
 static workspace) against sage_attn_fwd with a caller workspace, through the
-C ABI: two calls in a row on one GPU, the second with a smaller problem, each
+C ABI: calls in a row on one GPU, each with a smaller problem than the last, each
 bit for bit equal (output and log-sum-exp) to the workspace entry point's
 result on the same inputs, and a problem whose workspace exceeds the static
 array refused with SAGE_ERR_WORKSPACE."""
@@ -18,9 +18,13 @@ def _lse_like(w, q):
 
 
 def test_noalloc_matches_workspace_entry_twice():
+    # each call smaller than the one before; the last one smooths Q per block,
+    # which places the block means and deviation codes in the static array too
     cases = [synth.WORKLOADS["causal_gqa"],
              synth.scaled_down(synth.WORKLOADS["video_dit"], Hq=4, Hkv=4, Nq=700, Nkv=900,
-                               d=128, layout="HND", seed=31)]
+                               d=128, layout="HND", seed=31),
+             synth.scaled_down(synth.WORKLOADS["video_dit_block"], Hq=2, Hkv=2, Nq=600, Nkv=500,
+                               seed=32)]
     for w in cases:
         pu.say(f"[noalloc] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nkv={w.Nkv} d={w.d}")
         q, k, v, meta = pu.gpu_inputs(w)
