@@ -409,20 +409,18 @@ __device__ inline float swap_sum(float x) {
 // by the FP32 roundings of m (a product), of m - log2 448 and of the
 // exponent's FMA: up to three units in the last place of m.  Below |m| = 2^16
 // that is under 0.024, and 2^x stays below 464, where v_cvt_pk_fp8_f32 turns
-// from the top code 448 to the NaN code; above, it could reach the NaN code.
+// from the top code 448 to the NaN code; above, it could reach the NaN code
+// (and, with a 16-bit P, whose exponent has no 448 in it, p could overflow
+// once the unit in the last place of m is large).
 // There m is raised by 6 * 2^-23 * (|m| - 2^16), at least three units in its
 // last place from 2^17 on, which keeps every exponent at or below log2 448:
 // the softmax is the same for any m at or above the row's largest score, and
 // the rescale factors, l and the LSE follow the raised m.  Below 2^16 the
 // raise is exactly 0 (m unchanged); a row with no visible key yet (m = -inf)
 // keeps -inf (the clamp of d to 2^100).  Three VALU instructions per tile.
-template <bool ON>
 __device__ inline float raise_max(float m) {
-    if constexpr (ON) {
-        const float d = __builtin_amdgcn_fmed3f(fabsf(m) - 65536.0f, 0.0f, 0x1p100f);
-        m = fmaf(d, 6.0f * 0x1p-23f, m);
-    }
-    return m;
+    const float d = __builtin_amdgcn_fmed3f(fabsf(m) - 65536.0f, 0.0f, 0x1p100f);
+    return fmaf(d, 6.0f * 0x1p-23f, m);
 }
 
 // Online softmax of one tile, in two halves so that the fused kernel can run
@@ -493,7 +491,7 @@ __device__ inline float score_exp(v16i* sacc, float (&p)[4][16], float c0, float
         }
         // (raised per lane before the two halves of the row meet: the raise
         // grows with m, so the row's maximum is raised as a whole)
-        m_new = fmaxf(m_run, swap_max(raise_max<!PVH>(fm)));
+        m_new = fmaxf(m_run, swap_max(raise_max(fm)));
         const float nm = POFF - (m_new == -INFINITY ? 0.0f : m_new);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -516,7 +514,7 @@ __device__ inline float score_exp(v16i* sacc, float (&p)[4][16], float c0, float
                 mt = fmaxf(mt, y);
             }
         }
-        m_new = fmaxf(m_run, swap_max(raise_max<!PVH>(mt * sml2)));
+        m_new = fmaxf(m_run, swap_max(raise_max(mt * sml2)));
         const float nm = POFF - (m_new == -INFINITY ? 0.0f : m_new);
 #pragma unroll
         for (int b = 0; b < 4; ++b)

@@ -3,13 +3,14 @@
 The seeded inputs of a small causal GQA problem (and of a bf16 one) are
 rescaled or partly zeroed on the GPU, and both sides see the same bits:
 
-* large: Q and K scaled up (fp16 by 30 and 500, bf16 by 300), so that the
+* large: Q and K scaled up (fp16 by 30 and 500, bf16 by 300; the fp16 x500
+  case also with the 16-bit P.V variant), so that the
   logits reach 10^3 .. 2*10^6 and each row's softmax is nearly one-hot; row
   maxima up to 2^21.4 in log2 units, where the FP32 roundings of the
   exponent could lift the top P code past the E4M3 convert's headroom (to
   the NaN code) unless the kernel raises the maximum first;
 * tiny: Q, K and V scaled down to 10^-3 and 10^-5 of their size (fp16
-  subnormals included), so that the scales are of order 10^-9 and the
+  subnormals included; bf16 with the 16-bit P.V variant too), so that the scales are of order 10^-9 and the
   softmax is nearly uniform;
 * zero blocks: one 64-token Q block, one 64-token K block (no K smoothing)
   and one V channel all zero: their scales and codes are 0;
@@ -20,7 +21,8 @@ Beyond row maxima of 2^22 (log2 units; logits of about 3*10^6) one unit in
 the last place of the maximum exceeds half a unit of the exponent, so no
 FP32 evaluation of the exponent can place P on the E4M3 scale and the
 recipe's output there is not defined; the case "beyond_range" (bf16 scaled
-by 10^4, maxima near 2^31) checks only that no NaN comes out.
+by 10^4, maxima near 2^31, both P.V variants) checks only that no NaN comes
+out.
 
 Each case in range checks the pre-pass bit for bit, every output element finite,
 the output within max-abs 2e-2 (beyond the oracle's rounding-tie bound) and
@@ -67,10 +69,12 @@ def _constant_keys(q, k, v):
 
 
 CASES = {
-    # (workload, transform, compare with exact FP64)
+    # (workload, transform, compare with exact FP64[, P.V mode])
     "large_x30_f16": (BASE, _scaled(30.0, 30.0, 1.0), False),
     "large_x500_f16": (BASE, _scaled(500.0, 500.0, 1.0), False),
     "large_x300_bf16": (BASE_BF16, _scaled(300.0, 300.0, 1.0), False),
+    "large_x500_f16_pv_half": (BASE, _scaled(500.0, 500.0, 1.0), False, "half"),
+    "tiny_1e-5_bf16_pv_half": (BASE_BF16, _scaled(1e-5, 1e-5, 1e-5), True, "half"),
     "tiny_1e-3_f16": (BASE, _scaled(1e-3, 1e-3, 1e-3), True),
     "tiny_1e-5_f16_subnormal": (BASE, _scaled(1e-5, 1e-5, 1e-5), True),
     "zero_blocks": (R(BASE, smooth_k=False), _zero_blocks, True),
@@ -81,41 +85,42 @@ CASES = {
 @pytest.fixture(scope="module", params=list(CASES))
 def case(request):
     name = request.param
-    w, fn, exact = CASES[name]
-    pu.say(f"[edge values {name}] {w}")
+    w, fn, exact, pv = (CASES[name] + ("fp8",))[:4]
+    pu.say(f"[edge values {name}] {w} pv={pv}")
     q, k, v, meta = pu.gpu_inputs(w)
     q, k, v = fn(q, k, v)
     torch.cuda.synchronize()
-    prob = orc.problem_from_workload(w)
+    prob = orc.problem_from_workload(w, pv)
     ref = orc.prepass(prob, pu.u16(q), pu.u16(k), pu.u16(v))
-    return name, w, exact, q, k, v, meta, prob, ref
+    return name, w, exact, pv, q, k, v, meta, prob, ref
 
 
 def test_prepass_bit_exact(case):
-    name, w, exact, q, k, v, meta, prob, ref = case
+    name, w, exact, pv, q, k, v, meta, prob, ref = case
     pu.say(f"[edge prepass {name}]")
-    bufs = pu.run_quant(w, q, k, v, meta)
+    bufs = pu.run_quant(w, q, k, v, meta, pv=pv)
     torch.cuda.synchronize()
-    gpu, pads_ok = pu.unpack_quant(w, bufs)
+    gpu, pads_ok = pu.unpack_quant(w, bufs, pv=pv)
     assert pads_ok
     pu.assert_prepass_equal(gpu, ref, w)
 
 
-def test_beyond_range_gives_no_nan():
+@pytest.mark.parametrize("pv", ["fp8", "half"])
+def test_beyond_range_gives_no_nan(pv):
     w = BASE_BF16
-    pu.say("[edge beyond range: bf16 x 1e4]")
+    pu.say(f"[edge beyond range: bf16 x 1e4, pv={pv}]")
     q, k, v, meta = pu.gpu_inputs(w)
     q, k, v = _scaled(1e4, 1e4, 1.0)(q, k, v)
-    o, lse = pu.run_fwd(w, q, k, v, meta)
+    o, lse = pu.run_fwd(w, q, k, v, meta, pv=pv)
     torch.cuda.synchronize()
     assert not torch.isnan(o.float()).any()
     assert not torch.isnan(lse).any()
 
 
 def test_forward_matches_oracle(case):
-    name, w, exact, q, k, v, meta, prob, ref = case
+    name, w, exact, pv, q, k, v, meta, prob, ref = case
     pu.say(f"[edge forward {name}]")
-    o, lse = pu.run_fwd(w, q, k, v, meta)
+    o, lse = pu.run_fwd(w, q, k, v, meta, pv=pv)
     torch.cuda.synchronize()
     got = pu.gpu_out_per_seq(w, o, meta)
     rec, rec_lse, tie = orc.forward_rows(prob, ref, bkv=pu.KVT, tie=True)
