@@ -183,12 +183,24 @@ ORC_EXPORT void orc_smooth(const float* x, const float* mu, int64_t n, int d, fl
             xs[t * d + c] = mu ? x[t * d + c] - mu[c] : x[t * d + c];
 }
 
+/* The quotients k/a of the quantizers below (k = 127, 448 or 16256 over an
+   absmax a) leave the FP32 range once a falls below k/FLT_MAX, about
+   10^-36 .. 10^-34 (reachable with bf16 inputs); the inverse scale would be
+   infinite and the codes sign-only (and NaN for zeros).  For the INT8 Q/K
+   blocks and the 15-bit deviation code, where a < 2^-100 the values and a
+   are therefore scaled by 2^64 before the quotient: exact there (subnormals
+   included), and the codes are then those the same block gets at any other
+   power-of-two scale.  Above 2^-100 the factor is 1 and changes nothing.
+   (V channels that small count as zero instead: orc_quant_fp8_channels.)   */
+static float tiny_rescale(float a) { return a < 0x1p-100f ? 0x1p64f : 1.0f; }
+
 /* Per-block symmetric INT8 quantization (block size, absmax scale, rounding
    and the zero block are readings where the pages are silent): blocks of `blk` tokens
    aligned to the sequence start (the last one may be short).  a = max |x_s|
    over the block; a == 0 gives scale 0 and zero codes; otherwise
    inv = fl32(127/a), scale = fl32(a/127), code = clamp(rne(fl32(x_s*inv)),
-   -127, 127).  codes: [n][d]; scales: [ceil(n/blk)].                        */
+   -127, 127) (with the rescale of tiny_rescale: inv = fl32(127/(a*r)),
+   code from fl32((x_s*r)*inv)).  codes: [n][d]; scales: [ceil(n/blk)].      */
 ORC_EXPORT void orc_quant_int8_blocks(const float* xs, int64_t n, int d, int blk,
                                       int8_t* codes, float* scales) {
     for (int64_t b0 = 0, bi = 0; b0 < n; b0 += blk, ++bi) {
@@ -205,11 +217,12 @@ ORC_EXPORT void orc_quant_int8_blocks(const float* xs, int64_t n, int d, int blk
                 for (int c = 0; c < d; ++c) codes[t * d + c] = 0;
             continue;
         }
-        float inv = 127.0f / a;
+        const float r = tiny_rescale(a);
+        float inv = 127.0f / (a * r);
         scales[bi] = a / 127.0f;
         for (int64_t t = b0; t < b1; ++t)
             for (int c = 0; c < d; ++c) {
-                float y = xs[t * d + c] * inv;
+                float y = (xs[t * d + c] * r) * inv;
                 float r = nearbyintf(y);                      /* RNE         */
                 if (r > 127.0f) r = 127.0f;
                 if (r < -127.0f) r = -127.0f;
@@ -221,8 +234,10 @@ ORC_EXPORT void orc_quant_int8_blocks(const float* xs, int64_t n, int d, int blk
 /* Per-channel FP8 E4M3 quantization of (smoothed) V (per channel: a V scale
    must be constant along the contracted token axis): per
    channel c, a = max over the n tokens of |v_s|; a == 0 gives scale 0 and
-   zero codes; otherwise inv = fl32(448/a), scale = fl32(a/448) and
-   code = e4m3_rne_sat(fl32(v_s*inv)).  codes: [n][d]; scales: [d].          */
+   zero codes, and so does a < 2^-100 (a channel that small counts as zero:
+   the output moves by less than 2^-100); otherwise inv = fl32(448/a),
+   scale = fl32(a/448) and code = e4m3_rne_sat(fl32(v_s*inv)).
+   codes: [n][d]; scales: [d].                                               */
 ORC_EXPORT void orc_quant_fp8_channels(const float* vs, int64_t n, int d,
                                        uint8_t* codes, float* scales) {
     for (int c = 0; c < d; ++c) {
@@ -231,7 +246,7 @@ ORC_EXPORT void orc_quant_fp8_channels(const float* vs, int64_t n, int d,
             float v = fabsf(vs[t * d + c]);
             if (v > a) a = v;
         }
-        if (a == 0.0f) {
+        if (a < 0x1p-100f) {
             scales[c] = 0.0f;
             for (int64_t t = 0; t < n; ++t) codes[t * d + c] = 0;
             continue;
@@ -292,7 +307,8 @@ ORC_EXPORT void orc_smooth_blocks(const float* x, const float* mu, int64_t n, in
    gives scale 0 and zero codes; otherwise inv = fl32(16256/a),
    scale = fl32(a/16256) (16256 = 127*128), and per channel y = fl32(x_c*inv),
    hi = clamp(rne(y/128), -127, 127), lo = rne(y - 128*hi) (|lo| <= 64), so
-   that x_c ~ scale*(128*hi + lo) within scale/2.  hi, lo: [d] int8.        */
+   that x_c ~ scale*(128*hi + lo) within scale/2 (tiny_rescale as for INT8).
+   hi, lo: [d] int8.                                                         */
 ORC_EXPORT void orc_mu_code(const float* x, int d, int8_t* hi, int8_t* lo, float* scale) {
     float a = 0.0f;
     for (int c = 0; c < d; ++c) {
@@ -304,10 +320,11 @@ ORC_EXPORT void orc_mu_code(const float* x, int d, int8_t* hi, int8_t* lo, float
         for (int c = 0; c < d; ++c) hi[c] = lo[c] = 0;
         return;
     }
-    float inv = 16256.0f / a;
+    const float r = tiny_rescale(a);
+    float inv = 16256.0f / (a * r);
     *scale = a / 16256.0f;
     for (int c = 0; c < d; ++c) {
-        float y = x[c] * inv;
+        float y = (x[c] * r) * inv;
         float h = nearbyintf(y / 128.0f);                  /* exact scaling */
         if (h > 127.0f) h = 127.0f;
         if (h < -127.0f) h = -127.0f;

@@ -21,7 +21,15 @@
 //   int8  : a = max|x_s|, inv = 127/a, scale = a/127, code = rne(x_s*inv)
 //           clamped to [-127, 127]; a == 0 -> scale 0, codes 0;
 //   e4m3  : a = max over tokens |v_s|, inv = 448/a, scale = a/448,
-//           code = rne_e4m3(v_s*inv) (hardware convert, round to nearest even).
+//           code = rne_e4m3(v_s*inv) (hardware convert, round to nearest even);
+//   tiny a: where a < 2^-100 the quotients 127/a and 16256/a could leave
+//           the FP32 range (a below about 10^-36, bf16 inputs), so the values
+//           and a are scaled by 2^64 first (tiny_rescale: exact there, and the
+//           codes are those of the block at any power-of-two scale); a V
+//           channel that small counts as zero (scale 0, codes 0: the output
+//           moves by less than 2^-100).
+#include <type_traits>
+
 #include "sage_internal.h"
 
 #pragma clang fp contract(off)
@@ -49,6 +57,8 @@ __device__ inline void load8(const uint16_t* p, float* out) {
         out[2 * i + 1] = h2f<DT>((uint16_t)(w[i] >> 16));
     }
 }
+
+__device__ inline float tiny_rescale(float a) { return a < 0x1p-100f ? 0x1p64f : 1.0f; }
 
 __device__ inline float wave_max(float v) {
 #pragma unroll
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(WG) void k_stats(KParams P, StatJobs J) {
 // ---------------------------------------------------------------------------
 // Finalize per (sequence, head, channel).  STAT_SUM: mu = (chunk sums added in
 // chunk order) / n.  STAT_ABSMAX: amax = max of the chunk maxima and
-// scale = amax / 448.  A workgroup owns FIN_CH channels of one (sequence,
+// scale = amax / 448 (0 below 2^-100).  A workgroup owns FIN_CH channels of one (sequence,
 // head): it copies up to FIN_ROUND chunks of their partials into LDS with
 // every load in flight at once, transposed so that each channel's values are
 // contiguous, and thread c then combines channel c's values strictly in chunk
@@ -251,7 +261,8 @@ __device__ inline void finalize_one(const KParams& P, const FinJob& J, int blk, 
         J.out_mu[o] = n > 0 ? acc / (float)n : 0.0f;
     } else {
         J.out_amax[o] = acc;
-        J.out_scale[o] = acc / 448.0f;
+        // a channel below 2^-100 counts as zero (its codes are 0 as well)
+        J.out_scale[o] = acc >= 0x1p-100f ? acc / 448.0f : 0.0f;
     }
 }
 
@@ -369,13 +380,14 @@ __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restri
                 dv[k] = (c < D && nvalid > 0) ? mub_lds[wv * D + c] - mb[c] : 0.0f;
             }
             const float a = wave_max(fmaxf(fabsf(dv[0]), fabsf(dv[1])));
-            const float inv = a > 0.0f ? 16256.0f / a : 0.0f;
+            const float rs = tiny_rescale(a);
+            const float inv = a > 0.0f ? 16256.0f / (a * rs) : 0.0f;
             const int64_t ib = row0 / QB + blk * NSUB + wv;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int c = lane + 64 * k;
                 if (c < D) {
-                    const float y = dv[k] * inv;
+                    const float y = (dv[k] * rs) * inv;
                     const float hi = fminf(fmaxf(rintf(y * 0.0078125f), -127.0f), 127.0f);
                     const float lo = rintf(y - 128.0f * hi);
                     bq.code[ib * 2 * D + c] = (int8_t)(int)hi;
@@ -421,34 +433,45 @@ __device__ inline void quant_qk_block(const KParams& P, const uint16_t* __restri
         if ((threadIdx.x & 63) == 0) red[k * (WG / 64) + (threadIdx.x >> 6)] = wm;
     }
     __syncthreads();
-    float a[NSUB], inv[NSUB];
+    float a[NSUB], inv[NSUB], rs[NSUB];
 #pragma unroll
     for (int k = 0; k < NSUB; ++k) {
         a[k] = red[k * (WG / 64)];
 #pragma unroll
         for (int w = 1; w < WG / 64; ++w) a[k] = fmaxf(a[k], red[k * (WG / 64) + w]);
-        inv[k] = a[k] > 0.0f ? 127.0f / a[k] : 0.0f;
+        rs[k] = tiny_rescale(a[k]);
+        inv[k] = a[k] > 0.0f ? 127.0f / (a[k] * rs[k]) : 0.0f;
     }
+    // the codes; the rescale of tiny blocks (block-uniform) in a copy of its
+    // own, so that other blocks run without it
+    auto emit = [&](auto tiny) {
+        constexpr bool TINY = decltype(tiny)::value;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int gi = threadIdx.x + i * WG;
-        if (gi >= NG) continue;
-        const int r = gi / GPR, cg = (gi % GPR) * 8;
-        const float inv_r = (NSUB == 1 || r < QB) ? inv[0] : inv[NSUB - 1];
-        uint32_t w0 = 0, w1 = 0;
+        for (int i = 0; i < PER; ++i) {
+            const int gi = threadIdx.x + i * WG;
+            if (gi >= NG) continue;
+            const int r = gi / GPR, cg = (gi % GPR) * 8;
+            const bool first = NSUB == 1 || r < QB;
+            const float inv_r = first ? inv[0] : inv[NSUB - 1];
+            const float rs_r = first ? rs[0] : rs[NSUB - 1];
+            uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float q = rintf(val[i][e] * inv_r);
-            q = fminf(fmaxf(q, -127.0f), 127.0f);
-            const uint32_t b = (uint32_t)(int32_t)q & 0xffu;
-            if (e < 4) w0 |= b << (8 * e); else w1 |= b << (8 * (e - 4));
+            for (int e = 0; e < 8; ++e) {
+                const float x = TINY ? val[i][e] * rs_r : val[i][e];
+                float q = rintf(x * inv_r);
+                q = fminf(fmaxf(q, -127.0f), 127.0f);
+                const uint32_t b = (uint32_t)(int32_t)q & 0xffu;
+                if (e < 4) w0 |= b << (8 * e); else w1 |= b << (8 * (e - 4));
+            }
+            *reinterpret_cast<uint2*>(codes + (row0 + blk * QBLK + r) * D + cg) = make_uint2(w0, w1);
+            if constexpr (DELTA) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ks_lds[r * D + cg + e] = val[i][e];
+            }
         }
-        *reinterpret_cast<uint2*>(codes + (row0 + blk * QBLK + r) * D + cg) = make_uint2(w0, w1);
-        if constexpr (DELTA) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ks_lds[r * D + cg + e] = val[i][e];
-        }
-    }
+    };
+    if (rs[0] != 1.0f || rs[NSUB - 1] != 1.0f) emit(std::true_type{});
+    else emit(std::false_type{});
     if (threadIdx.x < NSUB) {
         const float av = threadIdx.x == 0 ? a[0] : a[NSUB - 1];
         scales[row0 / QB + blk * NSUB + threadIdx.x] = av > 0.0f ? av / 127.0f : 0.0f;
@@ -541,7 +564,8 @@ __device__ inline void quant_v_chunk(const KParams& P, const uint16_t* __restric
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float a = amh[cg + e];
-            inv[e] = a > 0.0f ? 448.0f / a : 0.0f;
+            // below 2^-100 the channel counts as zero (its scale is 0 too)
+            inv[e] = a >= 0x1p-100f ? 448.0f / a : 0.0f;
             m8[e] = muh ? muh[cg + e] : 0.0f;
         }
         uint32_t word[8];

@@ -10,8 +10,12 @@ rescaled or partly zeroed on the GPU, and both sides see the same bits:
   exponent could lift the top P code past the E4M3 convert's headroom (to
   the NaN code) unless the kernel raises the maximum first;
 * tiny: Q, K and V scaled down to 10^-3 and 10^-5 of their size (fp16
-  subnormals included; bf16 with the 16-bit P.V variant too), so that the scales are of order 10^-9 and the
-  softmax is nearly uniform;
+  subnormals included; bf16 with the 16-bit P.V variant too), and bf16 Q
+  and K to 10^-38 (FP32 subnormals; absmaxes below 2^-100, where the INT8
+  quantizer rescales by 2^64 before forming 127/a, or the codes would be
+  sign-only), so that the scores are nearly zero and the softmax nearly
+  uniform; and V to 10^-38, whose channels (absmax below 2^-100) count as
+  zero in the E4M3 quantizer: the output is 0 on both sides;
 * zero blocks: one 64-token Q block, one 64-token K block (no K smoothing)
   and one V channel all zero: their scales and codes are 0;
 * constant keys: every key row equal, which K smoothing turns into all-zero
@@ -75,6 +79,8 @@ CASES = {
     "large_x300_bf16": (BASE_BF16, _scaled(300.0, 300.0, 1.0), False),
     "large_x500_f16_pv_half": (BASE, _scaled(500.0, 500.0, 1.0), False, "half"),
     "tiny_1e-5_bf16_pv_half": (BASE_BF16, _scaled(1e-5, 1e-5, 1e-5), True, "half"),
+    "tiny_qk_1e-38_bf16": (BASE_BF16, _scaled(1e-38, 1e-38, 1.0), True),
+    "tiny_qk_1e-38_bf16_pv_half": (BASE_BF16, _scaled(1e-38, 1e-38, 1.0), True, "half"),
     "tiny_1e-3_f16": (BASE, _scaled(1e-3, 1e-3, 1e-3), True),
     "tiny_1e-5_f16_subnormal": (BASE, _scaled(1e-5, 1e-5, 1e-5), True),
     "zero_blocks": (R(BASE, smooth_k=False), _zero_blocks, True),
@@ -103,6 +109,27 @@ def test_prepass_bit_exact(case):
     gpu, pads_ok = pu.unpack_quant(w, bufs, pv=pv)
     assert pads_ok
     pu.assert_prepass_equal(gpu, ref, w)
+
+
+def test_tiny_v_channels_count_as_zero():
+    w = BASE_BF16
+    pu.say("[edge tiny V: bf16 V x 1e-38]")
+    q, k, v, meta = pu.gpu_inputs(w)
+    q, k, v = _scaled(1.0, 1.0, 1e-38)(q, k, v)
+    prob = orc.problem_from_workload(w)
+    ref = orc.prepass(prob, pu.u16(q), pu.u16(k), pu.u16(v))
+    assert not any(x.any() for x in ref.vs) and not any(x.any() for x in ref.vc)
+    bufs = pu.run_quant(w, q, k, v, meta)
+    torch.cuda.synchronize()
+    gpu, pads_ok = pu.unpack_quant(w, bufs)
+    assert pads_ok
+    pu.assert_prepass_equal(gpu, ref, w)
+    o, lse = pu.run_fwd(w, q, k, v, meta)
+    torch.cuda.synchronize()
+    assert not o.float().abs().max().item()
+    _, rec_lse = orc.forward_rows(prob, ref, bkv=pu.KVT)
+    gl = lse.cpu().numpy()[0]
+    assert np.abs(gl - rec_lse[0]).max() < 2e-3 * max(1.0, np.abs(rec_lse[0]).max())
 
 
 @pytest.mark.parametrize("pv", ["fp8", "half"])

@@ -139,3 +139,36 @@ def test_smooth_is_exact_subtraction(orc):
     mu = np.array([0.5, 3.0], np.float32)
     assert np.array_equal(orc.smooth(x, mu), np.array([[0.5, -1.0], [2.5, 2.0]], np.float32))
     assert np.array_equal(orc.smooth(x, None), x)
+
+
+@pytest.mark.parametrize("k", [0, 40, 100, 110, 122, 126, 130])
+def test_quantizers_are_scale_invariant_down_to_tiny_blocks(orc, k):
+    # codes depend on x / a only, so scaling a block by 2^-k (exact for these
+    # small integers, subnormal results included) leaves every INT8 and
+    # deviation code as it is; below an absmax of about 10^-36 the plain
+    # quotient 127/a (16256/a) would overflow FP32 and give sign-only codes
+    # (NaN for zeros), which this catches.  Zeros stay zero codes.
+    rng = np.random.default_rng(k)
+    f = np.float32(2.0 ** -k)
+    x = rng.integers(-1000, 1001, size=(150, 16)).astype(np.float32)
+    x[3, :5] = 0.0
+    c0, s0 = orc.quant_int8_blocks(x, 64)
+    c1, s1 = orc.quant_int8_blocks(x * f, 64)
+    assert np.array_equal(c0, c1)
+    assert np.all(c1[3, :5] == 0)
+    # the scale is a/127 of the scaled block (subnormal where that is)
+    a1 = np.abs(x * f).reshape(-1)[:64 * 16].max()
+    assert s1[0] == np.float32(a1) / np.float32(127)
+    # V channels keep their codes down to an absmax of 2^-100 and count as
+    # zero below it (scale 0, codes 0)
+    v0, t0 = orc.quant_fp8_channels(x)
+    v1, t1 = orc.quant_fp8_channels(x * f)
+    amax = np.abs(x * f).max(axis=0)
+    keep = amax >= np.float32(2.0 ** -100)
+    assert np.array_equal(v0[:, keep], v1[:, keep])
+    assert not v1[:, ~keep].any() and not t1[~keep].any()
+    if k >= 110:
+        assert not keep.any()
+    h0, l0, _ = orc.mu_code(x[0])
+    h1, l1, _ = orc.mu_code(x[0] * f)
+    assert np.array_equal(h0, h1) and np.array_equal(l0, l1)
