@@ -10,13 +10,17 @@ Prints ONE JSON line.  Besides the standard fields it carries
   roofline     : the fused kernel (the dominant launch) against the dense
                  INT8/FP8 MFMA peak of MI355X (5.0 POPS): algorithmic ops
                  (4*d per visible (q, k) pair) per launch / its average
-                 duration.  The call is split into its two halves
+                 duration.  The call is split into two halves
                  (sage_quant_qkv, then sage_attn_fwd_quantized on the same
-                 buffers: the same launches as sage_attn_fwd), and each half
-                 is timed in a loop of its own with HIP events on the launch
-                 stream around the loop; kernel_ms is the fused kernel's
-                 half, prepass_ms the other, measured, not a difference, and
-                 halves_sum_ms their sum next to ms_per_step;
+                 buffers), and each half is timed in a loop of its own with
+                 HIP events on the launch stream around the loop; kernel_ms
+                 is the fused kernel's half, prepass_ms the other, measured,
+                 not a difference, and halves_sum_ms their sum next to
+                 ms_per_step.  Inside sage_attn_fwd the fused kernel
+                 quantizes Q itself in its prologue and the pre-pass skips
+                 Q, so the call is a little shorter than the halves' sum;
+                 kernel_ms is the same kernel reading the pre-pass's Q
+                 codes (its loop and softmax are the same);
   n32k         : the same figures for the long-context varlen workload at
                  d=128 (four packed sequences, keys up to 32768 per
                  sequence), the metric's N=32K point;

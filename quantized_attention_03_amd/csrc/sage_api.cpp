@@ -382,9 +382,11 @@ int stat_blocks(const KParams& k, bool is_q, int heads) {
     } while (0)
 
 // The pre-pass.  `bufs` are the destination tensors, `sc` the scratch area.
+// With skip_q the Q codes are left to the fused kernel (its means are still
+// formed here).
 sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype, const void* q,
                         const void* k, const void* v, const sage_quant_bufs& b, uint8_t* sc,
-                        const WsLayout& w, hipStream_t st) {
+                        const WsLayout& w, hipStream_t st, bool skip_q = false) {
     float* part_q = reinterpret_cast<float*>(sc + w.part_q);
     float* part_k = reinterpret_cast<float*>(sc + w.part_k);
     float* part_v = reinterpret_cast<float*>(sc + w.part_v);
@@ -453,7 +455,7 @@ sage_status run_prepass(const Plan& p, const std::vector<KParams>& kp, int dtype
         qa.mu_qb = p.smooth_q_blk ? b.mu_qb : nullptr;
         qa.mq_code = p.smooth_q_blk ? b.mu_q_code : nullptr;
         qa.mq_scale = p.smooth_q_blk ? b.mu_q_cscale : nullptr;
-        qa.nq = chunk_blocks(P, true, p.hq, true);
+        qa.nq = skip_q ? 0 : chunk_blocks(P, true, p.hq, true);
         qa.nk = chunk_blocks(P, false, p.hkv, true);
         // 16-bit V: 64-token chunks (128-byte rows already); E4M3 V: one
         // 128-token key tile per workgroup
@@ -488,13 +490,16 @@ sage_quant_bufs bufs_in_ws(const Plan& p, uint8_t* ws, const WsLayout& w) {
 }
 
 // The fused kernel over every parameter block, then (split key range) the
-// merge of the partials.
+// merge of the partials.  q_raw: the kernel quantizes this Q itself (null:
+// it reads the codes in `b`).
 sage_status run_attn(const Plan& p, std::vector<KParams> kp, int dtype, const sage_quant_bufs& b,
                      const float* ds, const float* mu_v, void* o, float* lse, float* part_o,
-                     float* part_ml, hipStream_t st) {
+                     float* part_ml, hipStream_t st, const void* q_raw = nullptr) {
     for (KParams& P : kp) {
         P.part_o = part_o;
         P.part_ml = part_ml;
+        P.q_raw = static_cast<const uint16_t*>(q_raw);
+        P.mu_q = q_raw && p.smooth_q ? b.mu_q : nullptr;
         SAGE_TRY(launch_attn(P, dtype, b.q_codes, b.q_scale, b.k_codes, b.k_scale, b.v_codes,
                              b.v_scale, ds, mu_v, o, lse, p.smooth_q_blk ? b.mu_q_code : nullptr,
                              p.smooth_q_blk ? b.mu_q_cscale : nullptr, st));
@@ -538,11 +543,17 @@ sage_status forward(const sage_attn_desc* desc, const int32_t* cuq, const int32_
     uint8_t* base = align_up(ws);
     const sage_quant_bufs b = bufs_in_ws(p, base, w);
     const std::vector<KParams> kp = make_params(p);
-    if ((e = run_prepass(p, kp, desc->dtype, q, k, v, b, base, w, st)) != SAGE_OK) return e;
+    // The fused kernel quantizes Q itself (Q is read once, by the kernel that
+    // needs it), unless Q is smoothed per block (its block means are formed
+    // in the pre-pass) or a launch runs the decode kernel, which reads codes.
+    bool fuse_q = !p.smooth_q_blk;
+    for (const KParams& P : kp) fuse_q = fuse_q && !use_decode_kernel(P);
+    if ((e = run_prepass(p, kp, desc->dtype, q, k, v, b, base, w, st, fuse_q)) != SAGE_OK)
+        return e;
     return run_attn(p, kp, desc->dtype, b, p.smooth_q ? b.delta_s : nullptr,
                     p.smooth_v ? b.mu_v : nullptr, o, lse,
                     reinterpret_cast<float*>(base + w.split_o),
-                    reinterpret_cast<float*>(base + w.split_ml), st);
+                    reinterpret_cast<float*>(base + w.split_ml), st, fuse_q ? q : nullptr);
 }
 
 }  // namespace

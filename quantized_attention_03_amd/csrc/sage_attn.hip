@@ -279,6 +279,82 @@ __device__ inline void load_q(const int8_t* qrow, v4i* qf) {
         qf[c] = *reinterpret_cast<const v4i*>(qrow + 32 * c + 16 * h);
 }
 
+// Q quantized in the fused kernel (the pre-pass then skips Q): q_load reads
+// the lane's values of its row, channels [32c + 16*half, +16) for each
+// 32-channel chunk c as load_q reads their codes (rows past nq read as 0);
+// q_values converts them, smooths them by mu when given and returns the
+// lane's absmax.  q_codes then forms the codes with the
+// block's absmax a exactly as the pre-pass does: inv = 127/a (both scaled
+// by 2^64 first below 2^-100), code = clamp(rne(x*inv), +-127).
+template <int DT>
+__device__ inline float q_h2f(uint16_t u) {
+    if constexpr (DT == 0) return __half2float(__ushort_as_half(u));
+    else return __uint_as_float((uint32_t)u << 16);
+}
+
+template <int D>
+__device__ inline void q_load(const uint16_t* row, bool valid, uint4 (&raw)[D / 32][2]) {
+    const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+            raw[c][g] = valid ? *reinterpret_cast<const uint4*>(row + 32 * c + 16 * h + 8 * g)
+                              : make_uint4(0u, 0u, 0u, 0u);
+}
+
+template <int D, int DT>
+__device__ inline float q_values(const uint4 (&raw)[D / 32][2], const float* mu, bool valid,
+                                 float (&x)[D / 32][16]) {
+    const int h = (threadIdx.x & 63) >> 5;
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int ch = 32 * c + 16 * h + 8 * g;
+            const uint32_t wd[4] = {raw[c][g].x, raw[c][g].y, raw[c][g].z, raw[c][g].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float lo = q_h2f<DT>((uint16_t)(wd[k] & 0xffff));
+                float hi = q_h2f<DT>((uint16_t)(wd[k] >> 16));
+                if (mu && valid) {
+                    lo = lo - mu[ch + 2 * k];
+                    hi = hi - mu[ch + 2 * k + 1];
+                }
+                x[c][8 * g + 2 * k] = lo;
+                x[c][8 * g + 2 * k + 1] = hi;
+                m = fmaxf(m, fmaxf(fabsf(lo), fabsf(hi)));
+            }
+        }
+    return m;
+}
+
+template <int D>
+__device__ inline void q_codes(const float (&x)[D / 32][16], float a, v4i* qf) {
+    const float rs = a < 0x1p-100f ? 0x1p64f : 1.0f;
+    const float inv = a > 0.0f ? 127.0f / (a * rs) : 0.0f;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t wd = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float q = rintf((x[c][4 * j + e] * rs) * inv);
+                q = fminf(fmaxf(q, -127.0f), 127.0f);
+                wd |= ((uint32_t)(int32_t)q & 0xffu) << (8 * e);
+            }
+            qf[c][j] = (int)wd;
+        }
+}
+
+__device__ inline float wave_max64(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
 // S^T of one 128-key tile: sacc[b] covers keys 32b..32b+31; lane (row,
 // half) receives keys 32b + 16*half + r in register r (r = 0..15).  The
 // accumulators start at the bits of 1.5*2^23 (sbias_init), so that the int32
@@ -816,6 +892,15 @@ __device__ inline uint32_t f2h_bits(float f) {
 // that point); the softmax phases of both groups read them from the per-pair
 // stage of the tile (two stages: tile t is written in epoch 2t and read in
 // epochs 2t+1 and 2t+2).
+// Dynamic LDS of the fused kernel: K and V^T double buffers, the score-bias
+// stages and the per-block Q smoothing area (the kernel's own Q quantization
+// adds 64 bytes of slots after it).
+template <int D, bool HAS_DS, bool PVH, bool BQS = false, int QB = QBLK>
+constexpr int lds_bytes() {
+    return 2 * Tile<D, PVH>::KBYTES + 2 * Tile<D, PVH>::VBYTES +
+           (HAS_DS ? 3 * Tile<D, PVH>::DSBYTES : 0) + (BQS ? Bqs<QB>::BYTES : 0);
+}
+
 template <int D, int DT, bool HAS_DS, bool PVH, int QB, bool DUMP = false, bool BQS = false>
 __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __restrict__ qc,
                                                  const float* __restrict__ qsc,
@@ -848,7 +933,21 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
 
     v4i qf[D / 32];
     float sq = 0.0f;
-    if (w.nt_w > w.t0) {
+    // With raw Q the kernel quantizes it here (q_values, q_codes): every wave
+    // posts the absmax of its 32 rows to an LDS slot, and a 64-token block
+    // takes the larger of its two waves' after the first barrier below (so
+    // every wave posts, whether or not it has key tiles).
+    const bool qraw = !DUMP && !BQS && P.q_raw != nullptr;   // (BQS: Q codes from the pre-pass)
+    float qx[D / 32][16];
+    uint4 qraw_v[D / 32][2];
+    float* qslot = reinterpret_cast<float*>(smem + lds_bytes<D, HAS_DS, PVH, BQS, QB>());
+    if (qraw) {
+        // (the loads go out here; their values are first used after the
+        // first K tile's copies are issued, so the two latencies overlap)
+        const uint16_t* row = P.q_raw + si.q_el + (int64_t)w.head * P.qs.h +
+                              (int64_t)min(my_q, nq - 1) * P.qs.n;
+        q_load<D>(row, my_q < nq, qraw_v);
+    } else if (w.nt_w > w.t0) {
         const int64_t qrow0 = si.rq * P.hq + (int64_t)w.head * si.npq;
         load_q<D>(qc + (qrow0 + my_q) * D, qf);
         if constexpr (!DUMP) sq = qsc[(qrow0 + w.q0) / QB];
@@ -882,7 +981,19 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     if (w.nt_wg > w.t0)
         stage_k<D, FWD_NT, HAS_DS, PVH>(kst0, dst0, off, kbase, dsb, si.npk, w.t0, w.hpw);
     if constexpr (BQS) bqs_load<D, QB>(P, w, mcode, mcs, btab, btsc);
+    if (qraw) {
+        const float* muh = P.mu_q ? P.mu_q + ((int64_t)si.sid * P.hq + w.head) * D : nullptr;
+        const float m = wave_max64(q_values<D, DT>(qraw_v, muh, my_q < nq, qx));
+        if (lane == 0) qslot[threadIdx.x >> 6] = m;
+    }
     bar();
+    if (qraw) {
+        const int wave = threadIdx.x >> 6;
+        float a = qslot[wave];
+        if constexpr (QB == 64) a = fmaxf(a, qslot[((wave / w.hpw) ^ 1) * w.hpw + wave % w.hpw]);
+        q_codes<D>(qx, a, qf);
+        sq = a > 0.0f ? a / 127.0f : 0.0f;
+    }
     if (grp == 1) bar();
 
     v8i pb[2];                  // P^ of the previous tile (E4M3)
@@ -1422,11 +1533,6 @@ int wg_count_host(const KParams& P, int waves) {
     return tot;
 }
 
-template <int D, bool HAS_DS, bool PVH, bool BQS = false, int QB = QBLK>
-constexpr int lds_bytes() {
-    return 2 * Tile<D, PVH>::KBYTES + 2 * Tile<D, PVH>::VBYTES +
-           (HAS_DS ? 3 * Tile<D, PVH>::DSBYTES : 0) + (BQS ? Bqs<QB>::BYTES : 0);
-}
 
 // Allow a kernel its dynamic LDS beyond the default, once per device (the
 // attribute belongs to the function on the current device).  `done` holds one
@@ -1450,7 +1556,8 @@ hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const in
                   const float* mu_v, void* o, float* lse, const int8_t* mcode, const float* mcs,
                   hipStream_t st) {
     static std::atomic<uint64_t> attr_set{0};
-    constexpr int LDS = lds_bytes<D, HAS_DS, PVH, BQS, QB>();
+    // (+64 bytes: the absmax slots of the kernel's own Q quantization)
+    constexpr int LDS = lds_bytes<D, HAS_DS, PVH, BQS, QB>() + 64;
     auto* kern = &k_attn<D, DT, HAS_DS, PVH, QB, false, BQS>;
     hipError_t e = lds_attr(reinterpret_cast<const void*>(kern), LDS, attr_set);
     if (e != hipSuccess) return e;
@@ -1577,11 +1684,6 @@ hipError_t launch_qk_dump(const KParams& P, const int8_t* qc, const int8_t* kc, 
 // partial row).  Every split writes its partial (zeros and m = -inf when it
 // saw no key), so the loads need no guard.
 // ---------------------------------------------------------------------------
-__device__ inline float wave_max64(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
 __device__ inline float wave_sum64(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
