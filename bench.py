@@ -90,9 +90,19 @@ KERNEL_SRC = os.path.join(ROOT, "quantized_attention_03_amd", "csrc", "sage_attn
 
 
 def kernel_digest() -> str:
+    """sha256[:16] of the kernel source's code: comments removed and runs of
+    whitespace collapsed, so that a change to comments alone keeps the
+    committed counter summaries valid, and any change to the code does not."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        src = f.read()
+    # string and character literals are kept whole (a "//" inside one is not
+    # a comment); block and line comments go
+    tok = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|/\*.*?\*/|//[^\n]*', re.S)
+    code = tok.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", src)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel: str = "k_attn"):

@@ -46,6 +46,11 @@
 //    cycle, about half of what the SIMD takes from two waves).
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
+//  * Inside a whole forward call the kernel quantizes its own Q rows in its
+//    prologue (the pre-pass then skips Q); the entry point that takes
+//    caller codes reads them instead (q_load / q_values / q_codes).
+//  * Row maxima beyond 2^16 in log2 units are raised a few units in their
+//    last place (raise_max), so that no P code reaches the E4M3 NaN code.
 #include <algorithm>
 #include <atomic>
 #include <cfloat>
