@@ -16,9 +16,10 @@ Prints ONE JSON line.  Besides the standard fields it carries
                  HIP events on the launch stream around the loop; kernel_ms
                  is the fused kernel's half, prepass_ms the other, measured,
                  not a difference, and halves_sum_ms their sum next to
-                 ms_per_step.  Inside sage_attn_fwd the fused kernel
-                 quantizes Q itself in its prologue and the pre-pass skips
-                 Q, so the call is a little shorter than the halves' sum;
+                 ms_per_step.  Inside sage_attn_fwd (without Q smoothing)
+                 the fused kernel quantizes Q itself in its prologue and the
+                 pre-pass skips Q, so the call is a little shorter than the
+                 halves' sum;
                  kernel_ms is the same kernel reading the pre-pass's Q
                  codes (its loop and softmax are the same);
   n32k         : the same figures for the long-context varlen workload at

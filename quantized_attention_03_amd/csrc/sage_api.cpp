@@ -499,7 +499,6 @@ sage_status run_attn(const Plan& p, std::vector<KParams> kp, int dtype, const sa
         P.part_o = part_o;
         P.part_ml = part_ml;
         P.q_raw = static_cast<const uint16_t*>(q_raw);
-        P.mu_q = q_raw && p.smooth_q ? b.mu_q : nullptr;
         SAGE_TRY(launch_attn(P, dtype, b.q_codes, b.q_scale, b.k_codes, b.k_scale, b.v_codes,
                              b.v_scale, ds, mu_v, o, lse, p.smooth_q_blk ? b.mu_q_code : nullptr,
                              p.smooth_q_blk ? b.mu_q_cscale : nullptr, st));
@@ -544,9 +543,10 @@ sage_status forward(const sage_attn_desc* desc, const int32_t* cuq, const int32_
     const sage_quant_bufs b = bufs_in_ws(p, base, w);
     const std::vector<KParams> kp = make_params(p);
     // The fused kernel quantizes Q itself (Q is read once, by the kernel that
-    // needs it), unless Q is smoothed per block (its block means are formed
-    // in the pre-pass) or a launch runs the decode kernel, which reads codes.
-    bool fuse_q = !p.smooth_q_blk;
+    // needs it), unless Q is smoothed (with the score bias that measured
+    // slower than the pre-pass work it saves) or a launch runs the decode
+    // kernel, which reads codes.
+    bool fuse_q = !p.smooth_q;
     for (const KParams& P : kp) fuse_q = fuse_q && !use_decode_kernel(P);
     if ((e = run_prepass(p, kp, desc->dtype, q, k, v, b, base, w, st, fuse_q)) != SAGE_OK)
         return e;

@@ -46,9 +46,10 @@
 //    cycle, about half of what the SIMD takes from two waves).
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
-//  * Inside a whole forward call the kernel quantizes its own Q rows in its
-//    prologue (the pre-pass then skips Q); the entry point that takes
-//    caller codes reads them instead (q_load / q_values / q_codes).
+//  * Inside a whole forward call without Q smoothing the kernel quantizes its
+//    own Q rows in its prologue (the pre-pass then skips Q); otherwise, and
+//    in the entry point that takes caller codes, it reads the Q codes
+//    (q_load / q_values / q_codes).
 //  * Row maxima beyond 2^16 in log2 units are raised a few units in their
 //    last place (raise_max), so that no P code reaches the E4M3 NaN code.
 #include <algorithm>
@@ -284,10 +285,10 @@ __device__ inline void load_q(const int8_t* qrow, v4i* qf) {
         qf[c] = *reinterpret_cast<const v4i*>(qrow + 32 * c + 16 * h);
 }
 
-// Q quantized in the fused kernel (the pre-pass then skips Q): q_load reads
-// the lane's values of its row, channels [32c + 16*half, +16) for each
-// 32-channel chunk c as load_q reads their codes (rows past nq read as 0);
-// q_values converts them, smooths them by mu when given and returns the
+// Q quantized in the fused kernel (the pre-pass then skips Q; only where Q
+// is not smoothed): q_load reads the lane's values of its row, channels
+// [32c + 16*half, +16) for each 32-channel chunk c as load_q reads their
+// codes (rows past nq read as 0); q_values converts them and returns the
 // lane's absmax.  q_codes then forms the codes with the
 // block's absmax a exactly as the pre-pass does: inv = 127/a (both scaled
 // by 2^64 first below 2^-100), code = clamp(rne(x*inv), +-127).
@@ -309,24 +310,17 @@ __device__ inline void q_load(const uint16_t* row, bool valid, uint4 (&raw)[D / 
 }
 
 template <int D, int DT>
-__device__ inline float q_values(const uint4 (&raw)[D / 32][2], const float* mu, bool valid,
-                                 float (&x)[D / 32][16]) {
-    const int h = (threadIdx.x & 63) >> 5;
+__device__ inline float q_values(const uint4 (&raw)[D / 32][2], float (&x)[D / 32][16]) {
     float m = 0.0f;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-            const int ch = 32 * c + 16 * h + 8 * g;
             const uint32_t wd[4] = {raw[c][g].x, raw[c][g].y, raw[c][g].z, raw[c][g].w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                float lo = q_h2f<DT>((uint16_t)(wd[k] & 0xffff));
-                float hi = q_h2f<DT>((uint16_t)(wd[k] >> 16));
-                if (mu && valid) {
-                    lo = lo - mu[ch + 2 * k];
-                    hi = hi - mu[ch + 2 * k + 1];
-                }
+                const float lo = q_h2f<DT>((uint16_t)(wd[k] & 0xffff));
+                const float hi = q_h2f<DT>((uint16_t)(wd[k] >> 16));
                 x[c][8 * g + 2 * k] = lo;
                 x[c][8 * g + 2 * k + 1] = hi;
                 m = fmaxf(m, fmaxf(fabsf(lo), fabsf(hi)));
@@ -942,7 +936,9 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     // posts the absmax of its 32 rows to an LDS slot, and a 64-token block
     // takes the larger of its two waves' after the first barrier below (so
     // every wave posts, whether or not it has key tiles).
-    const bool qraw = !DUMP && !BQS && P.q_raw != nullptr;   // (BQS: Q codes from the pre-pass)
+    // (compiled only where Q is not smoothed: with the score bias the
+    // prologue measured slower than the pre-pass work it saves)
+    const bool qraw = !DUMP && !BQS && !HAS_DS && P.q_raw != nullptr;
     float qx[D / 32][16];
     uint4 qraw_v[D / 32][2];
     float* qslot = reinterpret_cast<float*>(smem + lds_bytes<D, HAS_DS, PVH, BQS, QB>());
@@ -987,8 +983,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         stage_k<D, FWD_NT, HAS_DS, PVH>(kst0, dst0, off, kbase, dsb, si.npk, w.t0, w.hpw);
     if constexpr (BQS) bqs_load<D, QB>(P, w, mcode, mcs, btab, btsc);
     if (qraw) {
-        const float* muh = P.mu_q ? P.mu_q + ((int64_t)si.sid * P.hq + w.head) * D : nullptr;
-        const float m = wave_max64(q_values<D, DT>(qraw_v, muh, my_q < nq, qx));
+        const float m = wave_max64(q_values<D, DT>(qraw_v, qx));
         if (lane == 0) qslot[threadIdx.x >> 6] = m;
     }
     bar();

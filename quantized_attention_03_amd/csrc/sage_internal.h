@@ -53,11 +53,9 @@ struct KParams {
     int32_t kv_tiles, nsplit;
     int64_t rows_total;
     int32_t bqs;                        // per-block Q smoothing (bias formed in the kernel)
-    // The fused kernel quantizes Q itself from these (null: it reads the
-    // pre-pass codes): the input tensor and, with Q smoothing, the means
-    // [S][hq][d]
+    // The fused kernel quantizes Q itself from this input tensor (null: it
+    // reads the pre-pass codes); only where Q is not smoothed
     const uint16_t* q_raw;
-    const float* mu_q;
     float* part_o;                      // [nsplit][rows_total][d]
     float* part_ml;                     // [nsplit][rows_total][2]: m (log2 units), l
     SeqTab tab;

@@ -6,9 +6,9 @@
 //     and V smoothing by channel-mean subtraction);
 //   * INT8 codes with one FP32 scale per 64-token block for Q and K (package
 //     page: per-block quantization of queries and keys; ComfyUI blog feature
-//     item 2: Q.K^T in INT8); inside a whole forward call the fused kernel
-//     forms the Q codes itself, with the same arithmetic, and this pass
-//     leaves Q out;
+//     item 2: Q.K^T in INT8); inside a whole forward call without Q
+//     smoothing the fused kernel forms the Q codes itself, with the same
+//     arithmetic, and this pass leaves Q out;
 //   * OCP E4M3 codes with one FP32 scale per channel for V (ComfyUI blog
 //     feature item 2: P.V in FP8, granularities differ);
 //   * the score bias that compensates Q smoothing.
