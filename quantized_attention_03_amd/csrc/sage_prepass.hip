@@ -92,10 +92,16 @@ struct ChunkCount {
 // walks its tokens in order with 16-byte row reads.
 // partial (s,h,g,c) at (((r_s/64)*heads + h*(np_s/64) + g)*d + c).
 // ---------------------------------------------------------------------------
+// One wave per statistics workgroup: its few chunks each still take one
+// thread per granule walking the tokens in order, and the smaller
+// workgroups give a small problem enough of them to cover the GPU (causal
+// GQA, 16 MiB of K and V each: 512 rather than 128 of 256 threads).
+constexpr int SWG = 64;
+
 template <int D>
 struct StatShape {
     static constexpr int GPR = D / 8;        // 16-byte granules per token row
-    static constexpr int CPW = WG / GPR;     // chunks per workgroup
+    static constexpr int CPW = SWG / GPR;    // chunks per workgroup
 };
 
 // Workgroups sequence s owns in a statistics launch.
@@ -176,7 +182,7 @@ __device__ inline void stats_job_d(const KParams& P, const StatJob& J, int blk) 
 // Up to three statistics jobs in one launch; the grid is their block counts
 // back to back.
 template <int DT, int D>
-__global__ __launch_bounds__(WG) void k_stats(KParams P, StatJobs J) {
+__global__ __launch_bounds__(SWG) void k_stats(KParams P, StatJobs J) {
     int blk = blockIdx.x;
     if (blk < J.j[0].nblocks) { stats_job_d<DT, D>(P, J.j[0], blk); return; }
     blk -= J.j[0].nblocks;
@@ -724,12 +730,12 @@ __global__ __launch_bounds__(WG) void k_quant(KParams P, QuantArgs A) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-int stat_chunks_per_wg(int d) { return WG / (d / 8); }
+int stat_chunks_per_wg(int d) { return SWG / (d / 8); }
 
 hipError_t launch_stats(const KParams& P, int dtype, const StatJobs& J, hipStream_t st) {
     const int nb = J.j[0].nblocks + J.j[1].nblocks + J.j[2].nblocks;
     if (nb <= 0) return hipSuccess;
-#define SAGE_ST(DT, D) k_stats<DT, D><<<nb, WG, 0, st>>>(P, J)
+#define SAGE_ST(DT, D) k_stats<DT, D><<<nb, SWG, 0, st>>>(P, J)
     if (dtype == 0) {
         if (P.d == 64) SAGE_ST(0, 64); else if (P.d == 96) SAGE_ST(0, 96); else SAGE_ST(0, 128);
     } else {

@@ -8,7 +8,7 @@
 #include "sage_internal.h"
 
 namespace sage {
-int stat_chunks_per_wg(int d) { return WG / (d / 8); }
+int stat_chunks_per_wg(int d) { return 64 / (d / 8); }   // one-wave statistics workgroups
 hipError_t launch_stats(const KParams&, int, const StatJobs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_finalize(const KParams&, const FinJobs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_quant(const KParams&, int, const QuantArgs&, hipStream_t) { return hipErrorNoDevice; }
