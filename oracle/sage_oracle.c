@@ -418,7 +418,17 @@ static int64_t last_visible(int64_t i, int64_t nq, int64_t nkv, int causal) {
  * none does; where the scores are so large that the window itself spans
  * several codes (a row maximum of 2^16 or more in log2 units, whose own unit
  * in the last place is then 2^-7 or coarser), it spans them all, the top
- * code 448 included. */
+ * code 448 included.  The same window moves each p itself, and so the row
+ * sum L: an evaluation whose p_j lie within e^(+-window_j) of the oracle's
+ * has a sum between L - LD and L + LU (LD = sum p_j (1 - e^-window_j),
+ * LU = sum p_j (e^window_j - 1), carried like l), which scales the whole row
+ * even where every code stays (a nearly one-hot row whose top p is 1 + 2^-9
+ * rather than 1 keeps the code 448 but divides by a larger L).  The factors
+ * that rescale a code after it is picked (alpha between key tiles, e^(m_s - M)
+ * in the split merge) are differences of such maxima, within the same window
+ * of 1: per key tacc therefore also takes the largest code in the window times
+ * (e^window - 1) times |v|.  The bound is tacc * |out_scale| / (L - LD) +
+ * |o - mu_v| * max(LD / (L - LD), LU / (L + LU)). */
 enum { P_FP8 = 0, P_F16 = 1, P_BF16 = 2 };
 
 /* Relative window within which a rounding midpoint counts as a tie: twice the
@@ -476,6 +486,8 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
     float* acc = (float*)malloc(sizeof(float) * (size_t)d);
     float* ties = (float*)malloc(sizeof(float) * (size_t)d * (size_t)nsplit);
     float* tacc = (float*)malloc(sizeof(float) * (size_t)d);
+    double* lus = (double*)malloc(sizeof(double) * (size_t)nsplit);
+    double* lds = (double*)malloc(sizeof(double) * (size_t)nsplit);
     for (int64_t r = 0; r < nrows; ++r) {
         int64_t i = rows[r];
         int64_t jmax = last_visible(i, nq, nkv, causal);
@@ -486,6 +498,7 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
             float* a = accs + sp * d;
             float* ta = ties + sp * d;
             float m = -INFINITY, l = 0.0f;
+            double lu = 0.0, ld = 0.0;      /* the window of l, up and down */
             for (int c = 0; c < d; ++c) a[c] = ta[c] = 0.0f;
             int64_t k_end = (sp + 1) * span - 1 < jmax ? (sp + 1) * span - 1 : jmax;
             for (int64_t t0 = sp * span; t0 <= k_end; t0 += bkv) {
@@ -507,32 +520,44 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
                 float mn = m > mt ? m : mt;
                 float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)(m - mn));
                 float psum = 0.0f;
+                double pu = 0.0, pd = 0.0;
                 for (int c = 0; c < d; ++c) a[c] = alpha * a[c];
                 if (tie)
                     for (int c = 0; c < d; ++c) ta[c] = alpha * ta[c];
                 for (int64_t jj = 0; jj < nt; ++jj) {
                     float p = (float)exp((double)(s[jj] - mn));
                     psum = psum + p;
+                    float ph = p_operand(p, p_mode);
                     if (tie) {
-                        float st = tie_step(p, p_mode, tie_window(mag[jj], mn));
-                        if (st > 0.0f) {
+                        const double wdw = tie_window(mag[jj], mn);
+                        pu += (double)p * expm1(wdw);
+                        pd -= (double)p * expm1(-wdw);
+                        const float st = tie_step(p, p_mode, wdw);
+                        /* the code spread, and the largest code scaled by the
+                           window of the factors that rescale it */
+                        const float kt = (float)((double)st + ((double)ph + st) * expm1(wdw));
+                        if (kt > 0.0f) {
                             const float* vrow = vdec + (t0 + jj) * d;
-                            for (int c = 0; c < d; ++c) ta[c] = ta[c] + st * fabsf(vrow[c]);
+                            for (int c = 0; c < d; ++c) ta[c] = ta[c] + kt * fabsf(vrow[c]);
                         }
                     }
-                    float ph = p_operand(p, p_mode);
                     if (ph == 0.0f) continue;     /* a zero product leaves acc as is */
                     const float* vrow = vdec + (t0 + jj) * d;
                     for (int c = 0; c < d; ++c) a[c] = a[c] + ph * vrow[c];
                 }
                 l = alpha * l + psum;
+                lu = (double)alpha * lu + pu;
+                ld = (double)alpha * ld + pd;
                 m = mn;
             }
             ms[sp] = m;
             ls[sp] = l;
+            lus[sp] = lu;
+            lds[sp] = ld;
         }
         /* merge the splits */
         float M = -INFINITY, L = 0.0f;
+        double LU = 0.0, LD = 0.0;
         for (int64_t sp = 0; sp < nsplit; ++sp)
             if (ms[sp] > M) M = ms[sp];
         for (int c = 0; c < d; ++c) acc[c] = tacc[c] = 0.0f;
@@ -541,23 +566,29 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
                 if (ms[sp] == -INFINITY) continue;   /* a split without visible keys */
                 float w = (float)exp((double)(ms[sp] - M));
                 L = L + w * ls[sp];
+                LU += (double)w * lus[sp];
+                LD += (double)w * lds[sp];
                 for (int c = 0; c < d; ++c) acc[c] = acc[c] + w * accs[sp * d + c];
                 if (tie)
                     for (int c = 0; c < d; ++c) tacc[c] = tacc[c] + w * ties[sp * d + c];
             }
         }
         float* o = out + r * d;
-        if (tie)
-            for (int c = 0; c < d; ++c)
-                tie[r * d + c] = (jmax < 0 || L == 0.0f) ? 0.0f
-                    : tacc[c] * (out_scale ? fabsf(out_scale[c]) : 1.0f) / L;
         if (jmax < 0 || L == 0.0f) {
             for (int c = 0; c < d; ++c) o[c] = 0.0f;
+            if (tie)
+                for (int c = 0; c < d; ++c) tie[r * d + c] = 0.0f;
             if (lse) lse[r] = -INFINITY;
             continue;
         }
         for (int c = 0; c < d; ++c) {
             float val = (out_scale ? acc[c] * out_scale[c] : acc[c]) / L;
+            if (tie) {
+                const double lo = (double)L - LD;
+                const double rel = fmax(LD / lo, LU / ((double)L + LU));
+                tie[r * d + c] = (float)((double)tacc[c] * (out_scale ? fabsf(out_scale[c]) : 1.0f) / lo
+                                         + fabs((double)val) * rel);
+            }
             if (mu_v) val = val + mu_v[c];
             o[c] = val;
         }
@@ -571,6 +602,8 @@ static void recipe_rows(const int8_t* qc, const float* q_scale, const int8_t* kc
     free(acc);
     free(ties);
     free(tacc);
+    free(lus);
+    free(lds);
 }
 
 /* The INT8-QK / FP8-PV recipe ([BLOG] item 2, [SA2] item 3):
