@@ -930,16 +930,27 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     // export) this is the plain one-item launch.
     const int G = gridDim.x;
     for (int rnd = 0; rnd * G < nitems; ++rnd) {
-    const int item = rnd * G + ((rnd & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    // (odd rounds reverse the order of the groups of 8 workgroups but keep
+    // the place in the group, so that a workgroup keeps its item index mod 8:
+    // workgroups go to the 8 XCDs in turn and the kv head is the fastest
+    // index of the items, so each XCD's L2 keeps serving the same kv heads)
+    int pos = (int)blockIdx.x;
+    if (rnd & 1) pos = G % 8 == 0 ? G - 8 * (1 + pos / 8) + pos % 8 : G - 1 - pos;
+    const int item = rnd * G + pos;
     if (item >= nitems) continue;       // (uniform over the workgroup)
     // the previous item's epilogue has read its rows out of LDS
     if (rnd > 0) __syncthreads();
     [&]() __attribute__((always_inline)) {
+    // the thread index, opaque to the compiler per item: values formed from
+    // it are formed per item instead of once before the item loop and held
+    // (spilled) across every item's tile loop
+    int tx = (int)threadIdx.x;
+    asm volatile("" : "+v"(tx));
     const Work w = decode_work<FWD_WAVES>(P, item);
     const SeqInfo& si = w.si;
-    const int lane = threadIdx.x & 63;
+    const int lane = tx & 63;
     const int h = lane >> 5, qi = lane & 31;
-    const int grp = (threadIdx.x >> 6) >> 2;
+    const int grp = (tx >> 6) >> 2;
     const int my_q = w.q0 + qi;
     const int nq = si.nq, nkv = si.nkv;
 
@@ -992,7 +1003,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     uint8_t* bq0 = dst0 + 3 * T::DSBYTES;      // per-pair stages, code table, scales (BQS)
     uint8_t* btab = bq0 + 2 * Bqs<QB>::STAGE;
     float* btsc = reinterpret_cast<float*>(btab + Bqs<QB>::TABLE);
-    const int my_pair = (32 * ((threadIdx.x >> 6) / w.hpw)) / QB * w.hpw + (threadIdx.x >> 6) % w.hpw;
+    const int my_pair = (32 * ((tx >> 6) / w.hpw)) / QB * w.hpw + (tx >> 6) % w.hpw;
     DmaOffsets<D, FWD_NT, PVH> off;
     off.init(si.npk);
 
@@ -1003,11 +1014,11 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     if constexpr (BQS) bqs_load<D, QB>(P, w, mcode, mcs, btab, btsc);
     if (qraw) {
         const float m = wave_max64(q_values<D, DT>(qraw_v, qx));
-        if (lane == 0) qslot[threadIdx.x >> 6] = m;
+        if (lane == 0) qslot[tx >> 6] = m;
     }
     bar();
     if (qraw) {
-        const int wave = threadIdx.x >> 6;
+        const int wave = tx >> 6;
         float a = qslot[wave];
         if constexpr (QB == 64) a = fmaxf(a, qslot[((wave / w.hpw) ^ 1) * w.hpw + wave % w.hpw]);
         q_codes<D>(qx, a, qf);
@@ -1217,7 +1228,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     constexpr int NGR = RS / 16;               // granules per staged row
     static_assert(FWD_WAVES * 32 * RS <= 2 * T::KBYTES + 2 * T::VBYTES, "staging fits the stages");
     __syncthreads();                           // every wave is done with the tile stages
-    uint8_t* stg = smem + (threadIdx.x >> 6) * 32 * RS;
+    uint8_t* stg = smem + (tx >> 6) * 32 * RS;
     if (w.q0 < nq) {
         const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         const int64_t vsb = ((int64_t)si.sid * P.hkv + w.hkv) * D;
