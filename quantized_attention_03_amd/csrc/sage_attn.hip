@@ -44,10 +44,6 @@
 //    bound, the operand half moves to the next MFMA phase, under its matrix
 //    instructions (a single wave issues VALU work only about every fifth
 //    cycle, about half of what the SIMD takes from two waves).
-//  * Persistent launch: one workgroup per compute unit, each looping over
-//    its share of the work items (snake order over the heavy-first list), so
-//    that the 3-7 items a compute unit takes do not each pay a workgroup
-//    dispatch and its start-up.
 //  * Causal (bottom-right) masking and sequence tails are applied only on
 //    the tiles that straddle them; fully hidden tiles are skipped.
 //  * Inside a whole forward call without Q smoothing the kernel quantizes its
@@ -226,7 +222,7 @@ __device__ inline int wg_count(const KParams& P, int nq) {
 }
 
 template <int WAVES>
-__device__ inline Work decode_work(const KParams& P, int item) {
+__device__ inline Work decode_work(const KParams& P) {
     Work w;
     const int hpw = heads_per_wg(P.group);
     const int rows = 32 * WAVES / hpw;
@@ -235,7 +231,7 @@ __device__ inline Work decode_work(const KParams& P, int item) {
     auto per = [&](int s) {
         return wg_count<WAVES>(P, P.tab.uniform ? P.tab.nq[0] : P.tab.nq[s]) * P.nsplit;
     };
-    const int s = find_seq(P, item, per, &local);
+    const int s = find_seq(P, blockIdx.x, per, &local);
     w.s = s;
     w.si = seq_info(P, s);
     const int nq = w.si.nq, nkv = w.si.nkv;
@@ -243,10 +239,8 @@ __device__ inline Work decode_work(const KParams& P, int item) {
     const int base = wg_count<WAVES>(P, nq);
     w.split = local / base;
     local %= base;
-    // kv head fastest (consecutive items go to consecutive workgroups, which
-    // land on different XCDs: in each round of the persistent launch an XCD
-    // serves one kv head), then the head group, then query tiles from the
-    // heaviest (last) to the lightest
+    // kv head fastest (consecutive workgroups land on different XCDs), then the
+    // head group, then query tiles from the heaviest (last) to the lightest
     w.hkv = local % P.hkv;
     const int rest = local / P.hkv;
     const int hg = rest % nhg;
@@ -918,39 +912,15 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                                                  uint16_t* __restrict__ o,
                                                  float* __restrict__ lse,
                                                  const int8_t* __restrict__ mcode,
-                                                 const float* __restrict__ mcs, int nitems) {
+                                                 const float* __restrict__ mcs) {
     static_assert(!BQS || (HAS_DS && !PVH && !DUMP), "per-block Q smoothing: FP8 P.V with bias");
     extern __shared__ __align__(16) uint8_t smem[];
     using T = Tile<D, PVH>;
-    // Work items: the workgroup takes items blockIdx.x + k*G in rounds k,
-    // in reverse order on odd rounds (snake), so that with the items sorted
-    // heavy-first every workgroup's sum of tiles is about the same (on the
-    // causal GQA workload exactly: 130 tiles each).  The launch has one
-    // workgroup per compute unit; with one workgroup per item (the Q.K^T
-    // export) this is the plain one-item launch.
-    const int G = gridDim.x;
-    for (int rnd = 0; rnd * G < nitems; ++rnd) {
-    // (odd rounds reverse the order of the groups of 8 workgroups but keep
-    // the place in the group, so that a workgroup keeps its item index mod 8:
-    // workgroups go to the 8 XCDs in turn and the kv head is the fastest
-    // index of the items, so each XCD's L2 keeps serving the same kv heads)
-    int pos = (int)blockIdx.x;
-    if (rnd & 1) pos = G % 8 == 0 ? G - 8 * (1 + pos / 8) + pos % 8 : G - 1 - pos;
-    const int item = rnd * G + pos;
-    if (item >= nitems) continue;       // (uniform over the workgroup)
-    // the previous item's epilogue has read its rows out of LDS
-    if (rnd > 0) __syncthreads();
-    [&]() __attribute__((always_inline)) {
-    // the thread index, opaque to the compiler per item: values formed from
-    // it are formed per item instead of once before the item loop and held
-    // (spilled) across every item's tile loop
-    int tx = (int)threadIdx.x;
-    asm volatile("" : "+v"(tx));
-    const Work w = decode_work<FWD_WAVES>(P, item);
+    const Work w = decode_work<FWD_WAVES>(P);
     const SeqInfo& si = w.si;
-    const int lane = tx & 63;
+    const int lane = threadIdx.x & 63;
     const int h = lane >> 5, qi = lane & 31;
-    const int grp = (tx >> 6) >> 2;
+    const int grp = (threadIdx.x >> 6) >> 2;
     const int my_q = w.q0 + qi;
     const int nq = si.nq, nkv = si.nkv;
 
@@ -1003,7 +973,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     uint8_t* bq0 = dst0 + 3 * T::DSBYTES;      // per-pair stages, code table, scales (BQS)
     uint8_t* btab = bq0 + 2 * Bqs<QB>::STAGE;
     float* btsc = reinterpret_cast<float*>(btab + Bqs<QB>::TABLE);
-    const int my_pair = (32 * ((tx >> 6) / w.hpw)) / QB * w.hpw + (tx >> 6) % w.hpw;
+    const int my_pair = (32 * ((threadIdx.x >> 6) / w.hpw)) / QB * w.hpw + (threadIdx.x >> 6) % w.hpw;
     DmaOffsets<D, FWD_NT, PVH> off;
     off.init(si.npk);
 
@@ -1014,11 +984,11 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     if constexpr (BQS) bqs_load<D, QB>(P, w, mcode, mcs, btab, btsc);
     if (qraw) {
         const float m = wave_max64(q_values<D, DT>(qraw_v, qx));
-        if (lane == 0) qslot[tx >> 6] = m;
+        if (lane == 0) qslot[threadIdx.x >> 6] = m;
     }
     bar();
     if (qraw) {
-        const int wave = tx >> 6;
+        const int wave = threadIdx.x >> 6;
         float a = qslot[wave];
         if constexpr (QB == 64) a = fmaxf(a, qslot[((wave / w.hpw) ^ 1) * w.hpw + wave % w.hpw]);
         q_codes<D>(qx, a, qf);
@@ -1228,7 +1198,7 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     constexpr int NGR = RS / 16;               // granules per staged row
     static_assert(FWD_WAVES * 32 * RS <= 2 * T::KBYTES + 2 * T::VBYTES, "staging fits the stages");
     __syncthreads();                           // every wave is done with the tile stages
-    uint8_t* stg = smem + (tx >> 6) * 32 * RS;
+    uint8_t* stg = smem + (threadIdx.x >> 6) * 32 * RS;
     if (w.q0 < nq) {
         const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         const int64_t vsb = ((int64_t)si.sid * P.hkv + w.hkv) * D;
@@ -1280,8 +1250,6 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
             const uint4 val = *reinterpret_cast<const uint4*>(stg + row * RS + ((gr ^ (row % NGR)) << 4));
             if (q < nq) *reinterpret_cast<uint4*>(obase + (int64_t)q * P.os.n + 8 * gr) = val;
         }
-    }
-    }();
     }
 }
 
@@ -1582,25 +1550,6 @@ hipError_t lds_attr(const void* kernel, int bytes, std::atomic<uint64_t>& done) 
     return hipSuccess;
 }
 
-// The compute units of the current device (cached per device id below 64).
-hipError_t cu_count(int* n) {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) {
-        const int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0) { *n = c; return hipSuccess; }
-    }
-    int c = 0;
-    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (c <= 0) return hipErrorInvalidDevice;
-    if (dev >= 0 && dev < 64) cache[dev].store(c, std::memory_order_relaxed);
-    *n = c;
-    return hipSuccess;
-}
-
 template <int D, int DT, bool HAS_DS, bool PVH, int QB, bool BQS = false>
 hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const int8_t* kc,
                   const float* ksc, const uint8_t* vc, const float* vsc, const float* ds,
@@ -1612,17 +1561,10 @@ hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const in
     auto* kern = &k_attn<D, DT, HAS_DS, PVH, QB, false, BQS>;
     hipError_t e = lds_attr(reinterpret_cast<const void*>(kern), LDS, attr_set);
     if (e != hipSuccess) return e;
-    const int items = wg_count_host(P, FWD_WAVES) * P.nsplit;
-    if (items <= 0) return hipSuccess;
-    // one workgroup per compute unit (a workgroup fills one: 8 waves of 256
-    // VGPRs), each looping over its share of the items: a workgroup
-    // dispatched per item measured 2-3% slower on the causal GQA workload
-    int ncu = 0;
-    e = cu_count(&ncu);
-    if (e != hipSuccess) return e;
-    const int nblocks = std::min(items, ncu);
+    const int nblocks = wg_count_host(P, FWD_WAVES) * P.nsplit;
+    if (nblocks <= 0) return hipSuccess;
     kern<<<nblocks, FWD_NT, LDS, st>>>(P, qc, qsc, kc, ksc, vc, vsc, ds, mu_v,
-                                       static_cast<uint16_t*>(o), lse, mcode, mcs, items);
+                                       static_cast<uint16_t*>(o), lse, mcode, mcs);
     return hipGetLastError();
 }
 
@@ -1720,7 +1662,7 @@ hipError_t qk_dump_d(const KParams& P, const int8_t* qc, const int8_t* kc, int32
     if (nblocks <= 0) return hipSuccess;
     kern<<<nblocks, FWD_NT, lds_bytes<D, false, false>(), st>>>(
         P, qc, nullptr, kc, nullptr, nullptr, nullptr, nullptr, nullptr,
-        reinterpret_cast<uint16_t*>(s_out), nullptr, nullptr, nullptr, nblocks);
+        reinterpret_cast<uint16_t*>(s_out), nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 }  // namespace
