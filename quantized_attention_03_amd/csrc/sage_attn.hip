@@ -977,6 +977,20 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     DmaOffsets<D, FWD_NT, PVH> off;
     off.init(si.npk);
 
+    // The epilogue's V scales (and V means) of the kv head: copied into LDS
+    // here, behind the 64 bytes of Q absmax slots, so that the epilogue reads
+    // them there instead of waiting on memory after the last tile (the
+    // 16-bit P.V has no V scale).
+    float* vslds = reinterpret_cast<float*>(smem + lds_bytes<D, HAS_DS, PVH, BQS, QB>() + 64);
+    const int64_t vsb = ((int64_t)si.sid * P.hkv + w.hkv) * D;
+    if constexpr (!DUMP) {
+        const int wave = threadIdx.x >> 6;
+        if (!PVH && wave == 0 && lane < D / 4)
+            dma16(vsc + vsb + 4 * lane, reinterpret_cast<uint8_t*>(vslds));
+        if (mu_v && wave == 1 && lane < D / 4)
+            dma16(mu_v + vsb + 4 * lane, reinterpret_cast<uint8_t*>(vslds + D));
+    }
+
     // stage the first tile (K and bias) with every wave, then offset group 1.
     // Stage buffers are chosen by the tile's place r = t - t0 in the split.
     if (w.nt_wg > w.t0)
@@ -1172,7 +1186,6 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
         if (my_q < nq) {
             const int64_t row = si.lse0 + (int64_t)w.head * P.lse_hstride + my_q;
             const int64_t pr = (int64_t)w.split * P.rows_total + row;
-            const int64_t vsb = ((int64_t)si.sid * P.hkv + w.hkv) * D;
             const bool add_mu = mu_v && l_tot > 0.0f;
             float* po = P.part_o + pr * D;
 #pragma unroll
@@ -1181,8 +1194,8 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const int ch0 = 32 * c + 8 * r4 + 4 * h;
                     const float4 s4 = PVH ? make_float4(1.f, 1.f, 1.f, 1.f)
-                                          : *reinterpret_cast<const float4*>(vsc + vsb + ch0);
-                    const float4 m4 = add_mu ? *reinterpret_cast<const float4*>(mu_v + vsb + ch0)
+                                          : *reinterpret_cast<const float4*>(vslds + ch0);
+                    const float4 m4 = add_mu ? *reinterpret_cast<const float4*>(vslds + D + ch0)
                                              : make_float4(0.f, 0.f, 0.f, 0.f);
                     *reinterpret_cast<float4*>(po + ch0) =
                         make_float4(fmaf(acc[c][4 * r4], s4.x, m4.x * l_tot),
@@ -1201,22 +1214,21 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
     uint8_t* stg = smem + (threadIdx.x >> 6) * 32 * RS;
     if (w.q0 < nq) {
         const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        const int64_t vsb = ((int64_t)si.sid * P.hkv + w.hkv) * D;
-        // all scale (and mean) loads go out before the first use; the
-        // 16-bit operands carry no scale
+        // the scales (and means) from their LDS copy; the 16-bit operands
+        // carry no scale
         float4 sv[D / 32][4], mv[D / 32][4];
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4)
                 sv[c][r4] = PVH ? make_float4(1.f, 1.f, 1.f, 1.f)
-                                : *reinterpret_cast<const float4*>(vsc + vsb + 32 * c + 8 * r4 + 4 * h);
+                                : *reinterpret_cast<const float4*>(vslds + 32 * c + 8 * r4 + 4 * h);
         const bool add_mu = mu_v && l_tot > 0.0f;
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4)
-                mv[c][r4] = add_mu ? *reinterpret_cast<const float4*>(mu_v + vsb + 32 * c + 8 * r4 + 4 * h)
+                mv[c][r4] = add_mu ? *reinterpret_cast<const float4*>(vslds + D + 32 * c + 8 * r4 + 4 * h)
                                    : make_float4(0.f, 0.f, 0.f, 0.f);
         uint8_t* mine = stg + qi * RS;
 #pragma unroll
@@ -1556,8 +1568,9 @@ hipError_t attn_d(const KParams& P, const int8_t* qc, const float* qsc, const in
                   const float* mu_v, void* o, float* lse, const int8_t* mcode, const float* mcs,
                   hipStream_t st) {
     static std::atomic<uint64_t> attr_set{0};
-    // (+64 bytes: the absmax slots of the kernel's own Q quantization)
-    constexpr int LDS = lds_bytes<D, HAS_DS, PVH, BQS, QB>() + 64;
+    // (+64 bytes: the absmax slots of the kernel's own Q quantization; then
+    // the V scales and means of the epilogue, 2*D floats)
+    constexpr int LDS = lds_bytes<D, HAS_DS, PVH, BQS, QB>() + 64 + 8 * D;
     auto* kern = &k_attn<D, DT, HAS_DS, PVH, QB, false, BQS>;
     hipError_t e = lds_attr(reinterpret_cast<const void*>(kern), LDS, attr_set);
     if (e != hipSuccess) return e;
