@@ -38,6 +38,11 @@ CASES = {
                               Nq=3, Nkv=900, d=64, seed=23), 128, "fp8"),
     "decode_smooth_all": (R(W["video_dit"], B=1, Hq=4, Hkv=2, Nq=7, Nkv=1100, d=128, seed=24,
                             layout="HND"), 384, "fp8"),
+    # the fused kernel's split partials with Q, K and V smoothed (V scales and
+    # means read from the workgroup's LDS copy; 80 rows per kv head, too many
+    # for the one-wave kernel)
+    "chunk_q40_smooth_all": (R(W["video_dit"], B=1, Hq=4, Hkv=2, Nq=40, Nkv=900, d=128,
+                               seed=32, layout="HND"), 256, "fp8"),
     "decode_half": (R(W["decode_gqa"], B=2, Hq=8, Hkv=2, Nkv=1300, seed=25), 256, "half"),
     "decode_half_bf16_smooth_v": (R(W["decode_gqa"], dtype="bf16", B=1, Hq=4, Hkv=4, Nq=2,
                                     Nkv=800, smooth_v=True, seed=26), 128, "half"),
