@@ -1241,12 +1241,10 @@ __global__ __launch_bounds__(FWD_NT) void k_attn(KParams P, const int8_t* __rest
                                        acc[c][4 * r4 + 1] * s4.y * inv_l + m4.y,
                                        acc[c][4 * r4 + 2] * s4.z * inv_l + m4.z,
                                        acc[c][4 * r4 + 3] * s4.w * inv_l + m4.w};
-                uint32_t bits[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bits[e] = f2h_bits<DT>(vals[e]);
+                // (rounded to nearest even by the packed converts)
                 const int byte = 2 * ch0;              // 8-byte half of granule byte / 16
                 *reinterpret_cast<uint2*>(mine + ((((byte >> 4) ^ (qi % NGR)) << 4) | (byte & 15))) =
-                    make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
+                    make_uint2(pack16<DT>(vals[0], vals[1]), pack16<DT>(vals[2], vals[3]));
             }
         if (lse && h == 0 && my_q < nq)
             lse[si.lse0 + (int64_t)w.head * P.lse_hstride + my_q] =
